@@ -1,0 +1,1 @@
+"""CPU fp64 oracle (test infrastructure only; never imported by the product path)."""

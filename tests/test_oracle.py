@@ -1,0 +1,334 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+* the mask against a brute-force reading of the rule in words and against
+  hand-derived fixtures of the BlockMask construction formula (SpecForge review,
+  §3 "BlockMask construction algorithm", §4 "BlockMask construction");
+* the forward pass against torch's scaled_dot_product_attention (a library
+  routine) with an independently built boolean mask, and against closed forms;
+* invariants that any correct masked attention satisfies;
+* the backward pass against central finite differences, torch autograd through
+  the library routine, and closed-form column sums.
+"""
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from masked_attention_eagle_amd import inputs
+from oracle import ttt_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def brute_mask(L, step, T):
+    """The rule in words: row i < T sees keys 0..i and key t*L + i of every block t >= 1;
+    row i >= T sees keys 0..T-1 of block 0.  Built with Python loops, not the formula."""
+    M = np.zeros((L, (step + 1) * L), dtype=bool)
+    for i in range(L):
+        if i < T:
+            for j in range(i + 1):
+                M[i, j] = True
+            for t in range(1, step + 1):
+                M[i, t * L + i] = True
+        else:
+            for j in range(T):
+                M[i, j] = True
+    return M
+
+
+def rand(shape, rng):
+    return rng.standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------- mask
+@pytest.mark.parametrize("L", range(1, 9))
+def test_mask_matches_rule_in_words(L):
+    for step in range(4):
+        for T in range(L + 1):
+            np.testing.assert_array_equal(O.mask(L, step, T), brute_mask(L, step, T),
+                                          err_msg=f"L={L} step={step} T={T}")
+
+
+@pytest.mark.parametrize("name", ["mask_L4_k1_T3.txt", "mask_L5_k2_T2.txt", "mask_L3_k2_T0.txt"])
+def test_mask_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        lines = f.read().splitlines()
+    head = lines[0]
+    L = int(head.split("Q_LEN=")[1].split()[0])
+    step = int(head.split("ttt_step=")[1].split()[0])
+    T = int(head.split("T=")[1].split()[0])
+    M = O.mask(L, step, T)
+    assert M.shape == (L, (step + 1) * L)
+    for line in lines[1:]:
+        i, keys = line.split(":")
+        want = sorted(int(x) for x in keys.split())
+        got = np.nonzero(M[int(i)])[0].tolist()
+        assert got == want, f"{name} row {i}"
+
+
+def test_mask_row_and_total_counts_closed_form():
+    for L in (1, 5, 16, 37):
+        for step in range(4):
+            for T in sorted({0, 1, L // 2, L - 1, L} - {-1}):
+                M = O.mask(L, step, T)
+                rows = M.sum(axis=1)
+                want = [(i + 1 + step) if i < T else T for i in range(L)]
+                np.testing.assert_array_equal(rows, want)
+                total = T * (T + 1) // 2 + (L - T) * T + step * T
+                assert O.unmasked_pairs(L, step, T) == total
+
+
+# ----------------------------------------------------------------------------- forward
+def _sdpa(q, k, v, M, scale):
+    """Library reference: torch SDPA in fp64 with an explicit boolean mask (GQA expanded)."""
+    G = q.shape[1] // k.shape[1]
+    kt = torch.from_numpy(np.repeat(k, G, axis=1))
+    vt = torch.from_numpy(np.repeat(v, G, axis=1))
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), kt, vt, attn_mask=torch.from_numpy(M), scale=scale).numpy()
+
+
+def test_step0_full_length_is_plain_causal_attention():
+    rng = np.random.default_rng(1)
+    B, Hq, Hkv, L, d = 2, 4, 2, 16, 8
+    q, k, v = rand((B, Hq, L, d), rng), rand((B, Hkv, L, d), rng), rand((B, Hkv, L, d), rng)
+    o, lse = O.forward(q, k, v, [L, L], 0.37)
+    G = Hq // Hkv
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(np.repeat(k, G, 1)), torch.from_numpy(np.repeat(v, G, 1)),
+        is_causal=True, scale=0.37).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("step,Ts", [(1, (7, 12)), (2, (12, 3)), (3, (1, 9))])
+def test_forward_matches_library_sdpa_with_brute_mask(step, Ts):
+    rng = np.random.default_rng(10 + step)
+    B, Hq, Hkv, L, d = 2, 6, 2, 12, 8
+    q = rand((B, Hq, L, d), rng)
+    k, v = rand((B, Hkv, (step + 1) * L, d), rng), rand((B, Hkv, (step + 1) * L, d), rng)
+    scale = 0.5
+    o, lse = O.forward(q, k, v, Ts, scale)
+    G = Hq // Hkv
+    for b in range(B):
+        M = brute_mask(L, step, Ts[b])
+        ref = _sdpa(q[b:b + 1], k[b:b + 1], v[b:b + 1], M, scale)[0]
+        np.testing.assert_allclose(o[b], ref, rtol=0, atol=1e-12)
+        for h in range(Hq):
+            s = scale * q[b, h] @ k[b, h // G].T
+            ref_lse = scipy.special.logsumexp(np.where(M, s, -np.inf), axis=1)
+            np.testing.assert_allclose(lse[b, h], ref_lse, rtol=0, atol=1e-12)
+
+
+def test_zero_keys_closed_form():
+    """K = 0: every visible logit is 0, so lse_i = ln|M_i| and O_i is the mean of the visible V rows."""
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, L, d, step = 1, 2, 1, 10, 4, 2
+    for T in (0, 1, 6, 10):
+        q = rand((B, Hq, L, d), rng)
+        k = np.zeros((B, Hkv, (step + 1) * L, d))
+        v = rand((B, Hkv, (step + 1) * L, d), rng)
+        o, lse = O.forward(q, k, v, [T], 0.9)
+        M = brute_mask(L, step, T)
+        for i in range(L):
+            idx = np.nonzero(M[i])[0]
+            if len(idx) == 0:
+                assert np.all(o[0, :, i] == 0) and np.all(np.isneginf(lse[0, :, i]))
+            else:
+                np.testing.assert_allclose(lse[0, :, i], np.log(len(idx)), atol=1e-14)
+                np.testing.assert_allclose(o[0, 0, i], v[0, 0, idx].mean(axis=0), atol=1e-13)
+
+
+def test_first_row_at_step0():
+    rng = np.random.default_rng(4)
+    q, k, v = rand((1, 1, 5, 3), rng), rand((1, 1, 5, 3), rng), rand((1, 1, 5, 3), rng)
+    o, lse = O.forward(q, k, v, [5], 0.25)
+    np.testing.assert_array_equal(o[0, 0, 0], v[0, 0, 0])
+    assert abs(lse[0, 0, 0] - 0.25 * q[0, 0, 0] @ k[0, 0, 0]) < 1e-15
+
+
+def test_probabilities_sum_to_one_on_mask():
+    """Feeding V = identity columns turns O into the probability rows themselves."""
+    rng = np.random.default_rng(5)
+    L, step, T = 6, 2, 4
+    KV = (step + 1) * L
+    q = rand((1, 1, L, 5), rng)
+    k = rand((1, 1, KV, 5), rng)
+    v = np.eye(KV)[None, None]
+    o, _ = O.forward(q, k, v, [T], 0.7)
+    P = o[0, 0]
+    M = brute_mask(L, step, T)
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-14)
+    assert np.all(P[~M] == 0)
+    assert np.all(P[M] > 0)
+
+
+def test_invariants_poison_permute_shift():
+    rng = np.random.default_rng(6)
+    B, Hq, Hkv, L, d, step, T = 1, 4, 2, 8, 6, 3, 5
+    q = rand((B, Hq, L, d), rng)
+    k, v = rand((B, Hkv, (step + 1) * L, d), rng), rand((B, Hkv, (step + 1) * L, d), rng)
+    o, lse = O.forward(q, k, v, [T], 0.6)
+    # rows no query may see: block-0 rows >= T and suffix rows t*L + i with i >= T
+    dead = [j for j in range((step + 1) * L) if (j % L) >= T]
+    kp, vp = k.copy(), v.copy()
+    kp[:, :, dead] = 1e4
+    vp[:, :, dead] = -3e4
+    o2, lse2 = O.forward(q, kp, vp, [T], 0.6)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, atol=1e-12)
+    # permuting suffix blocks 1..step leaves the result unchanged
+    perm = [0, 3, 1, 2]
+    kb = np.concatenate([k[:, :, p * L:(p + 1) * L] for p in perm], axis=2)
+    vb = np.concatenate([v[:, :, p * L:(p + 1) * L] for p in perm], axis=2)
+    o3, lse3 = O.forward(q, kb, vb, [T], 0.6)
+    np.testing.assert_allclose(o3, o, atol=1e-12)
+    # shifting every key by c shifts lse by scale * q . c and leaves O unchanged
+    c = rand((d,), rng)
+    o4, lse4 = O.forward(q, k + c, v, [T], 0.6)
+    np.testing.assert_allclose(o4, o, atol=1e-11)
+    np.testing.assert_allclose(lse4, lse + 0.6 * q @ c, atol=1e-11)
+
+
+def test_gqa_equals_repeated_heads():
+    """Contiguous GQA grouping equals MHA on repeat_interleave'd K/V (kv head = h // G)."""
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, L, d, step = 1, 6, 2, 7, 4, 1
+    q = rand((B, Hq, L, d), rng)
+    k, v = rand((B, Hkv, (step + 1) * L, d), rng), rand((B, Hkv, (step + 1) * L, d), rng)
+    do = rand((B, Hq, L, d), rng)
+    G = Hq // Hkv
+    kr = torch.from_numpy(k).repeat_interleave(G, dim=1).numpy()
+    vr = torch.from_numpy(v).repeat_interleave(G, dim=1).numpy()
+    o, lse = O.forward(q, k, v, [5], 0.4)
+    o_r, lse_r = O.forward(q, kr, vr, [5], 0.4)
+    np.testing.assert_allclose(o, o_r, atol=1e-13)
+    dq, dk, dv = O.backward(q, k, v, [5], 0.4, do)
+    dq_r, dk_r, dv_r = O.backward(q, kr, vr, [5], 0.4, do)
+    np.testing.assert_allclose(dq, dq_r, atol=1e-12)
+    np.testing.assert_allclose(dk, dk_r.reshape(B, Hkv, G, -1, d).sum(axis=2), atol=1e-12)
+    np.testing.assert_allclose(dv, dv_r.reshape(B, Hkv, G, -1, d).sum(axis=2), atol=1e-12)
+
+
+def test_merge_of_causal_block_and_diagonal_suffix():
+    """The full result is the log-sum-exp merge of the step-0 (causal-only) result and the
+    single diagonal key of every later block (one key per block: a closed form)."""
+    rng = np.random.default_rng(8)
+    L, d, step, T = 9, 5, 3, 7
+    q = rand((1, 1, L, d), rng)
+    k, v = rand((1, 1, (step + 1) * L, d), rng), rand((1, 1, (step + 1) * L, d), rng)
+    scale = 0.45
+    o, lse = O.forward(q, k, v, [T], scale)
+    oc, lsec = O.forward(q, k[:, :, :L], v[:, :, :L], [T], scale)
+    for i in range(L):
+        num = np.exp(lsec[0, 0, i]) * oc[0, 0, i]
+        den = np.exp(lsec[0, 0, i])
+        if i < T:
+            for t in range(1, step + 1):
+                s = scale * q[0, 0, i] @ k[0, 0, t * L + i]
+                num = num + np.exp(s) * v[0, 0, t * L + i]
+                den = den + np.exp(s)
+        np.testing.assert_allclose(o[0, 0, i], num / den, atol=1e-12)
+        np.testing.assert_allclose(lse[0, 0, i], np.log(den), atol=1e-12)
+
+
+def test_empty_sequence_gives_zero_output_and_neg_inf_lse():
+    rng = np.random.default_rng(9)
+    q = rand((1, 2, 4, 3), rng)
+    k, v = rand((1, 1, 12, 3), rng), rand((1, 1, 12, 3), rng)
+    o, lse = O.forward(q, k, v, [0], 1.0)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    dq, dk, dv = O.backward(q, k, v, [0], 1.0, rand((1, 2, 4, 3), rng))
+    assert np.all(dq == 0) and np.all(dk == 0) and np.all(dv == 0)
+
+
+# ----------------------------------------------------------------------------- backward
+def test_backward_finite_differences():
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, d, L, step, T = 1, 2, 1, 8, 8, 2, 6
+    scale = 0.3
+    q = rand((B, Hq, L, d), rng)
+    k, v = rand((B, Hkv, (step + 1) * L, d), rng), rand((B, Hkv, (step + 1) * L, d), rng)
+    do = rand((B, Hq, L, d), rng)
+    dq, dk, dv = O.backward(q, k, v, [T], scale, do)
+
+    def f(qq, kk, vv):
+        return float((O.forward(qq, kk, vv, [T], scale)[0] * do).sum())
+
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (f(args_p["q"], args_p["k"], args_p["v"]) -
+                        f(args_m["q"], args_m["k"], args_m["v"])) / (2 * eps)
+        err = np.abs(num - g).max() / max(np.abs(g).max(), 1e-30)
+        assert err < 1e-6, (name, err)
+
+
+@pytest.mark.parametrize("step,Ts", [(0, (16, 11)), (2, (16, 5)), (3, (1, 13))])
+def test_backward_matches_torch_autograd(step, Ts):
+    rng = np.random.default_rng(20 + step)
+    B, Hq, Hkv, L, d = 2, 4, 2, 16, 8
+    scale = 0.35
+    q = rand((B, Hq, L, d), rng)
+    k, v = rand((B, Hkv, (step + 1) * L, d), rng), rand((B, Hkv, (step + 1) * L, d), rng)
+    do = rand((B, Hq, L, d), rng)
+    dq, dk, dv = O.backward(q, k, v, Ts, scale, do)
+    G = Hq // Hkv
+    for b in range(B):
+        M = torch.from_numpy(brute_mask(L, step, Ts[b]))
+        qt = torch.from_numpy(q[b:b + 1]).requires_grad_()
+        kt = torch.from_numpy(k[b:b + 1]).requires_grad_()
+        vt = torch.from_numpy(v[b:b + 1]).requires_grad_()
+        out = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1), attn_mask=M, scale=scale)
+        out.backward(torch.from_numpy(do[b:b + 1]))
+        np.testing.assert_allclose(dq[b], qt.grad[0].numpy(), atol=1e-11)
+        np.testing.assert_allclose(dk[b], kt.grad[0].numpy(), atol=1e-11)
+        np.testing.assert_allclose(dv[b], vt.grad[0].numpy(), atol=1e-11)
+
+
+def test_backward_column_sums_and_dead_rows():
+    """sum_j dK_j = 0 (rows of dS sum to 0) and sum_j dV_j = sum of dO over non-empty rows
+    (rows of P sum to 1); keys that no query sees get zero gradient."""
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, L, d, step = 2, 4, 2, 10, 6, 2
+    Ts = (10, 4)
+    q = rand((B, Hq, L, d), rng)
+    k, v = rand((B, Hkv, (step + 1) * L, d), rng), rand((B, Hkv, (step + 1) * L, d), rng)
+    do = rand((B, Hq, L, d), rng)
+    dq, dk, dv = O.backward(q, k, v, Ts, 0.5, do)
+    G = Hq // Hkv
+    for b in range(B):
+        for g in range(Hkv):
+            np.testing.assert_allclose(dk[b, g].sum(axis=0), 0, atol=1e-12)
+            want = do[b, g * G:(g + 1) * G].sum(axis=(0, 1)) if Ts[b] > 0 else 0
+            np.testing.assert_allclose(dv[b, g].sum(axis=0), want, atol=1e-12)
+        dead = [j for j in range((step + 1) * L) if (j % L) >= Ts[b]]
+        assert np.all(dk[b][:, dead] == 0) and np.all(dv[b][:, dead] == 0)
+
+
+# ----------------------------------------------------------------------------- inputs
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal(100000).astype(np.float32)
+    ties = np.array([1.00390625, 1.01171875, -1.00390625, 3.0517578e-05], dtype=np.float32)
+    for arr in (x, ties):
+        want = torch.from_numpy(arr).to(torch.bfloat16).float().numpy()
+        np.testing.assert_array_equal(inputs.round_to_bf16(arr), want)
+
+
+def test_padding_heavy_lengths_are_seeded_and_in_range():
+    w = inputs.WORKLOADS[3]
+    T = inputs.seq_lengths(w)
+    assert T.shape == (8,) and T.min() >= 256 and T.max() <= 2048
+    np.testing.assert_array_equal(T, inputs.seq_lengths(w))
