@@ -1,0 +1,133 @@
+/*
+ * ttt_attn.h - C ABI of the TTT sparse tree attention library (MI355X / gfx950).
+ *
+ * The operation is softmax attention under the mask of the SpecForge paper review,
+ * "§3 Technical architecture -> Compute optimisation -> Sparse Tree Attention ->
+ * BlockMask construction algorithm" (restated in "§4 Core formulas -> BlockMask
+ * construction"), used when an EAGLE-3 draft model is trained with training-time
+ * test (TTT):
+ *
+ *   M_causal = (q_i >= kv_i) and (kv_i < T)
+ *   M_suffix = (kv_i >= Q_LEN) and (kv_i mod Q_LEN < T) and ((kv_i - q_i) mod Q_LEN == 0)
+ *   M        = M_causal or M_suffix
+ *
+ * Query row i (0 <= i < Q_LEN) of TTT step k sees keys 0..min(i, T-1) of block 0 and,
+ * when i < T, key t*Q_LEN + i of every later block t = 1..k.  Padded rows (i >= T) see
+ * keys 0..T-1.  A row with no visible key (T == 0) gets o = 0 and lse = -inf.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layouts   contiguous, row-major:
+ *              q, o, dout, dq      [B, Hq,  Q_LEN, d]
+ *              k, v, dk, dv        [B, Hkv, (k+1)*Q_LEN, d]   (block t = rows [t*Q_LEN, (t+1)*Q_LEN))
+ *              lse                 [B, Hq,  Q_LEN]  fp32, natural log
+ *              seq_T               [B] int32, device memory, one valid length per sequence
+ *            Query head h reads KV head h / (Hq / Hkv) (contiguous GQA groups).
+ *  Pointers  All tensors and the workspace are device memory owned by the caller; base
+ *            addresses must be 16-byte aligned.  The library never allocates, frees or
+ *            synchronises and keeps no state between calls (except the optional timing
+ *            records below).  Concurrent calls need distinct workspaces.
+ *  Outputs   write-only and fully overwritten: o, lse, dq, dk, dv.  dk/dv rows that no
+ *            query sees are written 0.  Gradients are not accumulated across calls.
+ *  seq_T     read on the device only; values outside [0, Q_LEN] are clamped into it.
+ *  Streams   all work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *            The return value reports argument validation and launch status only.
+ *  Errors    0 on success, else one of the negative TTT_E_* codes; nothing is launched
+ *            when validation fails.  No exception crosses the ABI.
+ */
+#ifndef TTT_ATTN_H
+#define TTT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ttt_attn_dtype {
+  TTT_DTYPE_F32 = 0,  /* fp32 tensors, fp32 arithmetic (VALU)                       */
+  TTT_DTYPE_BF16 = 1  /* bf16 tensors, bf16 MFMA with fp32 accumulation; lse in fp32 */
+};
+
+enum ttt_attn_status {
+  TTT_OK = 0,
+  TTT_E_NULL = -1,        /* a required pointer is NULL                              */
+  TTT_E_SHAPE = -2,       /* non-positive size, Hq % Hkv != 0, ttt_step < 0, overflow */
+  TTT_E_UNSUPPORTED = -3, /* head_dim/dtype/q_len combination not built (see below)  */
+  TTT_E_ALIGN = -4,       /* a pointer is not 16-byte aligned                        */
+  TTT_E_WORKSPACE = -5,   /* workspace smaller than *_workspace_size()               */
+  TTT_E_HIP = -6          /* a kernel launch failed (hipGetLastError)                */
+};
+
+/*
+ * Problem description.  Supported combinations:
+ *   dtype F32 : head_dim in {64, 128}, any q_len >= 1.
+ *   dtype BF16: head_dim == 128, q_len a multiple of 128.
+ * scale multiplies q.k before masking (1/sqrt(head_dim) in the usual setting).
+ */
+typedef struct ttt_attn_params {
+  int32_t batch;     /* B                                  */
+  int32_t heads_q;   /* Hq                                 */
+  int32_t heads_kv;  /* Hkv, divides Hq                    */
+  int32_t q_len;     /* Q_LEN                              */
+  int32_t head_dim;  /* d                                  */
+  int32_t ttt_step;  /* k >= 0; the KV length is (k+1)*Q_LEN */
+  float scale;
+  int32_t dtype;     /* enum ttt_attn_dtype                */
+} ttt_attn_params;
+
+/* Bytes of device workspace the call needs (0 when the params are invalid). */
+size_t ttt_attn_fwd_workspace_size(const ttt_attn_params* p);
+size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p);
+
+/*
+ * Forward: o = softmax_M(scale * q k^T) v and lse = log sum_{j in M} exp(scale * q.k_j).
+ * Streaming softmax (the review's §3 "Sparse Tree Attention": computed flash-style so the
+ * logits are never stored): the causal block 0 runs as tiled MFMA with fully masked
+ * tiles skipped; the diagonal suffix keys of blocks 1..k are gathered per query and
+ * merged into the same softmax state.
+ */
+int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                 const int32_t* seq_T, void* o, float* lse, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
+ * Backward: gradients of sum(dout * o) for the o/lse produced by ttt_attn_fwd on the same
+ * inputs.  P is recomputed from lse (nothing else is saved), the softmax Jacobian gives
+ * dS = P * (dP - rowsum(dout * o)), and dk/dv of every KV row are produced by exactly one
+ * workgroup summing the query heads of its GQA group in a fixed order (bitwise
+ * deterministic).  dq rows are likewise owned by one workgroup each.
+ */
+int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                 const int32_t* seq_T, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Static text for a status code. */
+const char* ttt_attn_status_string(int status);
+
+/* ABI version (major * 100 + minor). */
+int ttt_attn_version(void);
+
+/*
+ * Optional per-kernel timing, for measurement.  When enabled, every kernel launch of
+ * ttt_attn_fwd/bwd is bracketed by hipEvents on the launch stream; ttt_attn_timing_read
+ * synchronises those events and returns, per kernel name, the number of launches and the
+ * summed milliseconds since the last reset.  Not thread-safe; off by default.
+ */
+typedef struct ttt_attn_kernel_time {
+  char name[48];
+  int32_t launches;
+  double total_ms;
+} ttt_attn_kernel_time;
+
+int ttt_attn_timing_enable(int on);                       /* returns previous setting      */
+int ttt_attn_timing_read(ttt_attn_kernel_time* out, int max_entries); /* entries written, <0 on error */
+void ttt_attn_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_ATTN_H */

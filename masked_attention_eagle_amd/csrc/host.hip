@@ -1,0 +1,347 @@
+// C ABI of the TTT sparse tree attention library: validation, workspace layout, dispatch.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "launch.h"
+#include "ttt_attn.h"
+
+namespace ttt {
+
+// ------------------------------------------------------------------ per-launch timing hook
+namespace {
+struct TimingRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+bool g_timing_on = false;
+std::vector<TimingRecord> g_records;  // events recorded since the last read/reset
+size_t g_used = 0;
+
+struct Accum {
+  char name[48];
+  int launches;
+  double ms;
+};
+std::vector<Accum> g_accum;
+}  // namespace
+
+LaunchTimer::LaunchTimer(const char* name, hipStream_t st) : name_(name), st_(st), slot_(-1) {
+  if (!g_timing_on) return;
+  if (g_used == g_records.size()) {
+    TimingRecord r{name, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
+    g_records.push_back(r);
+  }
+  slot_ = (int)g_used++;
+  g_records[slot_].name = name;
+  hipEventRecord(g_records[slot_].start, st);
+}
+
+LaunchTimer::~LaunchTimer() {
+  if (slot_ >= 0) hipEventRecord(g_records[slot_].stop, st_);
+}
+
+static void accumulate(const char* name, double ms) {
+  for (auto& a : g_accum) {
+    if (strncmp(a.name, name, sizeof(a.name)) == 0) {
+      a.launches += 1;
+      a.ms += ms;
+      return;
+    }
+  }
+  Accum a{};
+  strncpy(a.name, name, sizeof(a.name) - 1);
+  a.launches = 1;
+  a.ms = ms;
+  g_accum.push_back(a);
+}
+
+// ------------------------------------------------------------------ validation and layout
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int validate(const ttt_attn_params* p) {
+  if (!p) return TTT_E_NULL;
+  if (p->batch <= 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->q_len <= 0 ||
+      p->head_dim <= 0 || p->ttt_step < 0)
+    return TTT_E_SHAPE;
+  if (p->heads_q % p->heads_kv != 0) return TTT_E_SHAPE;
+  if (!isfinite(p->scale)) return TTT_E_SHAPE;
+  const int64_t kv = (int64_t)(p->ttt_step + 1) * p->q_len;
+  if (kv > INT32_MAX) return TTT_E_SHAPE;
+  // Thread counts of the largest grids must stay below 2^32 and element counts below 2^40.
+  const int64_t rows_q = (int64_t)p->batch * p->heads_q * p->q_len;
+  const int64_t rows_kv = (int64_t)p->batch * p->heads_kv * kv;
+  if (rows_q * p->head_dim > (1ll << 40) || rows_kv * p->head_dim > (1ll << 40)) return TTT_E_SHAPE;
+  if (p->dtype == TTT_DTYPE_F32) {
+    if (p->head_dim != 64 && p->head_dim != 128) return TTT_E_UNSUPPORTED;
+    if (rows_q * 64 >= (1ll << 32) || (int64_t)p->batch * p->heads_kv * p->q_len * 64 >= (1ll << 32))
+      return TTT_E_SHAPE;
+  } else if (p->dtype == TTT_DTYPE_BF16) {
+    if (p->head_dim != 128 || p->q_len % 128 != 0) return TTT_E_UNSUPPORTED;
+    if ((int64_t)p->batch * p->heads_kv * p->q_len * 16 >= (1ll << 32)) return TTT_E_SHAPE;
+  } else {
+    return TTT_E_UNSUPPORTED;
+  }
+  return TTT_OK;
+}
+
+Shape make_shape(const ttt_attn_params* p) {
+  Shape s;
+  s.B = p->batch;
+  s.Hq = p->heads_q;
+  s.Hkv = p->heads_kv;
+  s.L = p->q_len;
+  s.D = p->head_dim;
+  s.step = p->ttt_step;
+  s.G = p->heads_q / p->heads_kv;
+  s.KV = (p->ttt_step + 1) * p->q_len;
+  s.scale = p->scale;
+  s.scale_log2 = p->scale * kLog2e;
+  return s;
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Number of workgroups that share the query heads of one KV group in the dK/dV kernel:
+// doubled while the grid is below two workgroups per CU and the group still splits evenly.
+int dkdv_nsplit(const Shape& s) {
+  const int64_t base = (int64_t)s.B * s.Hkv * (s.L / 128);
+  int n = 1;
+  while (base * n < 512 && n < s.G && s.G % (2 * n) == 0) n *= 2;
+  return n;
+}
+
+struct FwdLayout {
+  size_t vt = 0, oc = 0, lsec = 0, total = 0;
+};
+FwdLayout fwd_layout(const Shape& s, int dtype) {
+  FwdLayout w;
+  size_t off = 0;
+  const size_t rows_q = (size_t)s.B * s.Hq * s.L;
+  if (dtype == TTT_DTYPE_BF16) {
+    w.vt = off;
+    off += round_up((size_t)s.B * s.Hkv * s.D * s.L * 2);
+  }
+  if (s.step > 0) {
+    w.oc = off;
+    off += round_up(rows_q * s.D * 4);
+    w.lsec = off;
+    off += round_up(rows_q * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+struct BwdLayout {
+  size_t Dd = 0, dqacc = 0, qt = 0, dot = 0, kt = 0, part = 0, total = 0;
+  int nsplit = 1;
+};
+BwdLayout bwd_layout(const Shape& s, int dtype) {
+  BwdLayout w;
+  size_t off = 0;
+  const size_t rows_q = (size_t)s.B * s.Hq * s.L;
+  w.Dd = off;
+  off += round_up(rows_q * 4);
+  if (s.step > 0) {
+    w.dqacc = off;
+    off += round_up(rows_q * s.D * 4);
+  }
+  if (dtype == TTT_DTYPE_BF16) {
+    w.qt = off;
+    off += round_up(rows_q * s.D * 2);
+    w.dot = off;
+    off += round_up(rows_q * s.D * 2);
+    w.kt = off;
+    off += round_up((size_t)s.B * s.Hkv * s.L * s.D * 2);
+    w.nsplit = dkdv_nsplit(s);
+    if (w.nsplit > 1) {
+      w.part = off;
+      off += round_up((size_t)w.nsplit * 2 * s.B * s.Hkv * s.L * s.D * 4);
+    }
+  }
+  w.total = off;
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_E_HIP; }
+
+}  // namespace
+}  // namespace ttt
+
+using namespace ttt;
+
+extern "C" {
+
+int ttt_attn_version(void) { return 100; }
+
+const char* ttt_attn_status_string(int status) {
+  switch (status) {
+    case TTT_OK: return "ok";
+    case TTT_E_NULL: return "null pointer argument";
+    case TTT_E_SHAPE: return "invalid shape (non-positive size, heads_q % heads_kv != 0, ttt_step < 0, non-finite scale or size overflow)";
+    case TTT_E_UNSUPPORTED: return "unsupported configuration (f32: head_dim 64 or 128; bf16: head_dim 128 and q_len % 128 == 0)";
+    case TTT_E_ALIGN: return "pointer not 16-byte aligned";
+    case TTT_E_WORKSPACE: return "workspace smaller than required";
+    case TTT_E_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t ttt_attn_fwd_workspace_size(const ttt_attn_params* p) {
+  if (validate(p) != TTT_OK) return 0;
+  return fwd_layout(make_shape(p), p->dtype).total;
+}
+
+size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p) {
+  if (validate(p) != TTT_OK) return 0;
+  return bwd_layout(make_shape(p), p->dtype).total;
+}
+
+int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                 const int32_t* seq_T, void* o, float* lse, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  int rc = validate(p);
+  if (rc != TTT_OK) return rc;
+  if (!q || !k || !v || !seq_T || !o || !lse) return TTT_E_NULL;
+  const Shape s = make_shape(p);
+  const FwdLayout w = fwd_layout(s, p->dtype);
+  if (w.total > 0 && !workspace) return TTT_E_NULL;
+  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(workspace))
+    return TTT_E_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const bool final_causal = s.step == 0;
+  float* oc = final_causal ? nullptr : (float*)(ws + w.oc);
+  float* lsec = final_causal ? lse : (float*)(ws + w.lsec);
+  hipError_t e;
+  if (p->dtype == TTT_DTYPE_BF16) {
+    const bf16* qb = (const bf16*)q;
+    const bf16* kb = (const bf16*)k;
+    const bf16* vb = (const bf16*)v;
+    bf16* vt = (bf16*)(ws + w.vt);
+    e = launch_transpose_swz(vb, vt, s.L, (size_t)s.KV * s.D, s.B * s.Hkv, st);
+    if (e != hipSuccess) return TTT_E_HIP;
+    e = launch_fwd_causal_mfma(s, qb, kb, vt, seq_T, final_causal ? o : (void*)oc, lsec,
+                               final_causal, st);
+    if (e != hipSuccess) return TTT_E_HIP;
+    if (!final_causal)
+      e = launch_fwd_suffix<bf16>(s, qb, kb, vb, seq_T, oc, lsec, (bf16*)o, lse, st);
+  } else {
+    const float* qf = (const float*)q;
+    const float* kf = (const float*)k;
+    const float* vf = (const float*)v;
+    e = launch_fwd_causal_valu<float>(s, qf, kf, vf, seq_T, final_causal ? o : (void*)oc, lsec,
+                                      final_causal, st);
+    if (e != hipSuccess) return TTT_E_HIP;
+    if (!final_causal)
+      e = launch_fwd_suffix<float>(s, qf, kf, vf, seq_T, oc, lsec, (float*)o, lse, st);
+  }
+  return hip_status(e);
+}
+
+int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                 const int32_t* seq_T, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  int rc = validate(p);
+  if (rc != TTT_OK) return rc;
+  if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
+  const Shape s = make_shape(p);
+  const BwdLayout w = bwd_layout(s, p->dtype);
+  if (w.total > 0 && !workspace) return TTT_E_NULL;
+  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(workspace))
+    return TTT_E_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* Dd = (float*)(ws + w.Dd);
+  const bool final_causal = s.step == 0;
+  float* dqacc = final_causal ? nullptr : (float*)(ws + w.dqacc);
+  hipError_t e;
+  if (p->dtype == TTT_DTYPE_BF16) {
+    const bf16* qb = (const bf16*)q;
+    const bf16* kb = (const bf16*)k;
+    const bf16* vb = (const bf16*)v;
+    const bf16* dob = (const bf16*)dout;
+    bf16* qt = (bf16*)(ws + w.qt);
+    bf16* dot = (bf16*)(ws + w.dot);
+    bf16* kt = (bf16*)(ws + w.kt);
+    float* part = w.nsplit > 1 ? (float*)(ws + w.part) : nullptr;
+    if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, st)) != hipSuccess) return TTT_E_HIP;
+    if ((e = launch_transpose_swz(qb, qt, s.L, (size_t)s.L * s.D, s.B * s.Hq, st)) != hipSuccess) return TTT_E_HIP;
+    if ((e = launch_transpose_swz(dob, dot, s.L, (size_t)s.L * s.D, s.B * s.Hq, st)) != hipSuccess) return TTT_E_HIP;
+    if ((e = launch_transpose_swz(kb, kt, s.L, (size_t)s.KV * s.D, s.B * s.Hkv, st)) != hipSuccess) return TTT_E_HIP;
+    if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, qt, dot, dob, lse, Dd, seq_T, (bf16*)dk, (bf16*)dv,
+                                  part, w.nsplit, st)) != hipSuccess)
+      return TTT_E_HIP;
+    if (w.nsplit > 1 &&
+        (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
+      return TTT_E_HIP;
+    if ((e = launch_bwd_dq_mfma(s, qb, kb, vb, kt, dob, lse, Dd, seq_T,
+                                final_causal ? dq : (void*)dqacc, final_causal, st)) != hipSuccess)
+      return TTT_E_HIP;
+    if (!final_causal)
+      e = launch_bwd_suffix<bf16>(s, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq, (bf16*)dk,
+                                  (bf16*)dv, st);
+  } else {
+    const float* qf = (const float*)q;
+    const float* kf = (const float*)k;
+    const float* vf = (const float*)v;
+    const float* dof = (const float*)dout;
+    if ((e = launch_bwd_rowdot<float>(s, (const float*)o, dof, Dd, st)) != hipSuccess) return TTT_E_HIP;
+    if ((e = launch_bwd_dkdv_valu<float>(s, qf, kf, vf, dof, lse, Dd, seq_T, (float*)dk,
+                                         (float*)dv, st)) != hipSuccess)
+      return TTT_E_HIP;
+    if ((e = launch_bwd_dq_valu<float>(s, qf, kf, vf, dof, lse, Dd, seq_T,
+                                       final_causal ? dq : (void*)dqacc, final_causal, st)) != hipSuccess)
+      return TTT_E_HIP;
+    if (!final_causal)
+      e = launch_bwd_suffix<float>(s, qf, kf, vf, dof, lse, Dd, seq_T, dqacc, (float*)dq,
+                                   (float*)dk, (float*)dv, st);
+  }
+  return hip_status(e);
+}
+
+int ttt_attn_timing_enable(int on) {
+  const int prev = g_timing_on ? 1 : 0;
+  g_timing_on = on != 0;
+  return prev;
+}
+
+int ttt_attn_timing_read(ttt_attn_kernel_time* out, int max_entries) {
+  for (size_t i = 0; i < g_used; ++i) {
+    if (hipEventSynchronize(g_records[i].stop) != hipSuccess) return TTT_E_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_records[i].start, g_records[i].stop) != hipSuccess) return TTT_E_HIP;
+    accumulate(g_records[i].name, ms);
+  }
+  g_used = 0;
+  int n = 0;
+  for (const auto& a : g_accum) {
+    if (n >= max_entries) break;
+    if (out) {
+      memset(&out[n], 0, sizeof(out[n]));
+      strncpy(out[n].name, a.name, sizeof(out[n].name) - 1);
+      out[n].launches = a.launches;
+      out[n].total_ms = a.ms;
+    }
+    ++n;
+  }
+  return n;
+}
+
+void ttt_attn_timing_reset(void) {
+  for (size_t i = 0; i < g_used; ++i) hipEventSynchronize(g_records[i].stop);
+  g_used = 0;
+  g_accum.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,691 @@
+// Backward kernels of TTT sparse tree attention.
+//
+// Nothing but lse is saved by the forward (the review's §3 "Sparse Tree Attention": streamed
+// FlashAttention-style, no logits kept), so every kernel recomputes P = exp(scale q.k - lse)
+// and applies the softmax Jacobian dS = P * (dP - D), D = rowsum(dO * O), dP = dO V^T.
+// Block-0 (causal) keys are handled by two matrix-core kernels:
+//   dkdv: one workgroup owns 128 keys of one KV group and walks every query tile and every
+//         query head of the group that can see them, so dK/dV need no atomics and sum the
+//         heads in a fixed order (bitwise reproducible);
+//   dq:   one workgroup owns 128 query rows of one head and walks the key tiles they see.
+// The diagonal suffix keys of blocks 1..k are gathered by a bandwidth-bound kernel that also
+// finalises dQ.
+#include "launch.h"
+
+namespace ttt {
+
+constexpr int BD = 128;         // head dim of the matrix-core path
+constexpr int QSTR = BD + 8;    // row-major [token][d] tile stride (272 B rows)
+constexpr int TSTR = 64 + 8;    // transposed [d][64 tokens] tile stride (144 B rows)
+
+// ----------------------------------------------------------------------------------------
+// dK, dV of block 0, bf16 MFMA.  Workgroup = 4 waves x 32 keys = 128 keys; per 64-query tile
+// each wave computes
+//   S  = Q K^T,  dP = dO V^T          (M = queries, N = the wave's 32 keys; K, V in registers)
+//   P  = exp2(S * scale*log2e - lse*log2e), dS = P * (dP - D)
+//   dV += P^T dO,  dK += dS^T Q       (A operands straight from the S/dP accumulators,
+//                                      B = dO^T / Q^T tiles from LDS)
+// With nsplit > 1 the query heads of a group are split over nsplit workgroups that write
+// fp32 partial sums, reduced afterwards in split order.
+// ----------------------------------------------------------------------------------------
+constexpr int KBN = 128;  // keys per workgroup
+constexpr int KBM = 64;   // queries per tile
+
+struct DkdvStage {
+  bf16 q[KBM * QSTR];
+  bf16 dO[KBM * QSTR];
+  bf16 qt[BD * TSTR];
+  bf16 dOt[BD * TSTR];
+  float lse2[KBM];
+  float Dv[KBM];
+};
+
+__global__ __launch_bounds__(256) void bwd_dkdv_mfma_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ qt, const bf16* __restrict__ dot, const bf16* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ Dd, const int32_t* __restrict__ seq_T,
+    bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ part, int nsplit, Shape s) {
+  __shared__ __attribute__((aligned(16))) DkdvStage sm[2];
+
+  int unit, kt;
+  map_block(blockIdx.x, s.B * s.Hkv * nsplit, unit, kt);  // key tile 0 is the heaviest
+  const int split = unit % nsplit, bg = unit / nsplit;
+  const int b = bg / s.Hkv;
+  const int T = clamp_T(seq_T, b, s.L);
+  const int k0 = kt * KBN;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int kw = k0 + wave * 32;
+  const int my_key = kw + l32;
+  const int hpg = s.G / nsplit;
+  const int h_begin = (bg % s.Hkv) * s.G + split * hpg;
+
+  bf16x8 kf[8], vf[8];
+  {
+    const bf16* kr = k + ((size_t)bg * s.KV + my_key) * BD + 8 * hi;
+    const bf16* vr = v + ((size_t)bg * s.KV + my_key) * BD + 8 * hi;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      kf[t] = *reinterpret_cast<const bf16x8*>(kr + 16 * t);
+      vf[t] = *reinterpret_cast<const bf16x8*>(vr + 16 * t);
+    }
+  }
+  f32x16 dKacc[4], dVacc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) dKacc[u] = dVacc[u] = f32x16{};
+
+  // Queries that see keys [k0, k0 + 128): rows >= k0 (rows >= T see every key < T).
+  const int q_first = (k0 < T) ? (k0 / KBM) * KBM : s.L;
+  const int nq = (s.L - q_first) / KBM;
+  const int total = nq * hpg;
+
+  bf16x8 rq[4], rdo[4], rqt[4], rdot[4];
+  float rl = 0.f;
+  auto gload = [&](int it) {
+    const int h = h_begin + it / nq;
+    const int q0 = q_first + (it % nq) * KBM;
+    const size_t bh = (size_t)b * s.Hq + h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const size_t ro = (bh * s.L + q0 + (c >> 4)) * BD + (c & 15) * 8;
+      rq[i] = *reinterpret_cast<const bf16x8*>(q + ro);
+      rdo[i] = *reinterpret_cast<const bf16x8*>(dO + ro);
+      const size_t to = (bh * BD + (c >> 3)) * s.L + q0 + (c & 7) * 8;
+      rqt[i] = *reinterpret_cast<const bf16x8*>(qt + to);
+      rdot[i] = *reinterpret_cast<const bf16x8*>(dot + to);
+    }
+    if (tid < 64) rl = lse[bh * s.L + q0 + tid] * kLog2e;
+    else if (tid < 128) rl = Dd[bh * s.L + q0 + tid - 64];
+  };
+  auto lstore = [&](int buf) {
+    DkdvStage& S = sm[buf];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<bf16x8*>(&S.q[(c >> 4) * QSTR + (c & 15) * 8]) = rq[i];
+      *reinterpret_cast<bf16x8*>(&S.dO[(c >> 4) * QSTR + (c & 15) * 8]) = rdo[i];
+      *reinterpret_cast<bf16x8*>(&S.qt[(c >> 3) * TSTR + (c & 7) * 8]) = rqt[i];
+      *reinterpret_cast<bf16x8*>(&S.dOt[(c >> 3) * TSTR + (c & 7) * 8]) = rdot[i];
+    }
+    if (tid < 64) S.lse2[tid] = rl;
+    else if (tid < 128) S.Dv[tid - 64] = rl;
+  };
+
+  if (total > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < total; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < total) gload(it + 1);
+    const int q0 = q_first + (it % nq) * KBM;
+    const DkdvStage& S = sm[buf];
+    if (kw < T && q0 + KBM - 1 >= kw) {
+      f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int off = (qs * 32 + l32) * QSTR + 16 * t + 8 * hi;
+          sacc[qs] = mfma32(*reinterpret_cast<const bf16x8*>(&S.q[off]), kf[t], sacc[qs]);
+          pacc[qs] = mfma32(*reinterpret_cast<const bf16x8*>(&S.dO[off]), vf[t], pacc[qs]);
+        }
+      }
+      const bool full = (kw + 31 <= q0) && (kw + 32 <= T);
+      bf16x8 pb[4], dsb[4];
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int r0 = qs * 32 + 8 * i4 + 4 * hi;
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&S.lse2[r0]);
+          const f32x4 D4 = *reinterpret_cast<const f32x4*>(&S.Dv[r0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            float pv = exp2_fast(sacc[qs][i] * s.scale_log2 - L4[e]);
+            if (!full) {
+              const int qq = q0 + r0 + e;
+              if (my_key > qq || my_key >= T) pv = 0.f;
+            }
+            const float ds = pv * (pacc[qs][i] - D4[e]);
+            const int c = 2 * qs + (i >> 3), jj = i & 7;
+            pb[c][jj] = (bf16)pv;
+            dsb[c][jj] = (bf16)ds;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int off = (u * 32 + l32) * TSTR + 16 * c + 8 * hi;
+          dVacc[u] = mfma32(pb[c], *reinterpret_cast<const bf16x8*>(&S.dOt[off]), dVacc[u]);
+          dKacc[u] = mfma32(dsb[c], *reinterpret_cast<const bf16x8*>(&S.qt[off]), dKacc[u]);
+        }
+      }
+    }
+    if (it + 1 < total) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lane owns d = 32u + l32 of key rows kw + acc_row(i, hi)
+  if (nsplit == 1) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const size_t o = ((size_t)bg * s.KV + kw + acc_row(i, hi)) * BD + 32 * u + l32;
+        dk[o] = (bf16)(dKacc[u][i] * s.scale);
+        dv[o] = (bf16)dVacc[u][i];
+      }
+    }
+  } else {
+    const size_t plane = (size_t)s.B * s.Hkv * s.L * BD;
+    float* pk = part + (size_t)split * 2 * plane;
+    float* pv = pk + plane;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const size_t o = ((size_t)bg * s.L + kw + acc_row(i, hi)) * BD + 32 * u + l32;
+        pk[o] = dKacc[u][i] * s.scale;
+        pv[o] = dVacc[u][i];
+      }
+    }
+  }
+}
+
+hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
+                                const bf16* qt, const bf16* dot, const bf16* dout,
+                                const float* lse, const float* Dd, const int32_t* seq_T,
+                                bf16* dk, bf16* dv, float* part, int nsplit, hipStream_t st) {
+  const dim3 grid(s.B * s.Hkv * nsplit * (s.L / KBN));
+  LaunchTimer timer("bwd_dkdv_mfma", st);
+  bwd_dkdv_mfma_kernel<<<grid, 256, 0, st>>>(q, k, v, qt, dot, dout, lse, Dd, seq_T, dk, dv, part,
+                                             nsplit, s);
+  return hipGetLastError();
+}
+
+// Sum of the nsplit partial dK/dV planes, in split order, into block 0 of dk/dv.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
+                                                          int nsplit, bf16* __restrict__ dk,
+                                                          bf16* __restrict__ dv, Shape s) {
+  const size_t plane = (size_t)s.B * s.Hkv * s.L * BD;
+  const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= 2 * plane) return;
+  const bool is_v = e0 >= plane;
+  const size_t e = is_v ? e0 - plane : e0;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + (is_v ? plane : 0) + e);
+  for (int sp = 1; sp < nsplit; ++sp)
+    acc += *reinterpret_cast<const f32x4*>(part + (size_t)sp * 2 * plane + (is_v ? plane : 0) + e);
+  const size_t bg = e / ((size_t)s.L * BD), rem = e % ((size_t)s.L * BD);
+  bf16x4 w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = (bf16)acc[j];
+  *reinterpret_cast<bf16x4*>((is_v ? dv : dk) + bg * s.KV * BD + rem) = w;
+}
+
+hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
+                                  bf16* dv, hipStream_t st) {
+  const size_t n4 = (size_t)s.B * s.Hkv * s.L * BD * 2 / 4;
+  const dim3 grid((unsigned)((n4 + 255) / 256));
+  LaunchTimer timer("bwd_dkdv_reduce", st);
+  dkdv_reduce_kernel<<<grid, 256, 0, st>>>(part, nsplit, dk, dv, s);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------
+// dQ of block 0, bf16 MFMA.  Workgroup = 4 waves x 32 queries = 128 queries of one head;
+// 64-key tiles of block 0 stream through LDS.  Per wave and tile:
+//   S^T = K Q^T, dP^T = V dO^T      (A = K, V rows from LDS; B = Q, dO in registers)
+//   dS^T = P^T * (dP^T - D)         (each lane owns one query: one lse, one D)
+//   dQ^T += K^T dS^T                (A = K^T tile from LDS, B = dS^T from the accumulator)
+// ----------------------------------------------------------------------------------------
+constexpr int QBM = 128;
+constexpr int QBN = 64;
+
+struct DqStage {
+  bf16 k[QBN * QSTR];
+  bf16 v[QBN * QSTR];
+  bf16 kt[BD * TSTR];
+};
+
+template <bool FINAL>
+__global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ kt, const bf16* __restrict__ dO, const float* __restrict__ lse,
+    const float* __restrict__ Dd, const int32_t* __restrict__ seq_T, void* __restrict__ dq_out,
+    Shape s) {
+  __shared__ __attribute__((aligned(16))) DqStage sm[2];
+
+  const int n_qt = s.L / QBM;
+  int bh, rank;
+  map_block(blockIdx.x, s.B * s.Hq, bh, rank);
+  const int qtile = n_qt - 1 - rank;
+  const int b = bh / s.Hq, h = bh % s.Hq, g = h / s.G;
+  const int bg = b * s.Hkv + g;
+  const int T = clamp_T(seq_T, b, s.L);
+  const int q0 = qtile * QBM;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int qw = q0 + wave * 32;
+  const int my_q = qw + l32;
+  const size_t row = (size_t)bh * s.L + my_q;
+
+  bf16x8 qf[8], df[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    qf[t] = *reinterpret_cast<const bf16x8*>(q + row * BD + 16 * t + 8 * hi);
+    df[t] = *reinterpret_cast<const bf16x8*>(dO + row * BD + 16 * t + 8 * hi);
+  }
+  const float lse2 = lse[row] * kLog2e;
+  const float Dq = Dd[row];
+
+  const bf16* kb = k + (size_t)bg * s.KV * BD;
+  const bf16* vb = v + (size_t)bg * s.KV * BD;
+  const bf16* ktb = kt + (size_t)bg * BD * s.L;
+  const int kv_end = min(q0 + QBM, T);
+  const int ntiles = (kv_end + QBN - 1) / QBN;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
+
+  bf16x8 rk[4], rv[4], rkt[4];
+  auto gload = [&](int j) {
+    const int k0 = j * QBN;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const size_t ro = (size_t)(k0 + (c >> 4)) * BD + (c & 15) * 8;
+      rk[i] = *reinterpret_cast<const bf16x8*>(kb + ro);
+      rv[i] = *reinterpret_cast<const bf16x8*>(vb + ro);
+      rkt[i] = *reinterpret_cast<const bf16x8*>(ktb + (size_t)(c >> 3) * s.L + k0 + (c & 7) * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+    DqStage& S = sm[buf];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<bf16x8*>(&S.k[(c >> 4) * QSTR + (c & 15) * 8]) = rk[i];
+      *reinterpret_cast<bf16x8*>(&S.v[(c >> 4) * QSTR + (c & 15) * 8]) = rv[i];
+      *reinterpret_cast<bf16x8*>(&S.kt[(c >> 3) * TSTR + (c & 7) * 8]) = rkt[i];
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+    const int k0 = j * QBN;
+    const DqStage& S = sm[buf];
+    if (k0 <= qw + 31) {
+      f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int off = (st * 32 + l32) * QSTR + 16 * t + 8 * hi;
+          sacc[st] = mfma32(*reinterpret_cast<const bf16x8*>(&S.k[off]), qf[t], sacc[st]);
+          pacc[st] = mfma32(*reinterpret_cast<const bf16x8*>(&S.v[off]), df[t], pacc[st]);
+        }
+      }
+      const bool full = (k0 + QBN - 1 <= qw) && (k0 + QBN <= T);
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pv = exp2_fast(sacc[st][i] * s.scale_log2 - lse2);
+          if (!full) {
+            const int key = k0 + st * 32 + acc_row(i, hi);
+            if (key > my_q || key >= T) pv = 0.f;
+          }
+          dsb[2 * st + (i >> 3)][i & 7] = (bf16)(pv * (pacc[st][i] - Dq));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int off = (u * 32 + l32) * TSTR + 16 * c + 8 * hi;
+          acc[u] = mfma32(*reinterpret_cast<const bf16x8*>(&S.kt[off]), dsb[c], acc[u]);
+        }
+      }
+    }
+    if (j + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lane owns dQ[my_q][32u + 8*b4 + 4*hi + e] in acc[u][4*b4 + e]
+  if constexpr (FINAL) {
+    bf16* orow = reinterpret_cast<bf16*>(dq_out) + row * BD + 4 * hi;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[u][4 * b4 + e] * s.scale);
+        *reinterpret_cast<bf16x4*>(orow + 32 * u + 8 * b4) = w;
+      }
+    }
+  } else {
+    float* orow = reinterpret_cast<float*>(dq_out) + row * BD + 4 * hi;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[u][4 * b4 + e] * s.scale;
+        *reinterpret_cast<f32x4*>(orow + 32 * u + 8 * b4) = w;
+      }
+    }
+  }
+}
+
+hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
+                              const bf16* kt, const bf16* dout, const float* lse,
+                              const float* Dd, const int32_t* seq_T, void* dq, bool final_out,
+                              hipStream_t st) {
+  const dim3 grid(s.B * s.Hq * (s.L / QBM));
+  LaunchTimer timer("bwd_dq_mfma", st);
+  if (final_out)
+    bwd_dq_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, v, kt, dout, lse, Dd, seq_T, dq, s);
+  else
+    bwd_dq_mfma_kernel<false><<<grid, 256, 0, st>>>(q, k, v, kt, dout, lse, Dd, seq_T, dq, s);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------
+// Vector-ALU backward of block 0 (fp32 path).
+// dkdv: one wave per key row j of block 0; lanes take 64 queries at a time for p and ds,
+//       then split the head dimension for dV += p dO and dK += ds q (heads in order).
+// dq:   one wave per query row; lanes take 64 keys at a time, then split d for dQ += ds k.
+// ----------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_dkdv_valu_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
+    const int32_t* __restrict__ seq_T, T* __restrict__ dk, T* __restrict__ dv, Shape s) {
+  __shared__ float skv[2][D];
+  __shared__ float sp[2][64];
+  constexpr int E = D / 64;
+  const int bg = blockIdx.x / s.L, j = blockIdx.x % s.L;
+  const int b = bg / s.Hkv, g = bg % s.Hkv;
+  const int Tlen = clamp_T(seq_T, b, s.L);
+  const int lane = threadIdx.x;
+  const size_t krow = (size_t)bg * s.KV + j;
+  for (int e = lane; e < D; e += 64) {
+    skv[0][e] = to_f32(k[krow * D + e]);
+    skv[1][e] = to_f32(v[krow * D + e]);
+  }
+  __syncthreads();
+  float aK[E], aV[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) aK[e] = aV[e] = 0.f;
+  if (j < Tlen) {
+    for (int h = g * s.G; h < (g + 1) * s.G; ++h) {
+      const size_t bh = (size_t)b * s.Hq + h;
+      for (int c0 = j; c0 < s.L; c0 += 64) {  // queries i >= j see key j
+        const int i = c0 + lane;
+        float p = 0.f, ds = 0.f;
+        if (i < s.L) {
+          const T* qr = q + (bh * s.L + i) * D;
+          const T* dr = dO + (bh * s.L + i) * D;
+          float sd = 0.f, pd = 0.f;
+          for (int e = 0; e < D; ++e) {
+            sd += to_f32(qr[e]) * skv[0][e];
+            pd += to_f32(dr[e]) * skv[1][e];
+          }
+          p = exp2_fast(sd * s.scale_log2 - lse[bh * s.L + i] * kLog2e);
+          ds = p * (pd - Dd[bh * s.L + i]);
+        }
+        sp[0][lane] = p;
+        sp[1][lane] = ds;
+        __syncthreads();
+        const int cnt = min(64, s.L - c0);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int dd = lane + 64 * e;
+          float av = aV[e], ak = aK[e];
+          for (int ii = 0; ii < cnt; ++ii) {
+            const size_t r = (bh * s.L + c0 + ii) * D + dd;
+            av += sp[0][ii] * to_f32(dO[r]);
+            ak += sp[1][ii] * to_f32(q[r]);
+          }
+          aV[e] = av;
+          aK[e] = ak;
+        }
+        __syncthreads();
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int dd = lane + 64 * e;
+    dk[krow * D + dd] = from_f32<T>(aK[e] * s.scale);
+    dv[krow * D + dd] = from_f32<T>(aV[e]);
+  }
+}
+
+template <typename T>
+hipError_t launch_bwd_dkdv_valu(const Shape& s, const T* q, const T* k, const T* v,
+                                const T* dout, const float* lse, const float* Dd,
+                                const int32_t* seq_T, T* dk, T* dv, hipStream_t st) {
+  const dim3 grid(s.B * s.Hkv * s.L);
+  LaunchTimer timer("bwd_dkdv_valu", st);
+  if (s.D == 64)
+    bwd_dkdv_valu_kernel<T, 64><<<grid, 64, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dk, dv, s);
+  else
+    bwd_dkdv_valu_kernel<T, 128><<<grid, 64, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dk, dv, s);
+  return hipGetLastError();
+}
+template hipError_t launch_bwd_dkdv_valu<float>(const Shape&, const float*, const float*,
+                                                const float*, const float*, const float*,
+                                                const float*, const int32_t*, float*, float*,
+                                                hipStream_t);
+
+template <typename T, int D, bool FINAL>
+__global__ __launch_bounds__(64) void bwd_dq_valu_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
+    const int32_t* __restrict__ seq_T, void* __restrict__ dq_out, Shape s) {
+  __shared__ float sq[2][D];
+  __shared__ float sds[64];
+  constexpr int E = D / 64;
+  const int bh = blockIdx.x / s.L, i = blockIdx.x % s.L;
+  const int b = bh / s.Hq, h = bh % s.Hq, g = h / s.G;
+  const int Tlen = clamp_T(seq_T, b, s.L);
+  const int lane = threadIdx.x;
+  const size_t row = (size_t)bh * s.L + i;
+  for (int e = lane; e < D; e += 64) {
+    sq[0][e] = to_f32(q[row * D + e]);
+    sq[1][e] = to_f32(dO[row * D + e]);
+  }
+  __syncthreads();
+  const float lse2 = lse[row] * kLog2e, Di = Dd[row];
+  const int n = (i < Tlen) ? i + 1 : Tlen;
+  const T* kb = k + (size_t)(b * s.Hkv + g) * s.KV * D;
+  const T* vb = v + (size_t)(b * s.Hkv + g) * s.KV * D;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int j = c0 + lane;
+    float ds = 0.f;
+    if (j < n) {
+      float sd = 0.f, pd = 0.f;
+      for (int e = 0; e < D; ++e) {
+        sd += sq[0][e] * to_f32(kb[(size_t)j * D + e]);
+        pd += sq[1][e] * to_f32(vb[(size_t)j * D + e]);
+      }
+      const float p = exp2_fast(sd * s.scale_log2 - lse2);
+      ds = p * (pd - Di);
+    }
+    sds[lane] = ds;
+    __syncthreads();
+    const int cnt = min(64, n - c0);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int dd = lane + 64 * e;
+      float a = acc[e];
+      for (int jj = 0; jj < cnt; ++jj) a += sds[jj] * to_f32(kb[(size_t)(c0 + jj) * D + dd]);
+      acc[e] = a;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int dd = lane + 64 * e;
+    if constexpr (FINAL)
+      reinterpret_cast<T*>(dq_out)[row * D + dd] = from_f32<T>(acc[e] * s.scale);
+    else
+      reinterpret_cast<float*>(dq_out)[row * D + dd] = acc[e] * s.scale;
+  }
+}
+
+template <typename T>
+hipError_t launch_bwd_dq_valu(const Shape& s, const T* q, const T* k, const T* v, const T* dout,
+                              const float* lse, const float* Dd, const int32_t* seq_T, void* dq,
+                              bool final_out, hipStream_t st) {
+  const dim3 grid(s.B * s.Hq * s.L);
+  LaunchTimer timer("bwd_dq_valu", st);
+  if (s.D == 64) {
+    if (final_out) bwd_dq_valu_kernel<T, 64, true><<<grid, 64, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
+    else bwd_dq_valu_kernel<T, 64, false><<<grid, 64, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
+  } else {
+    if (final_out) bwd_dq_valu_kernel<T, 128, true><<<grid, 64, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
+    else bwd_dq_valu_kernel<T, 128, false><<<grid, 64, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
+  }
+  return hipGetLastError();
+}
+template hipError_t launch_bwd_dq_valu<float>(const Shape&, const float*, const float*,
+                                              const float*, const float*, const float*,
+                                              const float*, const int32_t*, void*, bool,
+                                              hipStream_t);
+
+// ----------------------------------------------------------------------------------------
+// Suffix backward + dQ finalisation.  One group of 16 lanes per (b, KV group, row i).
+// For i < T and t = 1..k (key row r = t*Q_LEN + i), per query head h of the group:
+//   p = exp(scale q_h.k_r - lse_h), dp = dO_h.v_r, ds = p (dp - D_h)
+//   dV_r = sum_h p dO_h,  dK_r = scale sum_h ds q_h,  dQ_h += scale ds k_r.
+// Rows i >= T get no suffix key: dK_r = dV_r = 0 and dQ_h is the block-0 part alone.
+// Two passes (dQ head by head, then dK/dV key row by key row) keep the register footprint
+// independent of the group size; the second pass re-reads q/dO from cache.
+// ----------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_suffix_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
+    const int32_t* __restrict__ seq_T, const float* __restrict__ dq_acc, T* __restrict__ dq,
+    T* __restrict__ dk, T* __restrict__ dv, Shape s) {
+  constexpr int E = D / 16;
+  const int sub = threadIdx.x & 15;
+  const int blocks_per_bg = (s.L + 15) / 16;
+  const int bg = blockIdx.x / blocks_per_bg;
+  const int i = (blockIdx.x % blocks_per_bg) * 16 + (threadIdx.x >> 4);
+  if (i >= s.L) return;
+  const int b = bg / s.Hkv, g = bg % s.Hkv;
+  const int Tlen = clamp_T(seq_T, b, s.L);
+  const size_t kv_base = (size_t)bg * s.KV * D + (size_t)i * D + sub * E;
+  const bool live = i < Tlen;
+
+  // pass 1: dQ
+  for (int h = g * s.G; h < (g + 1) * s.G; ++h) {
+    const size_t row = (size_t)(b * s.Hq + h) * s.L + i;
+    float acc[E];
+    load_vec<float, E>(dq_acc + row * D + sub * E, acc);
+    if (live) {
+      float qv[E], dv_[E];
+      load_vec<T, E>(q + row * D + sub * E, qv);
+      load_vec<T, E>(dO + row * D + sub * E, dv_);
+      const float lse2 = lse[row] * kLog2e, Di = Dd[row];
+      for (int t = 1; t <= s.step; ++t) {
+        float kv[E], vv[E];
+        load_vec<T, E>(k + kv_base + (size_t)t * s.L * D, kv);
+        load_vec<T, E>(v + kv_base + (size_t)t * s.L * D, vv);
+        float sd = 0.f, pd = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          sd += qv[e] * kv[e];
+          pd += dv_[e] * vv[e];
+        }
+        sd = sum16(sd);
+        pd = sum16(pd);
+        const float p = exp2_fast(sd * s.scale_log2 - lse2);
+        const float ds = p * (pd - Di) * s.scale;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += ds * kv[e];
+      }
+    }
+    store_vec<T, E>(dq + row * D + sub * E, acc);
+  }
+
+  // pass 2: dK, dV of the suffix key rows t*Q_LEN + i
+  for (int t = 1; t <= s.step; ++t) {
+    float aK[E], aV[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) aK[e] = aV[e] = 0.f;
+    if (live) {
+      float kv[E], vv[E];
+      load_vec<T, E>(k + kv_base + (size_t)t * s.L * D, kv);
+      load_vec<T, E>(v + kv_base + (size_t)t * s.L * D, vv);
+      for (int h = g * s.G; h < (g + 1) * s.G; ++h) {
+        const size_t row = (size_t)(b * s.Hq + h) * s.L + i;
+        float qv[E], dv_[E];
+        load_vec<T, E>(q + row * D + sub * E, qv);
+        load_vec<T, E>(dO + row * D + sub * E, dv_);
+        float sd = 0.f, pd = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          sd += qv[e] * kv[e];
+          pd += dv_[e] * vv[e];
+        }
+        sd = sum16(sd);
+        pd = sum16(pd);
+        const float p = exp2_fast(sd * s.scale_log2 - lse[row] * kLog2e);
+        const float ds = p * (pd - Dd[row]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          aV[e] += p * dv_[e];
+          aK[e] += ds * qv[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) aK[e] *= s.scale;
+    }
+    store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, aK);
+    store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, aV);
+  }
+}
+
+template <typename T>
+hipError_t launch_bwd_suffix(const Shape& s, const T* q, const T* k, const T* v, const T* dout,
+                             const float* lse, const float* Dd, const int32_t* seq_T,
+                             const float* dq_acc, T* dq, T* dk, T* dv, hipStream_t st) {
+  const dim3 grid(s.B * s.Hkv * ((s.L + 15) / 16));
+  LaunchTimer timer("bwd_suffix", st);
+  if (s.D == 64)
+    bwd_suffix_kernel<T, 64><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s);
+  else
+    bwd_suffix_kernel<T, 128><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s);
+  return hipGetLastError();
+}
+template hipError_t launch_bwd_suffix<float>(const Shape&, const float*, const float*,
+                                             const float*, const float*, const float*,
+                                             const float*, const int32_t*, const float*, float*,
+                                             float*, float*, hipStream_t);
+template hipError_t launch_bwd_suffix<bf16>(const Shape&, const bf16*, const bf16*, const bf16*,
+                                            const bf16*, const float*, const float*,
+                                            const int32_t*, const float*, bf16*, bf16*, bf16*,
+                                            hipStream_t);
+
+}  // namespace ttt

@@ -1,0 +1,361 @@
+// Forward kernels of TTT sparse tree attention.
+//
+// The mask is the BlockMask construction of the SpecForge paper review (§3 "Sparse Tree
+// Attention", §4 "BlockMask construction"): query i of the current TTT step sees keys
+// 0..min(i, T-1) of block 0 (the causal prefix) and, if i < T, key t*Q_LEN + i of each later
+// block t.  The causal part is dense-tileable and runs on the matrix cores; the suffix is one
+// key per query and block, so it is gathered row by row and merged into the softmax state.
+#include "launch.h"
+
+namespace ttt {
+
+// ----------------------------------------------------------------------------------------
+// Causal block-0 forward, bf16 MFMA, head_dim 128.
+//
+// Workgroup = 4 waves = 128 queries (32 per wave); the loop streams 64-key tiles of block 0
+// through LDS (double buffered, next tile prefetched into registers).  Per wave and tile:
+//   S^T[64 keys x 32 queries] = K Q^T     (A = K rows from LDS, B = Q kept in registers)
+//   online softmax on S^T (each lane owns one query; its keys sit in this lane and lane^32)
+//   O^T[128 x 32] += V^T P^T              (A = V^T from LDS, B = P^T straight from S^T)
+// Tiles past min(q0 + 128, T) are never loaded (the BlockMask "skip" class); only tiles that
+// straddle the diagonal or the T edge evaluate the mask ("partial"); the rest are "full".
+// On partial tiles P is split into bf16 hi + lo parts so that rows with few keys (where one
+// rounding of P would show in O) keep fp32-level accuracy.
+// ----------------------------------------------------------------------------------------
+constexpr int FD = 128;       // head dim
+constexpr int FBM = 128;      // queries per workgroup
+constexpr int FBN = 64;       // keys per tile
+constexpr int KSTR = FD + 8;  // K tile row stride (elements): 272 B rows spread the banks
+constexpr int VSTR = FBN + 8; // V^T tile row stride: 144 B
+
+template <bool FINAL>
+__global__ __launch_bounds__(256) void fwd_causal_mfma_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ vt,
+    const int32_t* __restrict__ seq_T, void* __restrict__ o_out, float* __restrict__ lse_out,
+    Shape s) {
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][FBN * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][FD * VSTR];
+
+  const int n_qt = s.L / FBM;
+  int bh, rank;
+  map_block(blockIdx.x, s.B * s.Hq, bh, rank);
+  const int qt = n_qt - 1 - rank;  // the last query tile sees the most keys: run it first
+  const int b = bh / s.Hq, h = bh % s.Hq, g = h / s.G;
+  const int T = clamp_T(seq_T, b, s.L);
+  const int q0 = qt * FBM;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int qw = q0 + wave * 32;
+  const int my_q = qw + l32;
+
+  bf16x8 qf[8];
+  {
+    const bf16* qrow = q + ((size_t)bh * s.L + my_q) * FD + 8 * hi;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qf[t] = *reinterpret_cast<const bf16x8*>(qrow + 16 * t);
+  }
+  const bf16* kb = k + (size_t)(b * s.Hkv + g) * s.KV * FD;
+  const bf16* vb = vt + (size_t)(b * s.Hkv + g) * FD * s.L;
+
+  const int kv_end = min(q0 + FBM, T);
+  const int ntiles = (kv_end + FBN - 1) / FBN;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
+  float m = kNegInf, l = 0.f;
+
+  bf16x8 rk[4], rv[4];
+  auto gload = [&](int j) {
+    const int k0 = j * FBN;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      rk[i] = *reinterpret_cast<const bf16x8*>(kb + (size_t)(k0 + (c >> 4)) * FD + (c & 15) * 8);
+      rv[i] = *reinterpret_cast<const bf16x8*>(vb + (size_t)(c >> 3) * s.L + k0 + (c & 7) * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<bf16x8*>(&sK[buf][(c >> 4) * KSTR + (c & 15) * 8]) = rk[i];
+      *reinterpret_cast<bf16x8*>(&sV[buf][(c >> 3) * VSTR + (c & 7) * 8]) = rv[i];
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+    const int k0 = j * FBN;
+    if (k0 <= qw + 31) {  // some query of this wave can see a key of the tile
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(&sK[buf][(st * 32 + l32) * KSTR + 16 * t + 8 * hi]);
+          sacc[st] = mfma32(a, qf[t], sacc[st]);
+        }
+      }
+      const bool full = (k0 + FBN - 1 <= qw) && (k0 + FBN <= T);
+      float rmax = kNegInf;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = sacc[st][i] * s.scale_log2;
+          if (!full) {
+            const int key = k0 + st * 32 + acc_row(i, hi);
+            if (key > my_q || key >= T) x = kNegInf;
+          }
+          sacc[st][i] = x;
+          rmax = fmaxf(rmax, x);
+        }
+      }
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+      const float m_new = fmaxf(m, rmax);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = exp2_fast(m - m_use);
+      float lsum = 0.f;
+      bf16x8 pf[4], pl[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float pv = exp2_fast(sacc[c >> 1][8 * (c & 1) + jj] - m_use);
+          lsum += pv;
+          const bf16 ph = (bf16)pv;
+          pf[c][jj] = ph;
+          pl[c][jj] = (bf16)(pv - (float)ph);
+        }
+      }
+      lsum += __shfl_xor(lsum, 32);
+      l = l * alpha + lsum;
+      m = m_new;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] *= alpha;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(&sV[buf][(u * 32 + l32) * VSTR + 16 * c + 8 * hi]);
+          acc[u] = mfma32(a, pf[c], acc[u]);
+          if (!full) acc[u] = mfma32(a, pl[c], acc[u]);
+        }
+      }
+    }
+    if (j + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
+  const float lse = l > 0.f ? (m + __log2f(l)) * kLn2 : kNegInf;
+  const size_t row = (size_t)bh * s.L + my_q;
+  if (hi == 0) lse_out[row] = lse;
+  // lane owns O[my_q][32u + 8*b4 + 4*hi + e] in acc[u][4*b4 + e]
+  if constexpr (FINAL) {
+    bf16* orow = reinterpret_cast<bf16*>(o_out) + row * FD + 4 * hi;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[u][4 * b4 + e] * inv_l);
+        *reinterpret_cast<bf16x4*>(orow + 32 * u + 8 * b4) = w;
+      }
+    }
+  } else {
+    float* orow = reinterpret_cast<float*>(o_out) + row * FD + 4 * hi;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[u][4 * b4 + e] * inv_l;
+        *reinterpret_cast<f32x4*>(orow + 32 * u + 8 * b4) = w;
+      }
+    }
+  }
+}
+
+hipError_t launch_fwd_causal_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* vt,
+                                  const int32_t* seq_T, void* o, float* lse, bool final_out,
+                                  hipStream_t st) {
+  const dim3 grid(s.B * s.Hq * (s.L / FBM));
+  LaunchTimer timer("fwd_causal_mfma", st);
+  if (final_out)
+    fwd_causal_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, vt, seq_T, o, lse, s);
+  else
+    fwd_causal_mfma_kernel<false><<<grid, 256, 0, st>>>(q, k, vt, seq_T, o, lse, s);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------
+// Causal block-0 forward on the vector ALUs (fp32 path).  One wave per query row: lanes take
+// 64 keys at a time for the logits, then split the head dimension for P V.
+// ----------------------------------------------------------------------------------------
+template <typename T, int D, bool FINAL>
+__global__ __launch_bounds__(64) void fwd_causal_valu_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ seq_T, void* __restrict__ o_out, float* __restrict__ lse_out,
+    Shape s) {
+  __shared__ float sq[D];
+  __shared__ float sp[64];
+  constexpr int E = D / 64;
+  const int bh = blockIdx.x / s.L, i = blockIdx.x % s.L;
+  const int b = bh / s.Hq, h = bh % s.Hq, g = h / s.G;
+  const int Tlen = clamp_T(seq_T, b, s.L);
+  const int lane = threadIdx.x;
+  const size_t row = (size_t)bh * s.L + i;
+  for (int e = lane; e < D; e += 64) sq[e] = to_f32(q[row * D + e]);
+  __syncthreads();
+  const int n = (i < Tlen) ? i + 1 : Tlen;  // keys 0..n-1 of block 0
+  const T* kb = k + (size_t)(b * s.Hkv + g) * s.KV * D;
+  const T* vb = v + (size_t)(b * s.Hkv + g) * s.KV * D;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float m = kNegInf, l = 0.f;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    const int j = c0 + lane;
+    float x = kNegInf;
+    if (j < n) {
+      float dot = 0.f;
+      for (int e = 0; e < D; ++e) dot += sq[e] * to_f32(kb[(size_t)j * D + e]);
+      x = dot * s.scale_log2;
+    }
+    const float m_new = fmaxf(m, wave_max(x));  // finite: key c0 is visible
+    const float alpha = exp2_fast(m - m_new);
+    const float p = exp2_fast(x - m_new);
+    l = l * alpha + wave_sum(p);
+    m = m_new;
+    sp[lane] = p;
+    __syncthreads();
+    const int cnt = min(64, n - c0);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float a = acc[e] * alpha;
+      const int dd = lane + 64 * e;
+      for (int jj = 0; jj < cnt; ++jj) a += sp[jj] * to_f32(vb[(size_t)(c0 + jj) * D + dd]);
+      acc[e] = a;
+    }
+    __syncthreads();
+  }
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
+  if (lane == 0) lse_out[row] = l > 0.f ? (m + __log2f(l)) * kLn2 : kNegInf;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int dd = lane + 64 * e;
+    if constexpr (FINAL)
+      reinterpret_cast<T*>(o_out)[row * D + dd] = from_f32<T>(acc[e] * inv_l);
+    else
+      reinterpret_cast<float*>(o_out)[row * D + dd] = acc[e] * inv_l;
+  }
+}
+
+template <typename T>
+hipError_t launch_fwd_causal_valu(const Shape& s, const T* q, const T* k, const T* v,
+                                  const int32_t* seq_T, void* o, float* lse, bool final_out,
+                                  hipStream_t st) {
+  const dim3 grid(s.B * s.Hq * s.L);
+  LaunchTimer timer("fwd_causal_valu", st);
+  if (s.D == 64) {
+    if (final_out) fwd_causal_valu_kernel<T, 64, true><<<grid, 64, 0, st>>>(q, k, v, seq_T, o, lse, s);
+    else fwd_causal_valu_kernel<T, 64, false><<<grid, 64, 0, st>>>(q, k, v, seq_T, o, lse, s);
+  } else {
+    if (final_out) fwd_causal_valu_kernel<T, 128, true><<<grid, 64, 0, st>>>(q, k, v, seq_T, o, lse, s);
+    else fwd_causal_valu_kernel<T, 128, false><<<grid, 64, 0, st>>>(q, k, v, seq_T, o, lse, s);
+  }
+  return hipGetLastError();
+}
+template hipError_t launch_fwd_causal_valu<float>(const Shape&, const float*, const float*,
+                                                  const float*, const int32_t*, void*, float*,
+                                                  bool, hipStream_t);
+
+// ----------------------------------------------------------------------------------------
+// Suffix forward: the diagonal keys t*Q_LEN + i (t = 1..k) of query row i < T.
+//
+// One aligned group of 16 lanes per (b, KV group, row i); each lane holds D/16 contiguous
+// elements of a row, so one K or V row is a single 256-byte coalesced read that serves every
+// query head of the group.  The causal result arrives normalised (o_c, lse_c), which is the
+// same softmax state as (m = lse_c, l = 1, acc = o_c); each diagonal logit is merged in with
+// the usual rescaling, then o = acc / l and lse = m + log l.  Rows i >= T only convert o_c.
+// ----------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd_suffix_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ seq_T, const float* __restrict__ oc,
+    const float* __restrict__ lsec, T* __restrict__ o, float* __restrict__ lse, Shape s) {
+  constexpr int E = D / 16;
+  const int sub = threadIdx.x & 15;
+  const int blocks_per_bg = (s.L + 15) / 16;
+  const int bg = blockIdx.x / blocks_per_bg;
+  const int i = (blockIdx.x % blocks_per_bg) * 16 + (threadIdx.x >> 4);
+  if (i >= s.L) return;
+  const int b = bg / s.Hkv, g = bg % s.Hkv;
+  const int Tlen = clamp_T(seq_T, b, s.L);
+  const size_t kv_base = (size_t)bg * s.KV * D + (size_t)i * D + sub * E;
+  for (int h = g * s.G; h < (g + 1) * s.G; ++h) {
+    const size_t row = (size_t)(b * s.Hq + h) * s.L + i;
+    float acc[E];
+    load_vec<float, E>(oc + row * D + sub * E, acc);
+    const float lc = lsec[row];
+    float m = lc * kLog2e;
+    float l = (lc == kNegInf) ? 0.f : 1.f;
+    if (i < Tlen) {
+      float qv[E];
+      load_vec<T, E>(q + row * D + sub * E, qv);
+      for (int t = 1; t <= s.step; ++t) {
+        float kv[E], vv[E];
+        load_vec<T, E>(k + kv_base + (size_t)t * s.L * D, kv);
+        load_vec<T, E>(v + kv_base + (size_t)t * s.L * D, vv);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dot += qv[e] * kv[e];
+        const float x = sum16(dot) * s.scale_log2;
+        const float m_new = fmaxf(m, x);
+        const float alpha = exp2_fast(m - m_new), beta = exp2_fast(x - m_new);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = acc[e] * alpha + beta * vv[e];
+        l = l * alpha + beta;
+        m = m_new;
+      }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float ov[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) ov[e] = acc[e] * inv;
+    store_vec<T, E>(o + row * D + sub * E, ov);
+    if (sub == 0) lse[row] = l > 0.f ? (m + __log2f(l)) * kLn2 : kNegInf;
+  }
+}
+
+template <typename T>
+hipError_t launch_fwd_suffix(const Shape& s, const T* q, const T* k, const T* v,
+                             const int32_t* seq_T, const float* oc, const float* lsec, T* o,
+                             float* lse, hipStream_t st) {
+  const dim3 grid(s.B * s.Hkv * ((s.L + 15) / 16));
+  LaunchTimer timer("fwd_suffix", st);
+  if (s.D == 64)
+    fwd_suffix_kernel<T, 64><<<grid, 256, 0, st>>>(q, k, v, seq_T, oc, lsec, o, lse, s);
+  else
+    fwd_suffix_kernel<T, 128><<<grid, 256, 0, st>>>(q, k, v, seq_T, oc, lsec, o, lse, s);
+  return hipGetLastError();
+}
+template hipError_t launch_fwd_suffix<float>(const Shape&, const float*, const float*,
+                                             const float*, const int32_t*, const float*,
+                                             const float*, float*, float*, hipStream_t);
+template hipError_t launch_fwd_suffix<bf16>(const Shape&, const bf16*, const bf16*, const bf16*,
+                                            const int32_t*, const float*, const float*, bf16*,
+                                            float*, hipStream_t);
+
+}  // namespace ttt

@@ -1,0 +1,246 @@
+"""Python binding of the C ABI in ``include/ttt_attn.h`` (ctypes; argument marshalling only).
+
+Every step of the computation runs in the HIP library ``libttt_attn.so``; this module only
+checks tensor metadata, allocates outputs and workspace with torch, and passes pointers and
+the current HIP stream.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttt_attn.so")
+
+TTT_DTYPE_F32 = 0
+TTT_DTYPE_BF16 = 1
+
+STATUS = {
+    0: "TTT_OK", -1: "TTT_E_NULL", -2: "TTT_E_SHAPE", -3: "TTT_E_UNSUPPORTED",
+    -4: "TTT_E_ALIGN", -5: "TTT_E_WORKSPACE", -6: "TTT_E_HIP",
+}
+
+# Every symbol the header declares.
+EXPORTS = (
+    "ttt_attn_fwd_workspace_size", "ttt_attn_bwd_workspace_size", "ttt_attn_fwd", "ttt_attn_bwd",
+    "ttt_attn_status_string", "ttt_attn_version", "ttt_attn_timing_enable",
+    "ttt_attn_timing_read", "ttt_attn_timing_reset",
+)
+
+
+class TTTError(RuntimeError):
+    def __init__(self, code: int, text: str):
+        super().__init__(f"{STATUS.get(code, code)}: {text}")
+        self.code = code
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+        ("q_len", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ttt_step", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m masked_attention_eagle_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Params)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.ttt_attn_fwd_workspace_size.argtypes = [P]
+    lib.ttt_attn_fwd_workspace_size.restype = sz
+    lib.ttt_attn_bwd_workspace_size.argtypes = [P]
+    lib.ttt_attn_bwd_workspace_size.restype = sz
+    lib.ttt_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ttt_attn_fwd.restype = ctypes.c_int
+    lib.ttt_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ttt_attn_bwd.restype = ctypes.c_int
+    lib.ttt_attn_status_string.argtypes = [ctypes.c_int]
+    lib.ttt_attn_status_string.restype = ctypes.c_char_p
+    lib.ttt_attn_version.argtypes = []
+    lib.ttt_attn_version.restype = ctypes.c_int
+    lib.ttt_attn_timing_enable.argtypes = [ctypes.c_int]
+    lib.ttt_attn_timing_enable.restype = ctypes.c_int
+    lib.ttt_attn_timing_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
+    lib.ttt_attn_timing_read.restype = ctypes.c_int
+    lib.ttt_attn_timing_reset.argtypes = []
+    lib.ttt_attn_timing_reset.restype = None
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().ttt_attn_status_string(code).decode()
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise TTTError(code, status_string(code))
+
+
+def make_params(B: int, Hq: int, Hkv: int, L: int, d: int, step: int, scale: float, dtype: int) -> Params:
+    return Params(B, Hq, Hkv, L, d, step, float(scale), dtype)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return TTT_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return TTT_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _params_from(q, k, scale) -> Params:
+    B, Hq, L, d = q.shape
+    Bk, Hkv, KV, dk = k.shape
+    if Bk != B or dk != d or KV % L != 0:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q shape {tuple(q.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return make_params(B, Hq, Hkv, L, d, KV // L - 1, scale, _dtype_code(q))
+
+
+def _require(t, name, dtype=None, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def fwd_workspace_size(p: Params) -> int:
+    return int(load().ttt_attn_fwd_workspace_size(ctypes.byref(p)))
+
+
+def bwd_workspace_size(p: Params) -> int:
+    return int(load().ttt_attn_bwd_workspace_size(ctypes.byref(p)))
+
+
+def _workspace(nbytes: int, device):
+    import torch
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def ttt_attn_fwd(q, k, v, seq_T, scale: Optional[float] = None, out=None, lse=None,
+                 workspace=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """o, lse = masked attention of q [B,Hq,L,d] over k, v [B,Hkv,(step+1)L,d].
+
+    seq_T: int32 [B] on the GPU.  The TTT step is k.shape[2] // L - 1.
+    """
+    import torch
+    lib = load()
+    p = _params_from(q, k, scale)
+    _require(q, "q")
+    _require(k, "k", q.dtype)
+    _require(v, "v", q.dtype, k.shape)
+    _require(seq_T, "seq_T", torch.int32, (q.shape[0],))
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o, "out", q.dtype, q.shape)
+    _require(lse_t, "lse", torch.float32, q.shape[:3])
+    need = fwd_workspace_size(p)
+    if need == 0 and p.dtype not in (TTT_DTYPE_F32, TTT_DTYPE_BF16):
+        raise TTTError(-3, "unsupported")
+    ws = _workspace(need, q.device) if workspace is None else workspace
+    _check(lib.ttt_attn_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            seq_T.data_ptr(), o.data_ptr(), lse_t.data_ptr(), ws.data_ptr(),
+                            ws.numel(), _stream()))
+    return o, lse_t
+
+
+def ttt_attn_bwd(q, k, v, seq_T, o, lse, dout, scale: Optional[float] = None, dq=None, dk=None,
+                 dv=None, workspace=None):
+    """dq, dk, dv: gradients of sum(dout * o) for the o/lse of ttt_attn_fwd."""
+    import torch
+    lib = load()
+    p = _params_from(q, k, scale)
+    _require(q, "q")
+    _require(k, "k", q.dtype)
+    _require(v, "v", q.dtype, k.shape)
+    _require(seq_T, "seq_T", torch.int32, (q.shape[0],))
+    _require(o, "o", q.dtype, q.shape)
+    _require(lse, "lse", torch.float32, q.shape[:3])
+    _require(dout, "dout", q.dtype, q.shape)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _require(dq, "dq", q.dtype, q.shape)
+    _require(dk, "dk", q.dtype, k.shape)
+    _require(dv, "dv", q.dtype, k.shape)
+    need = bwd_workspace_size(p)
+    ws = _workspace(need, q.device) if workspace is None else workspace
+    _check(lib.ttt_attn_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            seq_T.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+                            _stream()))
+    return dq, dk, dv
+
+
+def timing_enable(on: bool) -> bool:
+    return bool(load().ttt_attn_timing_enable(1 if on else 0))
+
+
+def timing_reset() -> None:
+    load().ttt_attn_timing_reset()
+
+
+def timing_read() -> dict:
+    """{kernel name: (launches, total ms)} accumulated since the last reset."""
+    arr = (KernelTime * 64)()
+    n = load().ttt_attn_timing_read(arr, 64)
+    if n < 0:
+        raise TTTError(n, status_string(n))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}
+
+
+def _autograd_fn():
+    import torch
+
+    class TTTAttentionFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, seq_T, scale):
+            o, lse = ttt_attn_fwd(q, k, v, seq_T, scale)
+            ctx.save_for_backward(q, k, v, seq_T, o, lse)
+            ctx.scale = scale
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, seq_T, o, lse = ctx.saved_tensors
+            dq, dk, dv = ttt_attn_bwd(q, k, v, seq_T, o, lse, do.contiguous(), ctx.scale)
+            return dq, dk, dv, None, None
+
+    return TTTAttentionFn
+
+
+def ttt_attention(q, k, v, seq_T, scale: Optional[float] = None):
+    """Autograd-aware wrapper: returns o; backward runs ttt_attn_bwd."""
+    return _autograd_fn().apply(q, k, v, seq_T, scale)
+
+
+fwd = ttt_attn_fwd
+bwd = ttt_attn_bwd

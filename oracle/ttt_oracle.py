@@ -43,8 +43,8 @@ import numpy as np
 ROW_CHUNK = 1024  # rows per block of the dense computation (memory bound only)
 
 
-def mask(q_len: int, ttt_step: int, valid_len: int) -> np.ndarray:
-    """Boolean mask M of shape [Q_LEN, (ttt_step + 1) * Q_LEN].
+def mask_rows(q_len: int, ttt_step: int, valid_len: int, r0: int, r1: int) -> np.ndarray:
+    """Rows [r0, r1) of the boolean mask M of shape [Q_LEN, (ttt_step + 1) * Q_LEN].
 
     Written term by term from the BlockMask construction formulas
     (review §3 "BlockMask construction algorithm", §4 "BlockMask construction").
@@ -53,7 +53,7 @@ def mask(q_len: int, ttt_step: int, valid_len: int) -> np.ndarray:
     L = int(q_len)
     kv_len = (int(ttt_step) + 1) * L
     T = int(valid_len)
-    q_i = np.arange(L, dtype=np.int64)[:, None]
+    q_i = np.arange(r0, r1, dtype=np.int64)[:, None]
     kv_i = np.arange(kv_len, dtype=np.int64)[None, :]
     m_causal = q_i >= kv_i
     m_pad_causal = kv_i < T
@@ -63,6 +63,20 @@ def mask(q_len: int, ttt_step: int, valid_len: int) -> np.ndarray:
     m_diag = ((kv_i - q_i) % L) == 0
     M_suffix = m_suffix & m_pad_suffix & m_diag
     return M_causal | M_suffix
+
+
+def mask(q_len: int, ttt_step: int, valid_len: int) -> np.ndarray:
+    """The whole mask M, shape [Q_LEN, (ttt_step + 1) * Q_LEN]."""
+    return mask_rows(q_len, ttt_step, valid_len, 0, int(q_len))
+
+
+def _chunk(q_len, ttt_step, valid_len, r0, r1):
+    """Mask rows [r0, r1) restricted to the key columns that at least one of those rows may
+    see.  Every other column holds exp(-inf) = 0 in each softmax sum and gradient, so leaving
+    it out changes no result; it only keeps the dense blocks small."""
+    Mr = mask_rows(q_len, ttt_step, valid_len, r0, r1)
+    cols = np.nonzero(Mr.any(axis=0))[0]
+    return Mr[:, cols], cols
 
 
 def _check_shapes(q, k, v, seq_T):
@@ -89,21 +103,20 @@ def forward(q, k, v, seq_T, scale):
     o = np.zeros((B, Hq, L, v.shape[3]))
     lse = np.full((B, Hq, L), -np.inf)
     for b in range(B):
-        M = mask(L, step, int(seq_T[b]))
-        for h in range(Hq):
-            g = h // G
-            for r0 in range(0, L, ROW_CHUNK):
-                r1 = min(L, r0 + ROW_CHUNK)
-                S = scale * (q[b, h, r0:r1] @ k[b, g].T)
-                Mr = M[r0:r1]
+        for r0 in range(0, L, ROW_CHUNK):
+            r1 = min(L, r0 + ROW_CHUNK)
+            Mr, cols = _chunk(L, step, int(seq_T[b]), r0, r1)
+            for h in range(Hq):
+                g = h // G
+                S = scale * (q[b, h, r0:r1] @ k[b, g, cols].T)
                 S = np.where(Mr, S, -np.inf)
                 nonempty = Mr.any(axis=1)
-                m = np.where(nonempty, S.max(axis=1), 0.0)
+                m = np.where(nonempty, S.max(axis=1, initial=-np.inf), 0.0)
                 P = np.exp(S - m[:, None])  # exp(-inf) = 0 off the mask
                 l = P.sum(axis=1)
                 safe_l = np.where(nonempty, l, 1.0)
                 P = P / safe_l[:, None]
-                o[b, h, r0:r1] = P @ v[b, g]
+                o[b, h, r0:r1] = P @ v[b, g, cols]
                 lse[b, h, r0:r1] = np.where(nonempty, m + np.log(safe_l), -np.inf)
     return o, lse
 
@@ -129,25 +142,25 @@ def backward(q, k, v, seq_T, scale, do, o=None):
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for b in range(B):
-        M = mask(L, step, int(seq_T[b]))
-        for h in range(Hq):
-            g = h // G
-            for r0 in range(0, L, ROW_CHUNK):
-                r1 = min(L, r0 + ROW_CHUNK)
-                Mr = M[r0:r1]
-                S = np.where(Mr, scale * (q[b, h, r0:r1] @ k[b, g].T), -np.inf)
+        for r0 in range(0, L, ROW_CHUNK):
+            r1 = min(L, r0 + ROW_CHUNK)
+            Mr, cols = _chunk(L, step, int(seq_T[b]), r0, r1)
+            for h in range(Hq):
+                g = h // G
+                Kc, Vc = k[b, g, cols], v[b, g, cols]
+                S = np.where(Mr, scale * (q[b, h, r0:r1] @ Kc.T), -np.inf)
                 nonempty = Mr.any(axis=1)
-                m = np.where(nonempty, S.max(axis=1), 0.0)
+                m = np.where(nonempty, S.max(axis=1, initial=-np.inf), 0.0)
                 P = np.exp(S - m[:, None])
                 l = np.where(nonempty, P.sum(axis=1), 1.0)
                 P = P / l[:, None]
                 dO = do[b, h, r0:r1]
                 D = (dO * o[b, h, r0:r1]).sum(axis=1)
-                dP = dO @ v[b, g].T
+                dP = dO @ Vc.T
                 dS = P * (dP - D[:, None])
-                dq[b, h, r0:r1] = scale * (dS @ k[b, g])
-                dk[b, g] += scale * (dS.T @ q[b, h, r0:r1])
-                dv[b, g] += P.T @ dO
+                dq[b, h, r0:r1] = scale * (dS @ Kc)
+                dk[b, g, cols] += scale * (dS.T @ q[b, h, r0:r1])
+                dv[b, g, cols] += P.T @ dO
     return dq, dk, dv
 
 

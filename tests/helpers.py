@@ -1,0 +1,68 @@
+"""Shared helpers of the GPU parity tests: device transfer, the HIP calls, and the tolerance checks.
+
+Tolerances (max-abs for o and lse, normalised max error max|d|/max|ref| for gradients):
+  fp32 workloads : 1e-5 max-abs on every output;
+  bf16 workloads : o 1e-2, lse 1e-3, dq/dk/dv 2e-2 normalised.
+"""
+import numpy as np
+
+TOL_F32 = 1e-5
+TOL_O, TOL_LSE, TOL_GRAD = 1e-2, 1e-3, 2e-2
+
+
+def to_dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device="cuda", dtype=dtype).contiguous()
+
+
+def to_np(t):
+    import torch
+    return t.detach().to(dtype=torch.float64).cpu().numpy()
+
+
+def gpu_fwd_bwd(lib, q, k, v, do, T, scale, dtype_name, with_bwd=True):
+    import torch
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    qd, kd, vd, dod = (to_dev(x, dt) for x in (q, k, v, do))
+    Td = torch.as_tensor(np.asarray(T, dtype=np.int32), device="cuda")
+    o, lse = lib.ttt_attn_fwd(qd, kd, vd, Td, scale)
+    out = {"o": to_np(o), "lse": to_np(lse)}
+    if with_bwd:
+        dq, dk, dv = lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, scale)
+        out.update(dq=to_np(dq), dk=to_np(dk), dv=to_np(dv))
+    torch.cuda.synchronize()
+    return out
+
+
+def _lse_err(got, ref):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), "empty-row lse must be -inf on both sides"
+    return float(np.abs(got[fin] - ref[fin]).max()) if fin.any() else 0.0
+
+
+def errors(got, ref):
+    e = {"o": float(np.abs(got["o"] - ref["o"]).max()) if ref["o"].size else 0.0,
+         "lse": _lse_err(got["lse"], ref["lse"])}
+    for name in ("dq", "dk", "dv"):
+        if name in got and name in ref:
+            den = np.abs(ref[name]).max()
+            diff = np.abs(got[name] - ref[name]).max()
+            e[name + "_abs"] = float(diff)
+            e[name] = float(diff / den) if den > 0 else float(diff)
+    return e
+
+
+def check(got, ref, dtype_name, label=""):
+    e = errors(got, ref)
+    if dtype_name == "f32":
+        for name in ("o", "lse", "dq_abs", "dk_abs", "dv_abs"):
+            if name in e:
+                assert e[name] <= TOL_F32, f"{label} {name} max-abs error {e[name]:.3g} > {TOL_F32}"
+    else:
+        assert e["o"] <= TOL_O, f"{label} o max-abs error {e['o']:.4g}"
+        assert e["lse"] <= TOL_LSE, f"{label} lse max-abs error {e['lse']:.4g}"
+        for name in ("dq", "dk", "dv"):
+            if name in e:
+                assert e[name] <= TOL_GRAD, f"{label} {name} normalised error {e[name]:.4g}"
+    return e

@@ -1,0 +1,108 @@
+"""CPU-side checks of the C ABI: the library loads, exports what the header declares, sizes its
+workspace, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from masked_attention_eagle_amd import ttt_attn as A
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ttt_attn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = A.load()
+    declared = header_functions()
+    assert set(declared) == set(A.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.ttt_attn_version() == 100
+
+
+def test_status_strings():
+    for code in A.STATUS:
+        assert A.status_string(code)
+    assert A.status_string(12345) == "unknown status"
+
+
+def P(**kw):
+    base = dict(B=2, Hq=32, Hkv=8, L=4096, d=128, step=3, scale=0.088, dtype=A.TTT_DTYPE_BF16)
+    base.update(kw)
+    return A.make_params(base["B"], base["Hq"], base["Hkv"], base["L"], base["d"], base["step"],
+                         base["scale"], base["dtype"])
+
+
+def test_workspace_sizes():
+    p = P()
+    B, Hq, Hkv, L, d = 2, 32, 8, 4096, 128
+    fwd = A.fwd_workspace_size(p)
+    # bf16 V^T copy + fp32 causal state (o_c, lse_c) for step > 0
+    assert fwd == B * Hkv * d * L * 2 + B * Hq * L * d * 4 + B * Hq * L * 4
+    assert A.fwd_workspace_size(P(step=0)) == B * Hkv * d * L * 2
+    assert A.fwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, step=0)) == 0
+    bwd = A.bwd_workspace_size(p)
+    rows = B * Hq * L
+    assert bwd == rows * 4 + rows * d * 4 + 2 * rows * d * 2 + B * Hkv * L * d * 2
+    # 1 batch x 8 KV heads x 32 key tiles < 512 workgroups: heads split in two, fp32 partials
+    p4 = P(B=1, Hq=64)
+    rows4 = 64 * L
+    assert A.bwd_workspace_size(p4) == (rows4 * 4 + rows4 * d * 4 + 2 * rows4 * d * 2 +
+                                       8 * L * d * 2 + 2 * 2 * 8 * L * d * 4)
+    assert A.fwd_workspace_size(P(Hq=30)) == 0  # invalid params -> 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(Hq=30), -2), (dict(step=-1), -2), (dict(L=-4), -2),
+    (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2),
+    (dict(d=64), -3), (dict(L=4000), -3), (dict(dtype=7), -3),
+    (dict(dtype=A.TTT_DTYPE_F32, d=96), -3), (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10), -2),
+])
+def test_validation_errors(kw, code):
+    lib = A.load()
+    p = P(**kw)
+    f = ctypes.c_void_p(16)
+    rc = lib.ttt_attn_fwd(ctypes.byref(p), f, f, f, f, f, f, f, 1 << 40, None)
+    assert rc == code
+    rc = lib.ttt_attn_bwd(ctypes.byref(p), f, f, f, f, f, f, f, f, f, f, f, 1 << 40, None)
+    assert rc == code
+
+
+def test_null_align_workspace_errors():
+    lib = A.load()
+    p = P()
+    good = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.ttt_attn_fwd(None, good, good, good, good, good, good, good, 1 << 40, None) == -1
+    assert lib.ttt_attn_fwd(ctypes.byref(p), None, good, good, good, good, good, good, 1 << 40, None) == -1
+    assert lib.ttt_attn_fwd(ctypes.byref(p), good, good, good, good, good, good, None, 1 << 40, None) == -1
+    assert lib.ttt_attn_fwd(ctypes.byref(p), good, good, good, good, good, good, good, 16, None) == -5
+    assert lib.ttt_attn_fwd(ctypes.byref(p), good, odd, good, good, good, good, good, 1 << 40, None) == -4
+    args = [good] * 11
+    assert lib.ttt_attn_bwd(ctypes.byref(p), *args, 16, None) == -5
+    args[9] = odd
+    assert lib.ttt_attn_bwd(ctypes.byref(p), *args, 1 << 40, None) == -4
+    args[9] = None
+    assert lib.ttt_attn_bwd(ctypes.byref(p), *args, 1 << 40, None) == -1
+
+
+def test_timing_api_without_launches():
+    was = A.timing_enable(True)
+    A.timing_reset()
+    assert A.timing_read() == {}
+    A.timing_enable(was)
+
+
+def test_oracle_is_not_imported_by_the_product():
+    pkg = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "masked_attention_eagle_amd")
+    pat = re.compile(r"^\s*(from\s+oracle\b|import\s+oracle\b)|ttt_oracle|#include\s+.*oracle", re.M)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cuh", ".h", ".cpp")):
+                assert not pat.search(open(os.path.join(root, f)).read()), f

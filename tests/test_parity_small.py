@@ -1,0 +1,82 @@
+"""GPU vs oracle on small shapes that still span several tiles, with the edge cases of the mask:
+T = 0 (every row empty), T = 1, T on and next to tile edges, T = Q_LEN, T outside [0, Q_LEN]
+(clamped), GQA group sizes 1..8, TTT steps 0..3, and a peaky-logit variant."""
+import numpy as np
+import pytest
+
+from masked_attention_eagle_amd import inputs
+from oracle import ttt_oracle as O
+from tests.helpers import check, gpu_fwd_bwd
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(lib, seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult=1.0, T_oracle=None):
+    q, k, v, do, Tarr = inputs.make_case(seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult)
+    scale = 1.0 / np.sqrt(d)
+    print(f"case seed={seed} B={B} Hq={Hq} Hkv={Hkv} d={d} L={L} step={step} T={list(Tarr)} {dtype}", flush=True)
+    got = gpu_fwd_bwd(lib, q, k, v, do, Tarr, scale, dtype)
+    To = Tarr if T_oracle is None else T_oracle
+    o, lse = O.forward(q, k, v, To, scale)
+    dq, dk, dv = O.backward(q, k, v, To, scale, do, o)
+    ref = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+    return check(got, ref, dtype, f"seed={seed} step={step} T={list(Tarr)}")
+
+
+# ------------------------------------------------------------------ fp32 path
+@pytest.mark.parametrize("step", [0, 1, 2])
+def test_tiny_fp32_workload(gpu_lib, step):
+    """The tiny fp32 workload (B1 Hq2 Hkv1 d64 L128 T100) at every step up to 2."""
+    w = inputs.WORKLOADS[1]
+    q = inputs.q_at(w, step)
+    k, v = inputs.kv_stack(w, step)
+    do = inputs.do_at(w, step)
+    T = inputs.seq_lengths(w)
+    got = gpu_fwd_bwd(gpu_lib, q, k, v, do, T, w.scale, "f32")
+    o, lse = O.forward(q, k, v, T, w.scale)
+    dq, dk, dv = O.backward(q, k, v, T, w.scale, do, o)
+    e = check(got, dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv), "f32", f"tiny step={step}")
+    print("tiny fp32 errors", e)
+
+
+@pytest.mark.parametrize("step,T,d,L", [(0, (37, 0), 64, 96), (2, (1, 77), 128, 64), (3, (64, 65), 64, 130)])
+def test_fp32_edge_cases(gpu_lib, step, T, d, L):
+    run_case(gpu_lib, 100 + step, 2, 4, 2, d, L, step, T, "f32")
+
+
+# ------------------------------------------------------------------ bf16 matrix-core path
+@pytest.mark.parametrize("step", [0, 1, 2, 3])
+@pytest.mark.parametrize("T", [(256, 256), (0, 256), (1, 255), (63, 64), (65, 127), (128, 129), (200, 17)])
+def test_bf16_tile_edges(gpu_lib, step, T):
+    run_case(gpu_lib, 7 + step, 2, 4, 2, 128, 256, step, T, "bf16")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2), (8, 2), (16, 2), (8, 1)])
+def test_bf16_gqa_groups(gpu_lib, Hq, Hkv):
+    run_case(gpu_lib, 20 + Hq, 2, Hq, Hkv, 128, 384, 2, (384, 300), "bf16")
+
+
+def test_bf16_peaky_logits(gpu_lib):
+    """q x 4 makes the softmax peaky, so the running max is overtaken often (online rescaling)."""
+    run_case(gpu_lib, 31, 2, 4, 1, 128, 512, 3, (512, 333), "bf16", q_mult=4.0)
+
+
+def test_bf16_out_of_range_lengths_are_clamped(gpu_lib):
+    run_case(gpu_lib, 41, 2, 2, 1, 128, 128, 1, (5000, -3), "bf16", T_oracle=np.array([128, 0]))
+
+
+def test_fp32_out_of_range_lengths_are_clamped(gpu_lib):
+    run_case(gpu_lib, 42, 2, 2, 1, 64, 40, 1, (99, -1), "f32", T_oracle=np.array([40, 0]))
+
+
+def test_bf16_backward_is_deterministic(gpu_lib):
+    import torch
+    from tests.helpers import to_dev
+    q, k, v, do, T = inputs.make_case(51, 1, 8, 1, 128, 512, 2, 400, "bf16")
+    qd, kd, vd, dod = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+    Td = torch.as_tensor(T, device="cuda")
+    o, lse = gpu_lib.ttt_attn_fwd(qd, kd, vd, Td)
+    r1 = gpu_lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod)
+    r2 = gpu_lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
