@@ -1,0 +1,235 @@
+"""Benchmark of the TTT sparse tree attention hot path on one MI355X.
+
+One step = one TTT sweep of a draft layer: the forward of every TTT step k = 0..K-1 (KV length
+(k+1) * Q_LEN) followed by the backward of every step in reverse order, i.e. all kernels of the
+path (tile classification, causal MFMA forward, suffix gather/merge, backward row dot, causal
+MFMA dK/dV and dQ, suffix backward with dQ finalisation).  Inputs are seeded synthetic tensors
+already resident in HBM; outputs and workspaces are preallocated, so the timed region only
+launches kernels.
+
+value = unmasked TFLOP/s = sum over steps of 14 * d * |M| * B * Hq (4d forward + 10d backward
+per unmasked (query, key) pair) / step time.  tokens/s = B * Q_LEN / step time.
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TTT-attn fwd+bwd unmasked TFLOP/s + tokens/s at Q_LEN=4096, TTT=7; % roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+
+
+def causal_pairs(L: int, T: int) -> int:
+    """|M_causal| for one (batch, head): T(T+1)/2 over rows i < T plus T keys for each of the
+    L - T padded rows."""
+    return T * (T + 1) // 2 + (L - T) * T
+
+
+def total_pairs(L: int, step: int, T: int) -> int:
+    """|M| for one (batch, head) at TTT step `step`: the causal part plus one diagonal key per
+    later block for every row i < T."""
+    return causal_pairs(L, T) + step * T
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload number (2: the 8B draft layer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the TTT attention path needs no collective and this "
+              "build runs no multi-GPU configuration (see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from masked_attention_eagle_amd import inputs
+    from masked_attention_eagle_amd import ttt_attn as A
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lib = A.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = inputs.WORKLOADS[args.config]
+    assert w.dtype == "bf16"
+    T = inputs.seq_lengths(w)
+    steps = list(w.steps)
+    K = len(steps)
+
+    # ---------------------------------------------------------------- resident inputs
+    t_setup = time.time()
+    bf = torch.bfloat16
+    blocks = [inputs.kv_block(w, t) for t in range(K)]
+    kv = []
+    for k in steps:
+        kk = np.concatenate([blocks[t][0] for t in range(k + 1)], axis=2)
+        vv = np.concatenate([blocks[t][1] for t in range(k + 1)], axis=2)
+        kv.append((torch.from_numpy(kk).to(dev, bf), torch.from_numpy(vv).to(dev, bf)))
+        del kk, vv
+    qs = [torch.from_numpy(inputs.q_at(w, k)).to(dev, bf) for k in steps]
+    dos = [torch.from_numpy(inputs.do_at(w, k)).to(dev, bf) for k in steps]
+    Td = torch.as_tensor(T, device=dev)
+    os_ = [torch.empty_like(q) for q in qs]
+    lses = [torch.empty(q.shape[:3], dtype=torch.float32, device=dev) for q in qs]
+    dqs = [torch.empty_like(q) for q in qs]
+    dks = [torch.empty_like(kv[i][0]) for i in range(K)]
+    dvs = [torch.empty_like(kv[i][1]) for i in range(K)]
+    params = [A.make_params(w.B, w.Hq, w.Hkv, w.L, w.d, k, w.scale, A.TTT_DTYPE_BF16) for k in steps]
+    ws_bytes = max(max(A.fwd_workspace_size(p), A.bwd_workspace_size(p)) for p in params)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    fwd_args = [(ctypes.byref(params[i]), qs[i].data_ptr(), kv[i][0].data_ptr(), kv[i][1].data_ptr(),
+                 Td.data_ptr(), os_[i].data_ptr(), lses[i].data_ptr(), ws.data_ptr(), ws_bytes, sp)
+                for i in range(K)]
+    bwd_args = [(ctypes.byref(params[i]), qs[i].data_ptr(), kv[i][0].data_ptr(), kv[i][1].data_ptr(),
+                 Td.data_ptr(), os_[i].data_ptr(), lses[i].data_ptr(), dos[i].data_ptr(),
+                 dqs[i].data_ptr(), dks[i].data_ptr(), dvs[i].data_ptr(), ws.data_ptr(), ws_bytes, sp)
+                for i in range(K)]
+
+    def one_step():
+        for i in range(K):
+            rc = lib.ttt_attn_fwd(*fwd_args[i])
+            if rc:
+                raise A.TTTError(rc, A.status_string(rc))
+        for i in reversed(range(K)):
+            rc = lib.ttt_attn_bwd(*bwd_args[i])
+            if rc:
+                raise A.TTTError(rc, A.status_string(rc))
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed region
+    timing = not args.no_kernel_timing
+    if timing:
+        A.timing_reset()
+        A.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernels = {}
+    if timing:
+        A.timing_enable(False)
+        kernels = A.timing_read()
+    sec = (t1 - t0) / args.steps
+
+    # ---------------------------------------------------------------- accounting
+    pairs_step = [sum(total_pairs(w.L, k, int(t)) for t in T) * w.Hq for k in steps]
+    causal = sum(causal_pairs(w.L, int(t)) for t in T) * w.Hq  # per launch of a causal kernel
+    flops = sum(14 * w.d * p for p in pairs_step)
+    value = flops / sec / 1e12
+    tokens = w.B * w.L / sec
+
+    kstats = {name: {"launches": n, "avg_ms": ms / n, "total_ms_per_step": ms / args.steps}
+              for name, (n, ms) in kernels.items()}
+    # algorithmic matrix-core flops per launch of each causal kernel: dK/dV kernel does the
+    # S, dP, dV and dK products (8d per pair), dQ kernel the dQ product (2d), forward 4d.
+    alg = {"bwd_dkdv_mfma": 8 * w.d * causal, "bwd_dq_mfma": 2 * w.d * causal,
+           "fwd_causal_mfma": 4 * w.d * causal}
+    roofline = None
+    if kstats:
+        mfma = {n: s for n, s in kstats.items() if n in alg}
+        dom = max(mfma, key=lambda n: mfma[n]["total_ms_per_step"])
+        achieved = alg[dom] / (mfma[dom]["avg_ms"] / 1e3) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+        for n in alg:
+            if n in kstats:
+                a = alg[n] / (kstats[n]["avg_ms"] / 1e3) / 1e12
+                kstats[n]["alg_tflops"] = round(a, 1)
+                kstats[n]["frac_mfma_peak"] = round(a / PEAK_BF16_TFLOPS, 4)
+        # suffix kernels: algorithmic HBM bytes per launch averaged over the steps with k >= 1
+        rows_q = w.B * w.Hq * w.L
+        live_q = int(sum(int(t) for t in T)) * w.Hq
+        live_kv = int(sum(int(t) for t in T)) * w.Hkv
+        kk = [k for k in steps if k > 0]
+        if kk and "fwd_suffix" in kstats:
+            b = np.mean([live_q * w.d * 2 + rows_q * (w.d * 4 + 4) + live_kv * k * 2 * w.d * 2 +
+                         rows_q * (w.d * 2 + 4) for k in kk])
+            gbs = b / (kstats["fwd_suffix"]["avg_ms"] / 1e3) / 1e9
+            kstats["fwd_suffix"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+        if kk and "bwd_suffix" in kstats:
+            b = np.mean([2 * live_q * w.d * 2 + 2 * live_q * 4 + rows_q * w.d * 4 + rows_q * w.d * 2 +
+                         live_kv * k * 2 * w.d * 2 + w.B * w.Hkv * k * w.L * 2 * w.d * 2 for k in kk])
+            gbs = b / (kstats["bwd_suffix"]["avg_ms"] / 1e3) / 1e9
+            kstats["bwd_suffix"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "Q_LEN": w.L,
+                   "T": [int(t) for t in T] if w.T_fixed is None else w.T_fixed,
+                   "ttt_steps": f"k=0..{steps[-1]}", "global_batch": w.B, "seq_len": w.L,
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(tokens, 1),
+        "unmasked_flop_per_step": flops,
+        "roofline": roofline,
+        "kernels": kstats,
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, T, steps)
+    print(json.dumps(out))
+
+
+def cpu_baseline(w, T, steps):
+    """The CPU oracle (fp64 NumPy, dense masked) on a bounded sample of the same workload:
+    forward + backward of one KV group (all of its query heads) of sequence 0 at the last TTT
+    step.  Reported in the same unit (unmasked TFLOP/s over the sample's own pairs)."""
+    from masked_attention_eagle_amd import inputs
+    from oracle import ttt_oracle as O
+    k = steps[-1]
+    G = w.Hq // w.Hkv
+    q = inputs.q_at(w, k)[0:1, 0:G]
+    kk, vv = inputs.kv_stack(w, k)
+    kk, vv = kk[0:1, 0:1], vv[0:1, 0:1]
+    do = inputs.do_at(w, k)[0:1, 0:G]
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    o, _ = O.forward(q, kk, vv, T[0:1], w.scale)
+    O.backward(q, kk, vv, T[0:1], w.scale, do, o)
+    sec = time.perf_counter() - t0
+    flops = 14 * w.d * total_pairs(w.L, k, int(T[0])) * G
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(sec, 2),
+            "sample": f"fwd+bwd of KV group 0 ({G} query heads) of sequence 0 at TTT step {k}"}
+
+
+if __name__ == "__main__":
+    main()

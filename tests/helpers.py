@@ -1,9 +1,15 @@
 """Shared helpers of the GPU parity tests: device transfer, the HIP calls, and the tolerance checks.
 
 Tolerances (max-abs for o and lse, normalised max error max|d|/max|ref| for gradients):
-  fp32 workloads : 1e-5 max-abs on every output;
-  bf16 workloads : o 1e-2, lse 1e-3, dq/dk/dv 2e-2 normalised.
+  fp32 tiny workload : 1e-5 max-abs on every output;
+  other fp32 shapes  : 1e-5 * max(1, max|ref|) per output (fp32 sums of up to a few hundred
+                       terms of magnitude ~|ref| carry a relative error of a few 1e-7);
+  bf16 workloads     : o 1e-2, lse 1e-3, dq/dk/dv 2e-2 normalised.
+Set TTT_ERRLOG to a file path to append every measured error as a JSON line.
 """
+import json
+import os
+
 import numpy as np
 
 TOL_F32 = 1e-5
@@ -53,14 +59,23 @@ def errors(got, ref):
     return e
 
 
-def check(got, ref, dtype_name, label=""):
+def check(got, ref, dtype_name, label="", f32_relative=False, o_tol=TOL_O):
     e = errors(got, ref)
+    log = os.environ.get("TTT_ERRLOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps({"case": label, "dtype": dtype_name, **e}) + "\n")
     if dtype_name == "f32":
         for name in ("o", "lse", "dq_abs", "dk_abs", "dv_abs"):
             if name in e:
-                assert e[name] <= TOL_F32, f"{label} {name} max-abs error {e[name]:.3g} > {TOL_F32}"
+                key = name.replace("_abs", "")
+                tol = TOL_F32
+                if f32_relative and key in ref:
+                    fin = ref[key][np.isfinite(ref[key])]
+                    tol = TOL_F32 * max(1.0, float(np.abs(fin).max()) if fin.size else 1.0)
+                assert e[name] <= tol, f"{label} {name} max-abs error {e[name]:.3g} > {tol:.3g}"
     else:
-        assert e["o"] <= TOL_O, f"{label} o max-abs error {e['o']:.4g}"
+        assert e["o"] <= o_tol, f"{label} o max-abs error {e['o']:.4g}"
         assert e["lse"] <= TOL_LSE, f"{label} lse max-abs error {e['lse']:.4g}"
         for name in ("dq", "dk", "dv"):
             if name in e:

@@ -11,7 +11,7 @@ from tests.helpers import check, gpu_fwd_bwd
 pytestmark = pytest.mark.gpu
 
 
-def run_case(lib, seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult=1.0, T_oracle=None):
+def run_case(lib, seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult=1.0, T_oracle=None, o_tol=1e-2):
     q, k, v, do, Tarr = inputs.make_case(seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult)
     scale = 1.0 / np.sqrt(d)
     print(f"case seed={seed} B={B} Hq={Hq} Hkv={Hkv} d={d} L={L} step={step} T={list(Tarr)} {dtype}", flush=True)
@@ -20,7 +20,8 @@ def run_case(lib, seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult=1.0, T_oracle=N
     o, lse = O.forward(q, k, v, To, scale)
     dq, dk, dv = O.backward(q, k, v, To, scale, do, o)
     ref = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
-    return check(got, ref, dtype, f"seed={seed} step={step} T={list(Tarr)}")
+    return check(got, ref, dtype, f"seed={seed} B={B} Hq={Hq} Hkv={Hkv} L={L} step={step} T={list(Tarr)}",
+                 f32_relative=True, o_tol=o_tol)
 
 
 # ------------------------------------------------------------------ fp32 path
@@ -57,8 +58,12 @@ def test_bf16_gqa_groups(gpu_lib, Hq, Hkv):
 
 
 def test_bf16_peaky_logits(gpu_lib):
-    """q x 4 makes the softmax peaky, so the running max is overtaken often (online rescaling)."""
-    run_case(gpu_lib, 31, 2, 4, 1, 128, 512, 3, (512, 333), "bf16", q_mult=4.0)
+    """q x 4 makes the softmax peaky, so the running max is overtaken often (online rescaling).
+
+    Outside the N(0,1) workloads, so the o bound is derived here: with nearly one-hot rows the
+    bf16 rounding of P (relative 2^-9) moves o by up to 2^-9 * max|v| ~ 0.009 (|v| <= 4.6 at
+    these sizes) on top of the bf16 output half-ulp 0.0078 for |o| in [2, 4): 2e-2."""
+    run_case(gpu_lib, 31, 2, 4, 1, 128, 512, 3, (512, 333), "bf16", q_mult=4.0, o_tol=2e-2)
 
 
 def test_bf16_out_of_range_lengths_are_clamped(gpu_lib):
