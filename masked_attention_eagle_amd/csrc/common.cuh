@@ -127,6 +127,17 @@ __device__ __forceinline__ void store_vec(T* p, const float* in) {
   }
 }
 
+// Asynchronous global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane l of the wave writes lds_base + 16 * l; lds_base must be the same for the whole wave.
+__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (incl. global -> LDS copies)
+// have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
 // Splits a grid of units * ranks workgroups into (unit, rank).  A unit is an
 // independent slice of work (a head, a KV group); rank 0 is its heaviest piece.  The
 // dispatcher deals workgroups to the 8 XCDs round robin, so when units % 8 == 0 each

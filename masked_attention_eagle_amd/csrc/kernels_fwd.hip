@@ -13,7 +13,7 @@ namespace ttt {
 // Causal block-0 forward, bf16 MFMA, head_dim 128.
 //
 // Workgroup = 4 waves = 128 queries (32 per wave); the loop streams 64-key tiles of block 0
-// through LDS (double buffered, next tile prefetched into registers).  Per wave and tile:
+// through LDS.  Per wave and tile:
 //   S^T[64 keys x 32 queries] = K Q^T     (A = K rows from LDS, B = Q kept in registers)
 //   online softmax on S^T (each lane owns one query; its keys sit in this lane and lane^32)
 //   O^T[128 x 32] += V^T P^T              (A = V^T from LDS, B = P^T straight from S^T)
@@ -21,20 +21,28 @@ namespace ttt {
 // straddle the diagonal or the T edge evaluate the mask ("partial"); the rest are "full".
 // On partial tiles P is split into bf16 hi + lo parts so that rows with few keys (where one
 // rounding of P would show in O) keep fp32-level accuracy.
+//
+// K and V^T tiles are copied global -> LDS without passing through registers (two stages),
+// which keeps the wave under 256 registers: two workgroups share a CU and the matrix cores
+// of one overlap the softmax of the other.  LDS rows are XOR-swizzled in 16-byte chunks so
+// that the 32 rows a wave reads at one column fall in distinct banks.
 // ----------------------------------------------------------------------------------------
-constexpr int FD = 128;       // head dim
-constexpr int FBM = 128;      // queries per workgroup
-constexpr int FBN = 64;       // keys per tile
-constexpr int KSTR = FD + 8;  // K tile row stride (elements): 272 B rows spread the banks
-constexpr int VSTR = FBN + 8; // V^T tile row stride: 144 B
+constexpr int FD = 128;  // head dim
+constexpr int FBM = 128; // queries per workgroup
+constexpr int FBN = 64;  // keys per tile
+
+// K tile: 64 rows x 256 B; 16-byte chunk c of row r stored at chunk c ^ (r & 15).
+__device__ __forceinline__ int kswz(int r, int c) { return r * 128 + ((c ^ (r & 15)) << 3); }
+// V^T tile: 128 rows x 128 B; chunk c of row r stored at chunk c ^ ((r & 7) ^ ((r >> 3) & 1)).
+__device__ __forceinline__ int vswz(int r, int c) { return r * 64 + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 3); }
 
 template <bool FINAL>
-__global__ __launch_bounds__(256) void fwd_causal_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ vt,
     const int32_t* __restrict__ seq_T, void* __restrict__ o_out, float* __restrict__ lse_out,
     Shape s) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][FBN * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][FD * VSTR];
+  __shared__ __attribute__((aligned(1024))) bf16 sK[2][FBN * FD];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[2][FD * FBN];
 
   const int n_qt = s.L / FBM;
   int bh, rank;
@@ -62,101 +70,123 @@ __global__ __launch_bounds__(256) void fwd_causal_mfma_kernel(
   f32x16 acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
-  float m = kNegInf, l = 0.f;
+  float m = kNegInf, l = 0.f;  // running max of the raw logits q.k, and the softmax sum
+  const float c2 = s.scale_log2;
 
-  bf16x8 rk[4], rv[4];
-  auto gload = [&](int j) {
+  // Each wave copies 4 KB of K and 4 KB of V^T per tile: 4 instructions x 64 lanes x 16 B.
+  auto issue = [&](int j, int buf) {
     const int k0 = j * FBN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      rk[i] = *reinterpret_cast<const bf16x8*>(kb + (size_t)(k0 + (c >> 4)) * FD + (c & 15) * 8);
-      rv[i] = *reinterpret_cast<const bf16x8*>(vb + (size_t)(c >> 3) * s.L + k0 + (c & 7) * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<bf16x8*>(&sK[buf][(c >> 4) * KSTR + (c & 15) * 8]) = rk[i];
-      *reinterpret_cast<bf16x8*>(&sV[buf][(c >> 3) * VSTR + (c & 7) * 8]) = rv[i];
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = wave * 4 + ii;
+      {
+        const int r = 4 * i + (lane >> 4), cp = lane & 15;
+        g2lds16(kb + (size_t)(k0 + r) * FD + ((cp ^ (r & 15)) << 3), &sK[buf][i * 512]);
+      }
+      {
+        const int r = 8 * i + (lane >> 3), cp = lane & 7;
+        g2lds16(vb + (size_t)r * s.L + k0 + ((cp ^ ((r & 7) ^ ((r >> 3) & 1))) << 3), &sV[buf][i * 512]);
+      }
     }
   };
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (ntiles > 0) issue(0, 0);
+  wait_vmem();
   __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
+    if (j + 1 < ntiles) issue(j + 1, buf ^ 1);
     const int k0 = j * FBN;
     if (k0 <= qw + 31) {  // some query of this wave can see a key of the tile
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(&sK[buf][(st * 32 + l32) * KSTR + 16 * t + 8 * hi]);
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[buf][kswz(st * 32 + l32, 2 * t + hi)]);
           sacc[st] = mfma32(a, qf[t], sacc[st]);
         }
       }
       const bool full = (k0 + FBN - 1 <= qw) && (k0 + FBN <= T);
+      if (!full) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + st * 32 + acc_row(i, hi);
+            if (key > my_q || key >= T) sacc[st][i] = kNegInf;
+          }
+        }
+      }
       float rmax = kNegInf;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = sacc[st][i] * s.scale_log2;
-          if (!full) {
-            const int key = k0 + st * 32 + acc_row(i, hi);
-            if (key > my_q || key >= T) x = kNegInf;
-          }
-          sacc[st][i] = x;
-          rmax = fmaxf(rmax, x);
-        }
+        for (int i = 0; i < 16; i += 2) rmax = fmaxf(rmax, fmaxf(sacc[st][i], sacc[st][i + 1]));
       }
       rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
       const float m_new = fmaxf(m, rmax);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2_fast(m - m_use);
+      const float mc = (m_new == kNegInf) ? 0.f : m_new * c2;
+      // Rescale the accumulator only when some row's running max moved (wave-uniform test).
+      if (__any(m_new > m)) {
+        const float alpha = exp2_fast(m * c2 - mc);
+        l *= alpha;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] *= alpha;
+      }
+      m = m_new;
       float lsum = 0.f;
-      bf16x8 pf[4], pl[4];
+      bf16x8 pf[4];
+      if (full) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 4; ++c) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const float pv = exp2_fast(sacc[c >> 1][8 * (c & 1) + jj] - m_use);
-          lsum += pv;
-          const bf16 ph = (bf16)pv;
-          pf[c][jj] = ph;
-          pl[c][jj] = (bf16)(pv - (float)ph);
+          for (int jj = 0; jj < 8; ++jj) {
+            const float pv = exp2_fast(__builtin_fmaf(sacc[c >> 1][8 * (c & 1) + jj], c2, -mc));
+            lsum += pv;
+            pf[c][jj] = (bf16)pv;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sV[buf][vswz(u * 32 + l32, 2 * c + hi)]);
+            acc[u] = mfma32(a, pf[c], acc[u]);
+          }
+        }
+      } else {  // P = hi + lo in bf16: both parts go through the same V^T operands
+        bf16x8 pl[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const float pv = exp2_fast(__builtin_fmaf(sacc[c >> 1][8 * (c & 1) + jj], c2, -mc));
+            lsum += pv;
+            const bf16 ph = (bf16)pv;
+            pf[c][jj] = ph;
+            pl[c][jj] = (bf16)(pv - (float)ph);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sV[buf][vswz(u * 32 + l32, 2 * c + hi)]);
+            acc[u] = mfma32(a, pf[c], acc[u]);
+            acc[u] = mfma32(a, pl[c], acc[u]);
+          }
         }
       }
       lsum += __shfl_xor(lsum, 32);
-      l = l * alpha + lsum;
-      m = m_new;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] *= alpha;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(&sV[buf][(u * 32 + l32) * VSTR + 16 * c + 8 * hi]);
-          acc[u] = mfma32(a, pf[c], acc[u]);
-          if (!full) acc[u] = mfma32(a, pl[c], acc[u]);
-        }
-      }
+      l += lsum;
     }
-    if (j + 1 < ntiles) lstore(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
-  const float lse = l > 0.f ? (m + __log2f(l)) * kLn2 : kNegInf;
+  const float lse = l > 0.f ? (m * c2 + __log2f(l)) * kLn2 : kNegInf;
   const size_t row = (size_t)bh * s.L + my_q;
   if (hi == 0) lse_out[row] = lse;
   // lane owns O[my_q][32u + 8*b4 + 4*hi + e] in acc[u][4*b4 + e]
