@@ -134,9 +134,103 @@ __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
                                    (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// Same, 4 bytes per lane (global_load_lds_dword): lane l writes lds_base + 4 * l.
+__device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
 // Wait until this wave's outstanding vector-memory operations (incl. global -> LDS copies)
 // have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---------------------------------------------------------------------------------------
+// LDS tiles of 128 bf16 per row (256 bytes).  The 16-byte chunk c of row r is stored at
+// chunk c ^ swz(r).  Two read patterns hit these tiles:
+//   row reads   : 16 lanes take 16 consecutive rows at one chunk       -> swz bijective on
+//                 any aligned block of 16 rows;
+//   column reads: 16 lanes take 4 consecutive rows x 2 adjacent chunks -> the 4 rows must
+//                 differ in bits 2-3 of swz.
+// swz(r) = 4*(r mod 4) + (r/4 mod 4) satisfies both, so neither pattern has bank conflicts.
+__device__ __forceinline__ constexpr int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ constexpr int tile_off(int r, int col) {
+  return r * 128 + ((((col >> 3) ^ swz(r))) << 3) + (col & 7);
+}
+
+// Copies rows [0, NROWS) of a [rows][128] bf16 matrix (row stride `ld` elements) into a
+// swizzled LDS tile, global -> LDS directly; each wave instruction moves 4 rows (1 KB).
+// `g` and `wave` are wave-uniform.  Wave w copies the 4-row groups i = w, w + NWAVES, ...;
+// with NWAVES a multiple of 4, row r = 4i + lane/16 has swz(r) = 4*(lane/16) + w % 4 for
+// every i, so one 32-bit lane offset serves all of the wave's copies.
+template <int NROWS, int NWAVES>
+__device__ __forceinline__ void load_tile(const bf16* g, int ld, bf16* lds, int wave, int lane) {
+  static_assert(NWAVES % 4 == 0, "swizzle term must be constant per wave");
+  const int rl = lane >> 4;
+  const unsigned lane_off = (unsigned)(rl * ld + (((lane & 15) ^ ((rl << 2) | (wave & 3))) << 3));
+#pragma unroll
+  for (int i = wave; i < NROWS / 4; i += NWAVES) g2lds16(g + (size_t)(4 * i) * ld + lane_off, lds + i * 512);
+}
+
+// Index of the calling wave inside its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Per-lane byte offsets of the matrix-core operand reads from a swizzled tile.  They depend
+// on the lane only; tile base, 32-row block and 16-row chunk add compile-time constants, so
+// every read is one VGPR offset plus an immediate.  The offsets are made opaque to the
+// compiler so that it keeps exactly these 16 registers instead of rebuilding an address per
+// (tile, fragment).
+struct FragOffsets {
+  int row[8];     // frag_row of row l32 (+ any multiple of 16), chunk 2t + hi: t = 0..7
+  int col[4][2];  // frag_col of column block 32u, rows 4h.. (k = 0) and 4h + 8.. (k = 1)
+};
+
+__device__ __forceinline__ FragOffsets make_frag_offsets(int lane) {
+  FragOffsets f;
+  const int l32 = lane & 31, hi = lane >> 5, sl = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    f.row[t] = 2 * (l32 * 128 + ((((2 * t + hi) ^ swz(l32))) << 3));
+    asm volatile("" : "+v"(f.row[t]));
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = 4 * hi + 8 * k + (sl >> 2);
+      const int col = 32 * u + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+      f.col[u][k] = 2 * tile_off(r, col);
+      asm volatile("" : "+v"(f.col[u][k]));
+    }
+  }
+  return f;
+}
+
+// Matrix-core operand with the contraction along the row (d) axis: rows rb + l32 (rb a
+// multiple of 32), elements 16t + 8*hi .. +7.
+__device__ __forceinline__ bf16x8 frag_row(const bf16* tile, int rb, int t, const FragOffsets& f) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile + rb * 128) + f.row[t]);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// receives element i % 4 of the 4-element pieces addressed by lanes i/4, 4 + i/4, 8 + i/4
+// and 12 + i/4.  With lane s addressing row r0 + s/4, column c0 + 4*(s % 4), lane i gets
+// rows r0..r0+3 of column c0 + i.
+__device__ __forceinline__ bf16x4 lds_tr4(const void* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Matrix-core operand with the contraction along the token (row) axis, taken from a
+// row-major tile: the lane holds column 32u + (lane % 32) and rows 16c + 4h .. +3 then
+// 16c + 8 + 4h .. +3 (h = lane / 32), the token order in which a 32x32 accumulator hands over
+// its values.  Rows 16c.. share the swizzle of rows 0.., so c only moves the base.
+__device__ __forceinline__ bf16x8 frag_col(const bf16* tile, int c, int u, const FragOffsets& f) {
+  const char* base = reinterpret_cast<const char*>(tile + 16 * c * 128);
+  const bf16x4 a = lds_tr4(base + f.col[u][0]);
+  const bf16x4 b = lds_tr4(base + f.col[u][1]);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 
 // Splits a grid of units * ranks workgroups into (unit, rank).  A unit is an
 // independent slice of work (a head, a KV group); rank 0 is its heaviest piece.  The

@@ -106,26 +106,23 @@ Shape make_shape(const ttt_attn_params* p) {
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Number of workgroups that share the query heads of one KV group in the dK/dV kernel:
-// doubled while the grid is below two workgroups per CU and the group still splits evenly.
+// Number of workgroups that share the query heads of one KV group in the dK/dV kernel
+// (each workgroup owns a pair of 128-key tiles): doubled while the grid is below two
+// workgroups per CU and the group still splits evenly.
 int dkdv_nsplit(const Shape& s) {
-  const int64_t base = (int64_t)s.B * s.Hkv * (s.L / 128);
+  const int64_t base = (int64_t)s.B * s.Hkv * ((s.L / 128 + 1) / 2);
   int n = 1;
   while (base * n < 512 && n < s.G && s.G % (2 * n) == 0) n *= 2;
   return n;
 }
 
 struct FwdLayout {
-  size_t vt = 0, oc = 0, lsec = 0, total = 0;
+  size_t oc = 0, lsec = 0, total = 0;
 };
-FwdLayout fwd_layout(const Shape& s, int dtype) {
+FwdLayout fwd_layout(const Shape& s, int /*dtype*/) {
   FwdLayout w;
   size_t off = 0;
   const size_t rows_q = (size_t)s.B * s.Hq * s.L;
-  if (dtype == TTT_DTYPE_BF16) {
-    w.vt = off;
-    off += round_up((size_t)s.B * s.Hkv * s.D * s.L * 2);
-  }
   if (s.step > 0) {
     w.oc = off;
     off += round_up(rows_q * s.D * 4);
@@ -137,7 +134,7 @@ FwdLayout fwd_layout(const Shape& s, int dtype) {
 }
 
 struct BwdLayout {
-  size_t Dd = 0, dqacc = 0, qt = 0, dot = 0, kt = 0, part = 0, total = 0;
+  size_t Dd = 0, dqacc = 0, part = 0, total = 0;
   int nsplit = 1;
 };
 BwdLayout bwd_layout(const Shape& s, int dtype) {
@@ -151,12 +148,6 @@ BwdLayout bwd_layout(const Shape& s, int dtype) {
     off += round_up(rows_q * s.D * 4);
   }
   if (dtype == TTT_DTYPE_BF16) {
-    w.qt = off;
-    off += round_up(rows_q * s.D * 2);
-    w.dot = off;
-    off += round_up(rows_q * s.D * 2);
-    w.kt = off;
-    off += round_up((size_t)s.B * s.Hkv * s.L * s.D * 2);
     w.nsplit = dkdv_nsplit(s);
     if (w.nsplit > 1) {
       w.part = off;
@@ -224,10 +215,7 @@ int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const v
     const bf16* qb = (const bf16*)q;
     const bf16* kb = (const bf16*)k;
     const bf16* vb = (const bf16*)v;
-    bf16* vt = (bf16*)(ws + w.vt);
-    e = launch_transpose_swz(vb, vt, s.L, (size_t)s.KV * s.D, s.B * s.Hkv, st);
-    if (e != hipSuccess) return TTT_E_HIP;
-    e = launch_fwd_causal_mfma(s, qb, kb, vt, seq_T, final_causal ? o : (void*)oc, lsec,
+    e = launch_fwd_causal_mfma(s, qb, kb, vb, seq_T, final_causal ? o : (void*)oc, lsec,
                                final_causal, st);
     if (e != hipSuccess) return TTT_E_HIP;
     if (!final_causal)
@@ -271,21 +259,15 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
     const bf16* kb = (const bf16*)k;
     const bf16* vb = (const bf16*)v;
     const bf16* dob = (const bf16*)dout;
-    bf16* qt = (bf16*)(ws + w.qt);
-    bf16* dot = (bf16*)(ws + w.dot);
-    bf16* kt = (bf16*)(ws + w.kt);
     float* part = w.nsplit > 1 ? (float*)(ws + w.part) : nullptr;
     if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, st)) != hipSuccess) return TTT_E_HIP;
-    if ((e = launch_transpose_swz(qb, qt, s.L, (size_t)s.L * s.D, s.B * s.Hq, st)) != hipSuccess) return TTT_E_HIP;
-    if ((e = launch_transpose_swz(dob, dot, s.L, (size_t)s.L * s.D, s.B * s.Hq, st)) != hipSuccess) return TTT_E_HIP;
-    if ((e = launch_transpose_swz(kb, kt, s.L, (size_t)s.KV * s.D, s.B * s.Hkv, st)) != hipSuccess) return TTT_E_HIP;
-    if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, qt, dot, dob, lse, Dd, seq_T, (bf16*)dk, (bf16*)dv,
-                                  part, w.nsplit, st)) != hipSuccess)
+    if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
+                                  w.nsplit, st)) != hipSuccess)
       return TTT_E_HIP;
     if (w.nsplit > 1 &&
         (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
       return TTT_E_HIP;
-    if ((e = launch_bwd_dq_mfma(s, qb, kb, vb, kt, dob, lse, Dd, seq_T,
+    if ((e = launch_bwd_dq_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T,
                                 final_causal ? dq : (void*)dqacc, final_causal, st)) != hipSuccess)
       return TTT_E_HIP;
     if (!final_causal)

@@ -1,47 +1,7 @@
-// Small bandwidth-bound helpers: operand layout transforms and the backward row dot.
+// Backward row term D_i = rowsum(dO_i * O_i) (bandwidth-bound).
 #include "launch.h"
 
 namespace ttt {
-
-// ----------------------------------------------------------------------------------------
-// [rows][128] -> [128][rows] for the operands that the matrix cores consume along the token
-// axis (V^T in the forward, Q^T, dO^T and K^T in the backward).  Positions inside each group
-// of 16 tokens are stored with bits 2 and 3 swapped (swap23), the order in which a 32x32
-// accumulator hands its probabilities to the next product, so that every lane reads its 8
-// operands with one 16-byte LDS load.
-// ----------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transpose_swz_kernel(const bf16* __restrict__ src,
-                                                            bf16* __restrict__ dst, int rows,
-                                                            size_t src_slab_stride) {
-  __shared__ __attribute__((aligned(16))) bf16 tile[64][128 + 8];
-  const int tid = threadIdx.x;
-  const int r0 = blockIdx.x * 64;
-  const bf16* sp = src + (size_t)blockIdx.y * src_slab_stride + (size_t)r0 * 128;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, row = c >> 4, col = (c & 15) * 8;
-    *reinterpret_cast<bf16x8*>(&tile[row][col]) =
-        *reinterpret_cast<const bf16x8*>(sp + (size_t)row * 128 + col);
-  }
-  __syncthreads();
-  bf16* dp = dst + (size_t)blockIdx.y * 128 * rows + r0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, d = c >> 3, p0 = (c & 7) * 8;
-    bf16x8 w;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) w[jj] = tile[(p0 & ~15) + swap23((p0 & 15) + jj)][d];
-    *reinterpret_cast<bf16x8*>(dp + (size_t)d * rows + p0) = w;
-  }
-}
-
-hipError_t launch_transpose_swz(const bf16* src, bf16* dst, int rows, size_t src_slab_stride,
-                                int nslabs, hipStream_t st) {
-  const dim3 grid(rows / 64, nslabs);
-  LaunchTimer timer("transpose_swz", st);
-  transpose_swz_kernel<<<grid, 256, 0, st>>>(src, dst, rows, src_slab_stride);
-  return hipGetLastError();
-}
 
 // ----------------------------------------------------------------------------------------
 // D_i = sum_d dO_i * O_i, the row term of the softmax Jacobian (dS = P * (dP - D)).

@@ -14,197 +14,184 @@
 
 namespace ttt {
 
-constexpr int BD = 128;         // head dim of the matrix-core path
-constexpr int QSTR = BD + 8;    // row-major [token][d] tile stride (272 B rows)
-constexpr int TSTR = 64 + 8;    // transposed [d][64 tokens] tile stride (144 B rows)
+constexpr int BD = 128;  // head dim of the matrix-core path
 
 // ----------------------------------------------------------------------------------------
-// dK, dV of block 0, bf16 MFMA.  Workgroup = 4 waves x 32 keys = 128 keys; per 64-query tile
-// each wave computes
-//   S  = Q K^T,  dP = dO V^T          (M = queries, N = the wave's 32 keys; K, V in registers)
+// dK, dV of block 0, bf16 MFMA.  Workgroup = 4 waves x 32 keys = 128 keys; K of its keys is
+// held in registers and V in LDS; query tiles of 32 rows (of every query head of the group
+// that sees the keys) stream through LDS.  Per wave and tile:
+//   S  = Q K^T,  dP = dO V^T          (M = queries, N = the wave's 32 keys; A = Q / dO rows)
 //   P  = exp2(S * scale*log2e - lse*log2e), dS = P * (dP - D)
 //   dV += P^T dO,  dK += dS^T Q       (A operands straight from the S/dP accumulators,
-//                                      B = dO^T / Q^T tiles from LDS)
+//                                      B = dO / Q columns through transposing LDS reads)
 // With nsplit > 1 the query heads of a group are split over nsplit workgroups that write
 // fp32 partial sums, reduced afterwards in split order.
 // ----------------------------------------------------------------------------------------
-constexpr int KBN = 128;  // keys per workgroup
-constexpr int KBM = 64;   // queries per tile
+constexpr int KBN = 128;  // keys per tile
+constexpr int KBM = 32;   // queries per tile
 
-struct DkdvStage {
-  bf16 q[KBM * QSTR];
-  bf16 dO[KBM * QSTR];
-  bf16 qt[BD * TSTR];
-  bf16 dOt[BD * TSTR];
-  float lse2[KBM];
-  float Dv[KBM];
-};
-
-__global__ __launch_bounds__(256) void bwd_dkdv_mfma_kernel(
+// Key tile kt is seen by every query row >= 128 * kt (padded rows see every key < T), so the
+// work of tile kt falls linearly with kt.  A workgroup takes the complementary pair
+// (p, n - 1 - p) of key tiles, which makes every workgroup's work equal.
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ qt, const bf16* __restrict__ dot, const bf16* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ Dd, const int32_t* __restrict__ seq_T,
-    bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ part, int nsplit, Shape s) {
-  __shared__ __attribute__((aligned(16))) DkdvStage sm[2];
+    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
+    const int32_t* __restrict__ seq_T, bf16* __restrict__ dk, bf16* __restrict__ dv,
+    float* __restrict__ part, int nsplit, Shape s) {
+  // Two stages in distinct arrays (the copy into one never stalls reads of the other).
+  __shared__ __attribute__((aligned(1024))) bf16 sQ0[KBM * BD];
+  __shared__ __attribute__((aligned(1024))) bf16 sO0[KBM * BD];
+  __shared__ __attribute__((aligned(256))) float sLD0[2 * KBM];  // lse (natural log), then D
+  __shared__ __attribute__((aligned(1024))) bf16 sQ1[KBM * BD];
+  __shared__ __attribute__((aligned(1024))) bf16 sO1[KBM * BD];
+  __shared__ __attribute__((aligned(256))) float sLD1[2 * KBM];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[KBN * BD];
 
-  int unit, kt;
-  map_block(blockIdx.x, s.B * s.Hkv * nsplit, unit, kt);  // key tile 0 is the heaviest
+  const int nkt = s.L / KBN;
+  int unit, pair;
+  map_block(blockIdx.x, s.B * s.Hkv * nsplit, unit, pair);
   const int split = unit % nsplit, bg = unit / nsplit;
   const int b = bg / s.Hkv;
   const int T = clamp_T(seq_T, b, s.L);
-  const int k0 = kt * KBN;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int kw = k0 + wave * 32;
-  const int my_key = kw + l32;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int hpg = s.G / nsplit;
   const int h_begin = (bg % s.Hkv) * s.G + split * hpg;
+  const float c2 = s.scale_log2;
+  const FragOffsets fo = make_frag_offsets(lane);
 
-  bf16x8 kf[8], vf[8];
-  {
-    const bf16* kr = k + ((size_t)bg * s.KV + my_key) * BD + 8 * hi;
-    const bf16* vr = v + ((size_t)bg * s.KV + my_key) * BD + 8 * hi;
+#pragma nounroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int kt = pass == 0 ? pair : nkt - 1 - pair;
+    if (pass == 1 && kt == pair) break;  // odd tile count: the middle tile has no partner
+    const int k0 = kt * KBN;
+    const int kw = k0 + wave * 32;
+    const int my_key = kw + l32;
+
+    bf16x8 kf[8];
+    {
+      const bf16* kr = k + ((size_t)bg * s.KV + my_key) * BD + 8 * hi;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      kf[t] = *reinterpret_cast<const bf16x8*>(kr + 16 * t);
-      vf[t] = *reinterpret_cast<const bf16x8*>(vr + 16 * t);
+      for (int t = 0; t < 8; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(kr + 16 * t);
     }
-  }
-  f32x16 dKacc[4], dVacc[4];
+    load_tile<KBN, 4>(v + ((size_t)bg * s.KV + k0) * BD, BD, sV, wave, lane);
+    f32x16 dKacc[4], dVacc[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) dKacc[u] = dVacc[u] = f32x16{};
+    for (int u = 0; u < 4; ++u) dKacc[u] = dVacc[u] = f32x16{};
 
-  // Queries that see keys [k0, k0 + 128): rows >= k0 (rows >= T see every key < T).
-  const int q_first = (k0 < T) ? (k0 / KBM) * KBM : s.L;
-  const int nq = (s.L - q_first) / KBM;
-  const int total = nq * hpg;
+    // Queries that see keys [k0, k0 + 128): rows >= k0 (rows >= T see every key < T).
+    const int q_first = (k0 < T) ? k0 : s.L;
+    const int nq = (s.L - q_first) / KBM;
+    const int total = nq * hpg;
 
-  bf16x8 rq[4], rdo[4], rqt[4], rdot[4];
-  float rl = 0.f;
-  auto gload = [&](int it) {
-    const int h = h_begin + it / nq;
-    const int q0 = q_first + (it % nq) * KBM;
-    const size_t bh = (size_t)b * s.Hq + h;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const size_t ro = (bh * s.L + q0 + (c >> 4)) * BD + (c & 15) * 8;
-      rq[i] = *reinterpret_cast<const bf16x8*>(q + ro);
-      rdo[i] = *reinterpret_cast<const bf16x8*>(dO + ro);
-      const size_t to = (bh * BD + (c >> 3)) * s.L + q0 + (c & 7) * 8;
-      rqt[i] = *reinterpret_cast<const bf16x8*>(qt + to);
-      rdot[i] = *reinterpret_cast<const bf16x8*>(dot + to);
-    }
-    if (tid < 64) rl = lse[bh * s.L + q0 + tid] * kLog2e;
-    else if (tid < 128) rl = Dd[bh * s.L + q0 + tid - 64];
-  };
-  auto lstore = [&](int buf) {
-    DkdvStage& S = sm[buf];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<bf16x8*>(&S.q[(c >> 4) * QSTR + (c & 15) * 8]) = rq[i];
-      *reinterpret_cast<bf16x8*>(&S.dO[(c >> 4) * QSTR + (c & 15) * 8]) = rdo[i];
-      *reinterpret_cast<bf16x8*>(&S.qt[(c >> 3) * TSTR + (c & 7) * 8]) = rqt[i];
-      *reinterpret_cast<bf16x8*>(&S.dOt[(c >> 3) * TSTR + (c & 7) * 8]) = rdot[i];
-    }
-    if (tid < 64) S.lse2[tid] = rl;
-    else if (tid < 128) S.Dv[tid - 64] = rl;
-  };
+    auto issue = [&](int it, bf16* dQ, bf16* dOt, float* dLD) {
+      const int h = h_begin + it / nq;
+      const int q0 = q_first + (it % nq) * KBM;
+      const size_t row0 = ((size_t)b * s.Hq + h) * s.L + q0;
+      load_tile<KBM, 4>(q + row0 * BD, BD, dQ, wave, lane);
+      load_tile<KBM, 4>(dO + row0 * BD, BD, dOt, wave, lane);
+      if (wave == 0) g2lds4(lane < KBM ? lse + row0 + lane : Dd + row0 + (lane - KBM), dLD);
+    };
 
-  if (total > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < total; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < total) gload(it + 1);
-    const int q0 = q_first + (it % nq) * KBM;
-    const DkdvStage& S = sm[buf];
-    if (kw < T && q0 + KBM - 1 >= kw) {
-      f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+    auto body = [&](int it, const bf16* cQ, const bf16* cO, const float* cLD, bf16* nQ, bf16* nO,
+                    float* nLD) {
+      if (it + 1 < total) issue(it + 1, nQ, nO, nLD);
+      const int q0 = q_first + (it % nq) * KBM;
+      if (kw < T && q0 + KBM - 1 >= kw) {
+        // S, then P (kept in bf16 only), then dP: one accumulator tile live at a time.
+        f32x16 acc = f32x16{};
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int off = (qs * 32 + l32) * QSTR + 16 * t + 8 * hi;
-          sacc[qs] = mfma32(*reinterpret_cast<const bf16x8*>(&S.q[off]), kf[t], sacc[qs]);
-          pacc[qs] = mfma32(*reinterpret_cast<const bf16x8*>(&S.dO[off]), vf[t], pacc[qs]);
-        }
-      }
-      const bool full = (kw + 31 <= q0) && (kw + 32 <= T);
-      bf16x8 pb[4], dsb[4];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
+        for (int t = 0; t < 8; ++t) acc = mfma32(frag_row(cQ, 0, t, fo), kf[t], acc);
+        const bool full = (kw + 31 <= q0) && (kw + 32 <= T);
+        bf16x8 pb[2], dsb[2];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int r0 = qs * 32 + 8 * i4 + 4 * hi;
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&S.lse2[r0]);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(&S.Dv[r0]);
+          const int r0 = 8 * i4 + 4 * hi;
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&cLD[r0]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
-            float pv = exp2_fast(sacc[qs][i] * s.scale_log2 - L4[e]);
+            float pv = exp2_fast(__builtin_fmaf(acc[i], c2, -L4[e] * kLog2e));
             if (!full) {
               const int qq = q0 + r0 + e;
               if (my_key > qq || my_key >= T) pv = 0.f;
             }
-            const float ds = pv * (pacc[qs][i] - D4[e]);
-            const int c = 2 * qs + (i >> 3), jj = i & 7;
-            pb[c][jj] = (bf16)pv;
-            dsb[c][jj] = (bf16)ds;
+            pb[i >> 3][i & 7] = (bf16)pv;
           }
         }
+        acc = f32x16{};
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          acc = mfma32(frag_row(cO, 0, t, fo), frag_row(sV, wave * 32, t, fo), acc);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 D4 = *reinterpret_cast<const f32x4*>(&cLD[KBM + 8 * i4 + 4 * hi]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            dsb[i >> 3][i & 7] = (bf16)((float)pb[i >> 3][i & 7] * (acc[i] - D4[e]));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            dVacc[u] = mfma32(pb[c], frag_col(cO, c, u, fo), dVacc[u]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            dKacc[u] = mfma32(dsb[c], frag_col(cQ, c, u, fo), dKacc[u]);
+        }
       }
+      wait_vmem();
+      __syncthreads();
+    };
+
+    if (total > 0) issue(0, sQ0, sO0, sLD0);
+    wait_vmem();
+    __syncthreads();
+    for (int it = 0; it < total; it += 2) {
+      body(it, sQ0, sO0, sLD0, sQ1, sO1, sLD1);
+      if (it + 1 < total) body(it + 1, sQ1, sO1, sLD1, sQ0, sO0, sLD0);
+    }
+
+    // lane owns d = 32u + l32 of key rows kw + acc_row(i, hi)
+    if (nsplit == 1) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int off = (u * 32 + l32) * TSTR + 16 * c + 8 * hi;
-          dVacc[u] = mfma32(pb[c], *reinterpret_cast<const bf16x8*>(&S.dOt[off]), dVacc[u]);
-          dKacc[u] = mfma32(dsb[c], *reinterpret_cast<const bf16x8*>(&S.qt[off]), dKacc[u]);
+        for (int i = 0; i < 16; ++i) {
+          const size_t o = ((size_t)bg * s.KV + kw + acc_row(i, hi)) * BD + 32 * u + l32;
+          dk[o] = (bf16)(dKacc[u][i] * s.scale);
+          dv[o] = (bf16)dVacc[u][i];
         }
       }
-    }
-    if (it + 1 < total) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // lane owns d = 32u + l32 of key rows kw + acc_row(i, hi)
-  if (nsplit == 1) {
+    } else {
+      const size_t plane = (size_t)s.B * s.Hkv * s.L * BD;
+      float* pk = part + (size_t)split * 2 * plane;
+      float* pv = pk + plane;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 4; ++u) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const size_t o = ((size_t)bg * s.KV + kw + acc_row(i, hi)) * BD + 32 * u + l32;
-        dk[o] = (bf16)(dKacc[u][i] * s.scale);
-        dv[o] = (bf16)dVacc[u][i];
-      }
-    }
-  } else {
-    const size_t plane = (size_t)s.B * s.Hkv * s.L * BD;
-    float* pk = part + (size_t)split * 2 * plane;
-    float* pv = pk + plane;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const size_t o = ((size_t)bg * s.L + kw + acc_row(i, hi)) * BD + 32 * u + l32;
-        pk[o] = dKacc[u][i] * s.scale;
-        pv[o] = dVacc[u][i];
+        for (int i = 0; i < 16; ++i) {
+          const size_t o = ((size_t)bg * s.L + kw + acc_row(i, hi)) * BD + 32 * u + l32;
+          pk[o] = dKacc[u][i] * s.scale;
+          pv[o] = dVacc[u][i];
+        }
       }
     }
   }
 }
 
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
-                                const bf16* qt, const bf16* dot, const bf16* dout,
-                                const float* lse, const float* Dd, const int32_t* seq_T,
-                                bf16* dk, bf16* dv, float* part, int nsplit, hipStream_t st) {
-  const dim3 grid(s.B * s.Hkv * nsplit * (s.L / KBN));
+                                const bf16* dout, const float* lse, const float* Dd,
+                                const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
+                                int nsplit, hipStream_t st) {
+  const dim3 grid(s.B * s.Hkv * nsplit * ((s.L / KBN + 1) / 2));
   LaunchTimer timer("bwd_dkdv_mfma", st);
-  bwd_dkdv_mfma_kernel<<<grid, 256, 0, st>>>(q, k, v, qt, dot, dout, lse, Dd, seq_T, dk, dv, part,
-                                             nsplit, s);
+  bwd_dkdv_mfma_kernel<<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dk, dv, part, nsplit, s);
   return hipGetLastError();
 }
 
@@ -241,24 +228,22 @@ hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit,
 // 64-key tiles of block 0 stream through LDS.  Per wave and tile:
 //   S^T = K Q^T, dP^T = V dO^T      (A = K, V rows from LDS; B = Q, dO in registers)
 //   dS^T = P^T * (dP^T - D)         (each lane owns one query: one lse, one D)
-//   dQ^T += K^T dS^T                (A = K^T tile from LDS, B = dS^T from the accumulator)
+//   dQ^T += K^T dS^T                (A = K columns through transposing LDS reads,
+//                                    B = dS^T from the accumulator)
 // ----------------------------------------------------------------------------------------
 constexpr int QBM = 128;
 constexpr int QBN = 64;
 
-struct DqStage {
-  bf16 k[QBN * QSTR];
-  bf16 v[QBN * QSTR];
-  bf16 kt[BD * TSTR];
-};
-
 template <bool FINAL>
-__global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ kt, const bf16* __restrict__ dO, const float* __restrict__ lse,
-    const float* __restrict__ Dd, const int32_t* __restrict__ seq_T, void* __restrict__ dq_out,
-    Shape s) {
-  __shared__ __attribute__((aligned(16))) DqStage sm[2];
+    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
+    const int32_t* __restrict__ seq_T, void* __restrict__ dq_out, Shape s) {
+  // Two stages in distinct arrays (the copy into one never stalls reads of the other).
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[QBN * BD];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[QBN * BD];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[QBN * BD];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[QBN * BD];
 
   const int n_qt = s.L / QBM;
   int bh, rank;
@@ -268,10 +253,11 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(
   const int bg = b * s.Hkv + g;
   const int T = clamp_T(seq_T, b, s.L);
   const int q0 = qtile * QBM;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int qw = q0 + wave * 32;
   const int my_q = qw + l32;
   const size_t row = (size_t)bh * s.L + my_q;
+  const float c2 = s.scale_log2;
 
   bf16x8 qf[8], df[8];
 #pragma unroll
@@ -281,10 +267,10 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(
   }
   const float lse2 = lse[row] * kLog2e;
   const float Dq = Dd[row];
+  const FragOffsets fo = make_frag_offsets(lane);
 
   const bf16* kb = k + (size_t)bg * s.KV * BD;
   const bf16* vb = v + (size_t)bg * s.KV * BD;
-  const bf16* ktb = kt + (size_t)bg * BD * s.L;
   const int kv_end = min(q0 + QBM, T);
   const int ntiles = (kv_end + QBN - 1) / QBN;
 
@@ -292,48 +278,22 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
 
-  bf16x8 rk[4], rv[4], rkt[4];
-  auto gload = [&](int j) {
-    const int k0 = j * QBN;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const size_t ro = (size_t)(k0 + (c >> 4)) * BD + (c & 15) * 8;
-      rk[i] = *reinterpret_cast<const bf16x8*>(kb + ro);
-      rv[i] = *reinterpret_cast<const bf16x8*>(vb + ro);
-      rkt[i] = *reinterpret_cast<const bf16x8*>(ktb + (size_t)(c >> 3) * s.L + k0 + (c & 7) * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-    DqStage& S = sm[buf];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<bf16x8*>(&S.k[(c >> 4) * QSTR + (c & 15) * 8]) = rk[i];
-      *reinterpret_cast<bf16x8*>(&S.v[(c >> 4) * QSTR + (c & 15) * 8]) = rv[i];
-      *reinterpret_cast<bf16x8*>(&S.kt[(c >> 3) * TSTR + (c & 7) * 8]) = rkt[i];
-    }
+  auto issue = [&](int j, bf16* dK, bf16* dV) {
+    load_tile<QBN, 4>(kb + (size_t)j * QBN * BD, BD, dK, wave, lane);
+    load_tile<QBN, 4>(vb + (size_t)j * QBN * BD, BD, dV, wave, lane);
   };
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
+  auto body = [&](int j, const bf16* cK, const bf16* cV, bf16* nK, bf16* nV) {
+    if (j + 1 < ntiles) issue(j + 1, nK, nV);
     const int k0 = j * QBN;
-    const DqStage& S = sm[buf];
     if (k0 <= qw + 31) {
       f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int off = (st * 32 + l32) * QSTR + 16 * t + 8 * hi;
-          sacc[st] = mfma32(*reinterpret_cast<const bf16x8*>(&S.k[off]), qf[t], sacc[st]);
-          pacc[st] = mfma32(*reinterpret_cast<const bf16x8*>(&S.v[off]), df[t], pacc[st]);
+        for (int st = 0; st < 2; ++st) {
+          sacc[st] = mfma32(frag_row(cK, st * 32, t, fo), qf[t], sacc[st]);
+          pacc[st] = mfma32(frag_row(cV, st * 32, t, fo), df[t], pacc[st]);
         }
       }
       const bool full = (k0 + QBN - 1 <= qw) && (k0 + QBN <= T);
@@ -342,7 +302,7 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float pv = exp2_fast(sacc[st][i] * s.scale_log2 - lse2);
+          float pv = exp2_fast(__builtin_fmaf(sacc[st][i], c2, -lse2));
           if (!full) {
             const int key = k0 + st * 32 + acc_row(i, hi);
             if (key > my_q || key >= T) pv = 0.f;
@@ -353,14 +313,20 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int off = (u * 32 + l32) * TSTR + 16 * c + 8 * hi;
-          acc[u] = mfma32(*reinterpret_cast<const bf16x8*>(&S.kt[off]), dsb[c], acc[u]);
-        }
+        for (int c = 0; c < 4; ++c)
+          acc[u] = mfma32(frag_col(cK, c, u, fo), dsb[c], acc[u]);
       }
     }
-    if (j + 1 < ntiles) lstore(buf ^ 1);
+    wait_vmem();
     __syncthreads();
+  };
+
+  if (ntiles > 0) issue(0, sK0, sV0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    body(j, sK0, sV0, sK1, sV1);
+    if (j + 1 < ntiles) body(j + 1, sK1, sV1, sK0, sV0);
   }
 
   // lane owns dQ[my_q][32u + 8*b4 + 4*hi + e] in acc[u][4*b4 + e]
@@ -392,15 +358,14 @@ __global__ __launch_bounds__(256) void bwd_dq_mfma_kernel(
 }
 
 hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
-                              const bf16* kt, const bf16* dout, const float* lse,
-                              const float* Dd, const int32_t* seq_T, void* dq, bool final_out,
-                              hipStream_t st) {
+                              const bf16* dout, const float* lse, const float* Dd,
+                              const int32_t* seq_T, void* dq, bool final_out, hipStream_t st) {
   const dim3 grid(s.B * s.Hq * (s.L / QBM));
   LaunchTimer timer("bwd_dq_mfma", st);
   if (final_out)
-    bwd_dq_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, v, kt, dout, lse, Dd, seq_T, dq, s);
+    bwd_dq_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
   else
-    bwd_dq_mfma_kernel<false><<<grid, 256, 0, st>>>(q, k, v, kt, dout, lse, Dd, seq_T, dq, s);
+    bwd_dq_mfma_kernel<false><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
   return hipGetLastError();
 }
 

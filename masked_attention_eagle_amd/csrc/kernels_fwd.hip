@@ -16,33 +16,32 @@ namespace ttt {
 // through LDS.  Per wave and tile:
 //   S^T[64 keys x 32 queries] = K Q^T     (A = K rows from LDS, B = Q kept in registers)
 //   online softmax on S^T (each lane owns one query; its keys sit in this lane and lane^32)
-//   O^T[128 x 32] += V^T P^T              (A = V^T from LDS, B = P^T straight from S^T)
+//   O^T[128 x 32] += V^T P^T              (A = V columns from LDS through transposing
+//                                          reads, B = P^T straight from S^T)
 // Tiles past min(q0 + 128, T) are never loaded (the BlockMask "skip" class); only tiles that
 // straddle the diagonal or the T edge evaluate the mask ("partial"); the rest are "full".
 // On partial tiles P is split into bf16 hi + lo parts so that rows with few keys (where one
 // rounding of P would show in O) keep fp32-level accuracy.
 //
-// K and V^T tiles are copied global -> LDS without passing through registers (two stages),
+// K and V tiles are copied global -> LDS without passing through registers (two stages),
 // which keeps the wave under 256 registers: two workgroups share a CU and the matrix cores
-// of one overlap the softmax of the other.  LDS rows are XOR-swizzled in 16-byte chunks so
-// that the 32 rows a wave reads at one column fall in distinct banks.
+// of one overlap the softmax of the other.
 // ----------------------------------------------------------------------------------------
 constexpr int FD = 128;  // head dim
 constexpr int FBM = 128; // queries per workgroup
 constexpr int FBN = 64;  // keys per tile
 
-// K tile: 64 rows x 256 B; 16-byte chunk c of row r stored at chunk c ^ (r & 15).
-__device__ __forceinline__ int kswz(int r, int c) { return r * 128 + ((c ^ (r & 15)) << 3); }
-// V^T tile: 128 rows x 128 B; chunk c of row r stored at chunk c ^ ((r & 7) ^ ((r >> 3) & 1)).
-__device__ __forceinline__ int vswz(int r, int c) { return r * 64 + ((c ^ ((r & 7) ^ ((r >> 3) & 1))) << 3); }
-
 template <bool FINAL>
 __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ vt,
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ seq_T, void* __restrict__ o_out, float* __restrict__ lse_out,
     Shape s) {
-  __shared__ __attribute__((aligned(1024))) bf16 sK[2][FBN * FD];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[2][FD * FBN];
+  // Two stages in distinct arrays: the compiler can then tell the copy into one stage from
+  // the reads of the other and does not wait for the copy before computing.
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[FBN * FD];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[FBN * FD];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[FBN * FD];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[FBN * FD];
 
   const int n_qt = s.L / FBM;
   int bh, rank;
@@ -62,7 +61,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
     for (int t = 0; t < 8; ++t) qf[t] = *reinterpret_cast<const bf16x8*>(qrow + 16 * t);
   }
   const bf16* kb = k + (size_t)(b * s.Hkv + g) * s.KV * FD;
-  const bf16* vb = vt + (size_t)(b * s.Hkv + g) * FD * s.L;
+  const bf16* vb = v + (size_t)(b * s.Hkv + g) * s.KV * FD;
 
   const int kv_end = min(q0 + FBM, T);
   const int ntiles = (kv_end + FBN - 1) / FBN;
@@ -72,40 +71,24 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
   float m = kNegInf, l = 0.f;  // running max of the raw logits q.k, and the softmax sum
   const float c2 = s.scale_log2;
+  const FragOffsets fo = make_frag_offsets(lane);
 
-  // Each wave copies 4 KB of K and 4 KB of V^T per tile: 4 instructions x 64 lanes x 16 B.
-  auto issue = [&](int j, int buf) {
-    const int k0 = j * FBN;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = wave * 4 + ii;
-      {
-        const int r = 4 * i + (lane >> 4), cp = lane & 15;
-        g2lds16(kb + (size_t)(k0 + r) * FD + ((cp ^ (r & 15)) << 3), &sK[buf][i * 512]);
-      }
-      {
-        const int r = 8 * i + (lane >> 3), cp = lane & 7;
-        g2lds16(vb + (size_t)r * s.L + k0 + ((cp ^ ((r & 7) ^ ((r >> 3) & 1))) << 3), &sV[buf][i * 512]);
-      }
-    }
+  auto issue = [&](int j, bf16* dK, bf16* dV) {
+    load_tile<FBN, 4>(kb + (size_t)j * FBN * FD, FD, dK, wave, lane);
+    load_tile<FBN, 4>(vb + (size_t)j * FBN * FD, FD, dV, wave, lane);
   };
 
-  if (ntiles > 0) issue(0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) issue(j + 1, buf ^ 1);
+  // One tile: prefetch tile j + 1 into (nK, nV) while computing tile j from (cK, cV).
+  auto body = [&](int j, const bf16* cK, const bf16* cV, bf16* nK, bf16* nV) {
+    if (j + 1 < ntiles) issue(j + 1, nK, nV);
     const int k0 = j * FBN;
     if (k0 <= qw + 31) {  // some query of this wave can see a key of the tile
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[buf][kswz(st * 32 + l32, 2 * t + hi)]);
-          sacc[st] = mfma32(a, qf[t], sacc[st]);
-        }
+        for (int st = 0; st < 2; ++st)
+          sacc[st] = mfma32(frag_row(cK, st * 32, t, fo), qf[t], sacc[st]);
       }
       const bool full = (k0 + FBN - 1 <= qw) && (k0 + FBN <= T);
       if (!full) {
@@ -150,12 +133,10 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sV[buf][vswz(u * 32 + l32, 2 * c + hi)]);
-            acc[u] = mfma32(a, pf[c], acc[u]);
-          }
+          for (int c = 0; c < 4; ++c)
+            acc[u] = mfma32(frag_col(cV, c, u, fo), pf[c], acc[u]);
         }
-      } else {  // P = hi + lo in bf16: both parts go through the same V^T operands
+      } else {  // P = hi + lo in bf16: both parts go through the same V operands
         bf16x8 pl[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -172,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sV[buf][vswz(u * 32 + l32, 2 * c + hi)]);
+            const bf16x8 a = frag_col(cV, c, u, fo);
             acc[u] = mfma32(a, pf[c], acc[u]);
             acc[u] = mfma32(a, pl[c], acc[u]);
           }
@@ -183,6 +164,14 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
     }
     wait_vmem();
     __syncthreads();
+  };
+
+  if (ntiles > 0) issue(0, sK0, sV0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    body(j, sK0, sV0, sK1, sV1);
+    if (j + 1 < ntiles) body(j + 1, sK1, sV1, sK0, sV0);
   }
 
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
@@ -217,15 +206,15 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
   }
 }
 
-hipError_t launch_fwd_causal_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* vt,
+hipError_t launch_fwd_causal_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                   const int32_t* seq_T, void* o, float* lse, bool final_out,
                                   hipStream_t st) {
   const dim3 grid(s.B * s.Hq * (s.L / FBM));
   LaunchTimer timer("fwd_causal_mfma", st);
   if (final_out)
-    fwd_causal_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, vt, seq_T, o, lse, s);
+    fwd_causal_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, v, seq_T, o, lse, s);
   else
-    fwd_causal_mfma_kernel<false><<<grid, 256, 0, st>>>(q, k, vt, seq_T, o, lse, s);
+    fwd_causal_mfma_kernel<false><<<grid, 256, 0, st>>>(q, k, v, seq_T, o, lse, s);
   return hipGetLastError();
 }
 

@@ -17,14 +17,8 @@ struct LaunchTimer {
   int slot_;
 };
 
-// Layout transform of bf16 head slabs: src slab s (rows [0, rows) of `row_dim` = 128
-// elements, slab stride src_slab_stride elements) -> dst slab s = [128][rows], with the
-// row index stored swapped (bits 2 and 3 of its position inside each group of 16).
-hipError_t launch_transpose_swz(const bf16* src, bf16* dst, int rows, size_t src_slab_stride,
-                                int nslabs, hipStream_t st);
-
 // Forward.
-hipError_t launch_fwd_causal_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* vt,
+hipError_t launch_fwd_causal_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                   const int32_t* seq_T, void* o, float* lse, bool final_out,
                                   hipStream_t st);
 template <typename T>
@@ -40,15 +34,14 @@ hipError_t launch_fwd_suffix(const Shape& s, const T* q, const T* k, const T* v,
 template <typename T>
 hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* Dd, hipStream_t st);
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
-                                const bf16* qt, const bf16* dot, const bf16* dout,
-                                const float* lse, const float* Dd, const int32_t* seq_T,
-                                bf16* dk, bf16* dv, float* part, int nsplit, hipStream_t st);
+                                const bf16* dout, const float* lse, const float* Dd,
+                                const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
+                                int nsplit, hipStream_t st);
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
                                   bf16* dv, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
-                              const bf16* kt, const bf16* dout, const float* lse,
-                              const float* Dd, const int32_t* seq_T, void* dq, bool final_out,
-                              hipStream_t st);
+                              const bf16* dout, const float* lse, const float* Dd,
+                              const int32_t* seq_T, void* dq, bool final_out, hipStream_t st);
 template <typename T>
 hipError_t launch_bwd_dkdv_valu(const Shape& s, const T* q, const T* k, const T* v,
                                 const T* dout, const float* lse, const float* Dd,
