@@ -47,12 +47,18 @@ def test_workspace_sizes():
     assert A.fwd_workspace_size(p) == rows * d * 4 + rows * 4
     assert A.fwd_workspace_size(P(step=0)) == 0
     assert A.fwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, step=0)) == 0
-    # D rows + fp32 dQ accumulator for step > 0
-    assert A.bwd_workspace_size(p) == rows * 4 + rows * d * 4
-    assert A.bwd_workspace_size(P(step=0)) == rows * 4
-    # 1 batch x 8 KV heads x 32 key tiles < 512 workgroups: heads split in two, fp32 partials
+    # D rows + fp32 dQ accumulator for step > 0 + fp32 dK/dV partial planes: each workgroup
+    # of the dK/dV kernel owns a pair of 128-key tiles, so 2 x 8 x 16 = 256 workgroups double
+    # to 512 by splitting each KV group's 4 query heads in two.
+    part = 2 * 2 * B * Hkv * L * d * 4
+    assert A.bwd_workspace_size(p) == rows * 4 + rows * d * 4 + part
+    assert A.bwd_workspace_size(P(step=0)) == rows * 4 + part
+    # 1 x 8 x 16 = 128 pair workgroups: heads split in four
     rows4 = 64 * L
-    assert A.bwd_workspace_size(P(B=1, Hq=64)) == rows4 * 4 + rows4 * d * 4 + 2 * 2 * 8 * L * d * 4
+    assert A.bwd_workspace_size(P(B=1, Hq=64)) == rows4 * 4 + rows4 * d * 4 + 4 * 2 * 8 * L * d * 4
+    # 8 x 8 x 8 = 512 already: no split, no partials
+    rows3 = 8 * 32 * 2048
+    assert A.bwd_workspace_size(P(B=8, L=2048)) == rows3 * 4 + rows3 * d * 4
     assert A.fwd_workspace_size(P(Hq=30)) == 0  # invalid params -> 0
 
 
