@@ -51,7 +51,23 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload number (2: the 8B draft layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run one plain device-to-device copy of MIB MiB (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    """One plain copy of known size, so that HBM byte counters can be scaled by what they read
+    for it (expected: mib MiB fetched and mib MiB written)."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": mib, "bytes": 2 * n}))
 
 
 def main():
@@ -67,6 +83,9 @@ def main():
     from masked_attention_eagle_amd import ttt_attn as A
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     lib = A.load()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)

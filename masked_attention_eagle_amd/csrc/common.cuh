@@ -64,6 +64,17 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
+// Reductions over the two halves of a wave (lane l with lane l ^ 32) on the vector ALU:
+// v_permlane32_swap exchanges the halves, leaving {x[l], x[l ^ 32]} in the two results.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;

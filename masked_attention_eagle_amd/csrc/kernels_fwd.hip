@@ -101,13 +101,14 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
           }
         }
       }
-      float rmax = kNegInf;
+      float rmax = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) rmax = fmaxf(rmax, fmaxf(sacc[st][i], sacc[st][i + 1]));
+        for (int i = 1; i < 15; i += 2) rmax = fmaxf(fmaxf(rmax, sacc[st][i]), sacc[st][i + 1]);
+        rmax = fmaxf(rmax, sacc[st][15]);
       }
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+      rmax = half_max(rmax);
       const float m_new = fmaxf(m, rmax);
       const float mc = (m_new == kNegInf) ? 0.f : m_new * c2;
       // Rescale the accumulator only when some row's running max moved (wave-uniform test).
@@ -159,8 +160,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
           }
         }
       }
-      lsum += __shfl_xor(lsum, 32);
-      l += lsum;
+      l += half_sum(lsum);
     }
     wait_vmem();
     __syncthreads();
