@@ -632,6 +632,121 @@ __global__ __launch_bounds__(256) void bwd_suffix_kernel(
   }
 }
 
+// Single pass with the step loop outside and every head of the group in registers: each
+// diagonal K/V row is read once per (row, group) and its dK/dV row is written right away;
+// dQ of all heads accumulates in registers and is written at the end.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
+    const int32_t* __restrict__ seq_T, const float* __restrict__ dq_acc, T* __restrict__ dq,
+    T* __restrict__ dk, T* __restrict__ dv, Shape s) {
+  constexpr int E = D / 16;
+  const int sub = threadIdx.x & 15;
+  const int blocks_per_bg = (s.L + 15) / 16;
+  const int bg = blockIdx.x / blocks_per_bg;
+  const int i = (blockIdx.x % blocks_per_bg) * 16 + (threadIdx.x >> 4);
+  if (i >= s.L) return;
+  const int b = bg / s.Hkv, g = bg % s.Hkv;
+  const int Tlen = clamp_T(seq_T, b, s.L);
+  const size_t kv_base = (size_t)bg * s.KV * D + (size_t)i * D + sub * E;
+  const size_t row0 = (size_t)(b * s.Hq + g * G) * s.L + i;
+  const bool live = i < Tlen;
+
+  float dqa[G][E];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) dqa[h][e] = 0.f;
+
+  if (live) {
+    float qv[G][E], ov[G][E], l2[G], Dh[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const size_t row = row0 + (size_t)h * s.L;
+      load_vec<T, E>(q + row * D + sub * E, qv[h]);
+      load_vec<T, E>(dO + row * D + sub * E, ov[h]);
+      l2[h] = lse[row] * kLog2e;
+      Dh[h] = Dd[row];
+    }
+    float kc[E], vc[E];
+    load_vec<T, E>(k + kv_base + (size_t)s.L * D, kc);
+    load_vec<T, E>(v + kv_base + (size_t)s.L * D, vc);
+    for (int t = 1; t <= s.step; ++t) {
+      float kn[E], vn[E];
+      if (t < s.step) {
+        load_vec<T, E>(k + kv_base + (size_t)(t + 1) * s.L * D, kn);
+        load_vec<T, E>(v + kv_base + (size_t)(t + 1) * s.L * D, vn);
+      }
+      float aK[E], aV[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) aK[e] = aV[e] = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float sd = 0.f, pd = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          sd += qv[h][e] * kc[e];
+          pd += ov[h][e] * vc[e];
+        }
+        sd = sum16(sd);
+        pd = sum16(pd);
+        const float p = exp2_fast(sd * s.scale_log2 - l2[h]);
+        const float ds = p * (pd - Dh[h]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          aV[e] += p * ov[h][e];
+          aK[e] += ds * qv[h][e];
+          dqa[h][e] += ds * kc[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) aK[e] *= s.scale;
+      store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, aK);
+      store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, aV);
+      if (t < s.step) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          kc[e] = kn[e];
+          vc[e] = vn[e];
+        }
+      }
+    }
+  } else {
+    float z[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) z[e] = 0.f;
+    for (int t = 1; t <= s.step; ++t) {
+      store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, z);
+      store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, z);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const size_t row = row0 + (size_t)h * s.L;
+    float a[E];
+    load_vec<float, E>(dq_acc + row * D + sub * E, a);
+#pragma unroll
+    for (int e = 0; e < E; ++e) a[e] += s.scale * dqa[h][e];
+    store_vec<T, E>(dq + row * D + sub * E, a);
+  }
+}
+
+template <typename T, int D>
+static hipError_t bwd_suffix_dispatch(const Shape& s, dim3 grid, hipStream_t st, const T* q,
+                                      const T* k, const T* v, const T* dout, const float* lse,
+                                      const float* Dd, const int32_t* seq_T, const float* dq_acc,
+                                      T* dq, T* dk, T* dv) {
+  switch (s.G) {
+    case 1: bwd_suffix_g_kernel<T, D, 1><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 2: bwd_suffix_g_kernel<T, D, 2><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 4: bwd_suffix_g_kernel<T, D, 4><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 8: bwd_suffix_g_kernel<T, D, 8><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    default: bwd_suffix_kernel<T, D><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_bwd_suffix(const Shape& s, const T* q, const T* k, const T* v, const T* dout,
                              const float* lse, const float* Dd, const int32_t* seq_T,
@@ -639,10 +754,8 @@ hipError_t launch_bwd_suffix(const Shape& s, const T* q, const T* k, const T* v,
   const dim3 grid(s.B * s.Hkv * ((s.L + 15) / 16));
   LaunchTimer timer("bwd_suffix", st);
   if (s.D == 64)
-    bwd_suffix_kernel<T, 64><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s);
-  else
-    bwd_suffix_kernel<T, 128><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s);
-  return hipGetLastError();
+    return bwd_suffix_dispatch<T, 64>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv);
+  return bwd_suffix_dispatch<T, 128>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv);
 }
 template hipError_t launch_bwd_suffix<float>(const Shape&, const float*, const float*,
                                              const float*, const float*, const float*,

@@ -358,17 +358,103 @@ __global__ __launch_bounds__(256) void fwd_suffix_kernel(
   }
 }
 
+// Same computation with the step loop outside and every head of the group in registers: each
+// diagonal K/V row is read once per (row, group), and step t + 1's rows are in flight while
+// step t is merged.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void fwd_suffix_g_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ seq_T, const float* __restrict__ oc,
+    const float* __restrict__ lsec, T* __restrict__ o, float* __restrict__ lse, Shape s) {
+  constexpr int E = D / 16;
+  const int sub = threadIdx.x & 15;
+  const int blocks_per_bg = (s.L + 15) / 16;
+  const int bg = blockIdx.x / blocks_per_bg;
+  const int i = (blockIdx.x % blocks_per_bg) * 16 + (threadIdx.x >> 4);
+  if (i >= s.L) return;
+  const int b = bg / s.Hkv, g = bg % s.Hkv;
+  const int Tlen = clamp_T(seq_T, b, s.L);
+  const size_t kv_base = (size_t)bg * s.KV * D + (size_t)i * D + sub * E;
+  const size_t row0 = (size_t)(b * s.Hq + g * G) * s.L + i;  // row of head g*G; heads are L rows apart
+
+  float acc[G][E], m[G], l[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const size_t row = row0 + (size_t)h * s.L;
+    load_vec<float, E>(oc + row * D + sub * E, acc[h]);
+    const float lc = lsec[row];
+    m[h] = lc * kLog2e;
+    l[h] = (lc == kNegInf) ? 0.f : 1.f;
+  }
+  if (i < Tlen && s.step > 0) {
+    float qv[G][E];
+#pragma unroll
+    for (int h = 0; h < G; ++h) load_vec<T, E>(q + (row0 + (size_t)h * s.L) * D + sub * E, qv[h]);
+    float kc[E], vc[E];
+    load_vec<T, E>(k + kv_base + (size_t)s.L * D, kc);
+    load_vec<T, E>(v + kv_base + (size_t)s.L * D, vc);
+    for (int t = 1; t <= s.step; ++t) {
+      float kn[E], vn[E];
+      if (t < s.step) {
+        load_vec<T, E>(k + kv_base + (size_t)(t + 1) * s.L * D, kn);
+        load_vec<T, E>(v + kv_base + (size_t)(t + 1) * s.L * D, vn);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dot += qv[h][e] * kc[e];
+        const float x = sum16(dot) * s.scale_log2;
+        const float m_new = fmaxf(m[h], x);
+        const float alpha = exp2_fast(m[h] - m_new), beta = exp2_fast(x - m_new);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = acc[h][e] * alpha + beta * vc[e];
+        l[h] = l[h] * alpha + beta;
+        m[h] = m_new;
+      }
+      if (t < s.step) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          kc[e] = kn[e];
+          vc[e] = vn[e];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const size_t row = row0 + (size_t)h * s.L;
+    const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
+    float ov[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) ov[e] = acc[h][e] * inv;
+    store_vec<T, E>(o + row * D + sub * E, ov);
+    if (sub == 0) lse[row] = l[h] > 0.f ? (m[h] + __log2f(l[h])) * kLn2 : kNegInf;
+  }
+}
+
+template <typename T, int D>
+static hipError_t fwd_suffix_dispatch(const Shape& s, dim3 grid, hipStream_t st, const T* q,
+                                      const T* k, const T* v, const int32_t* seq_T,
+                                      const float* oc, const float* lsec, T* o, float* lse) {
+  switch (s.G) {
+    case 1: fwd_suffix_g_kernel<T, D, 1><<<grid, 256, 0, st>>>(q, k, v, seq_T, oc, lsec, o, lse, s); break;
+    case 2: fwd_suffix_g_kernel<T, D, 2><<<grid, 256, 0, st>>>(q, k, v, seq_T, oc, lsec, o, lse, s); break;
+    case 4: fwd_suffix_g_kernel<T, D, 4><<<grid, 256, 0, st>>>(q, k, v, seq_T, oc, lsec, o, lse, s); break;
+    case 8: fwd_suffix_g_kernel<T, D, 8><<<grid, 256, 0, st>>>(q, k, v, seq_T, oc, lsec, o, lse, s); break;
+    default: fwd_suffix_kernel<T, D><<<grid, 256, 0, st>>>(q, k, v, seq_T, oc, lsec, o, lse, s); break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_fwd_suffix(const Shape& s, const T* q, const T* k, const T* v,
                              const int32_t* seq_T, const float* oc, const float* lsec, T* o,
                              float* lse, hipStream_t st) {
   const dim3 grid(s.B * s.Hkv * ((s.L + 15) / 16));
   LaunchTimer timer("fwd_suffix", st);
-  if (s.D == 64)
-    fwd_suffix_kernel<T, 64><<<grid, 256, 0, st>>>(q, k, v, seq_T, oc, lsec, o, lse, s);
-  else
-    fwd_suffix_kernel<T, 128><<<grid, 256, 0, st>>>(q, k, v, seq_T, oc, lsec, o, lse, s);
-  return hipGetLastError();
+  if (s.D == 64) return fwd_suffix_dispatch<T, 64>(s, grid, st, q, k, v, seq_T, oc, lsec, o, lse);
+  return fwd_suffix_dispatch<T, 128>(s, grid, st, q, k, v, seq_T, oc, lsec, o, lse);
 }
 template hipError_t launch_fwd_suffix<float>(const Shape&, const float*, const float*,
                                              const float*, const int32_t*, const float*,
