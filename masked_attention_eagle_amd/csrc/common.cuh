@@ -155,6 +155,14 @@ __device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
 // have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most N (< 16) of this wave's vector-memory operations are outstanding
+// (s_waitcnt vmcnt(N); the LDS and export counters are left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
+
 // ---------------------------------------------------------------------------------------
 // LDS tiles of 128 bf16 per row (256 bytes).  The 16-byte chunk c of row r is stored at
 // chunk c ^ swz(r).  Two read patterns hit these tiles:
