@@ -29,6 +29,35 @@ sys.path.insert(0, ROOT)
 METRIC = "TTT-attn fwd+bwd unmasked TFLOP/s + tokens/s at Q_LEN=4096, TTT=7; % roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+# Scaled FETCH_SIZE + WRITE_SIZE counter readings per kernel launch, taken with rocprofv3 on the
+# same workload; used only while the kernel's source is unchanged since they were taken.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+TRAFFIC_TAG = {2: "llama31_8b", 3: "padding_heavy", 4: "llama33_70b", 5: "qwen3_30b_a3b"}
+CSRC = os.path.join(ROOT, "masked_attention_eagle_amd", "csrc")
+
+
+def kernel_source(name: str) -> str:
+    if name.startswith("fwd_"):
+        return "kernels_fwd.hip"
+    return "kernels_aux.hip" if name == "bwd_rowdot" else "kernels_bwd.hip"
+
+
+def measured_traffic(config: int, name: str):
+    """HBM bytes per launch of kernel `name` from the committed counter summary, or None when
+    there is none for this workload or the kernel's source has changed since."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entry = json.load(f)[TRAFFIC_TAG[config]]["kernels"][name]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for fn in (kernel_source(name), "common.cuh"):
+        with open(os.path.join(CSRC, fn), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != entry.get("source_sha256_16"):
+        return None
+    return int(entry["bytes_per_launch"])
 
 
 def causal_pairs(L: int, T: int) -> int:
@@ -180,7 +209,8 @@ def main():
         achieved = alg[dom] / (mfma[dom]["avg_ms"] / 1e3) / 1e12
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic(args.config, dom)}
         for n in alg:
             if n in kstats:
                 a = alg[n] / (kstats[n]["avg_ms"] / 1e3) / 1e12
