@@ -53,7 +53,7 @@ enum ttt_attn_dtype {
 enum ttt_attn_status {
   TTT_OK = 0,
   TTT_E_NULL = -1,        /* a required pointer is NULL                              */
-  TTT_E_SHAPE = -2,       /* non-positive size, Hq % Hkv != 0, ttt_step < 0, overflow */
+  TTT_E_SHAPE = -2,       /* non-positive size, Hq % Hkv != 0, ttt_step < 0, scale <= 0, overflow */
   TTT_E_UNSUPPORTED = -3, /* head_dim/dtype/q_len combination not built (see below)  */
   TTT_E_ALIGN = -4,       /* a pointer is not 16-byte aligned                        */
   TTT_E_WORKSPACE = -5,   /* workspace smaller than *_workspace_size()               */
@@ -64,7 +64,8 @@ enum ttt_attn_status {
  * Problem description.  Supported combinations:
  *   dtype F32 : head_dim in {64, 128}, any q_len >= 1.
  *   dtype BF16: head_dim == 128, q_len a multiple of 128.
- * scale multiplies q.k before masking (1/sqrt(head_dim) in the usual setting).
+ * scale multiplies q.k before masking (1/sqrt(head_dim) in the usual setting); it must be
+ * finite and positive (the streaming softmax tracks the row maximum of the raw q.k).
  */
 typedef struct ttt_attn_params {
   int32_t batch;     /* B                                  */

@@ -190,6 +190,43 @@ __device__ __forceinline__ void load_tile(const bf16* g, int ld, bf16* lds, int 
   for (int i = wave; i < NROWS / 4; i += NWAVES) g2lds16(g + (size_t)(4 * i) * ld + lane_off, lds + i * 512);
 }
 
+// Buffer descriptor over `bytes` bytes at `base` (raw buffer: no stride, no format; reads past
+// the end return zero).  The address stays in scalar registers, so a copy costs each lane only
+// a 32-bit offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Asynchronous buffer -> LDS copy of 16 (or 4) bytes per lane: lane l writes lds_base +
+// SIZE * l from byte voff + soff of the buffer.
+template <int SIZE>
+__device__ __forceinline__ void buf2lds(__amdgpu_buffer_rsrc_t r, void* lds_base, unsigned voff, int soff) {
+  static_assert(SIZE == 16 || SIZE == 4, "copy size");
+  if constexpr (SIZE == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                             voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4,
+                                             voff, soff, 0, 0);
+}
+
+// Per-lane byte offset used by load_tile_buf (depends on the lane and on wave % 4 only).
+__device__ __forceinline__ unsigned tile_lane_offset(int wave, int lane) {
+  const int rl = lane >> 4;
+  return (unsigned)(rl * 128 + (((lane & 15) ^ ((rl << 2) | (wave & 3))) << 3)) * 2u;
+}
+
+// load_tile for a [NROWS][128] bf16 block starting at `g`, through a buffer descriptor: the
+// same swizzled layout, each wave instruction moving 4 rows (1 KB).  `lane_off` comes from
+// tile_lane_offset(wave, lane).
+template <int NROWS, int NWAVES>
+__device__ __forceinline__ void load_tile_buf(const bf16* g, bf16* lds, int wave, unsigned lane_off) {
+  static_assert(NWAVES % 4 == 0, "swizzle term must be constant per wave");
+  const __amdgpu_buffer_rsrc_t r = buffer_rsrc(g, NROWS * 256);
+#pragma unroll
+  for (int i = wave; i < NROWS / 4; i += NWAVES) buf2lds<16>(r, lds + i * 512, lane_off, i * 1024);
+}
+
 // Index of the calling wave inside its workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 

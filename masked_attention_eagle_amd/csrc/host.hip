@@ -69,7 +69,7 @@ int validate(const ttt_attn_params* p) {
       p->head_dim <= 0 || p->ttt_step < 0)
     return TTT_E_SHAPE;
   if (p->heads_q % p->heads_kv != 0) return TTT_E_SHAPE;
-  if (!isfinite(p->scale)) return TTT_E_SHAPE;
+  if (!isfinite(p->scale) || !(p->scale > 0.f)) return TTT_E_SHAPE;
   const int64_t kv = (int64_t)(p->ttt_step + 1) * p->q_len;
   if (kv > INT32_MAX) return TTT_E_SHAPE;
   // Thread counts of the largest grids must stay below 2^32 and element counts below 2^40.
@@ -173,7 +173,7 @@ const char* ttt_attn_status_string(int status) {
   switch (status) {
     case TTT_OK: return "ok";
     case TTT_E_NULL: return "null pointer argument";
-    case TTT_E_SHAPE: return "invalid shape (non-positive size, heads_q % heads_kv != 0, ttt_step < 0, non-finite scale or size overflow)";
+    case TTT_E_SHAPE: return "invalid shape (non-positive size, heads_q % heads_kv != 0, ttt_step < 0, scale not finite and positive, or size overflow)";
     case TTT_E_UNSUPPORTED: return "unsupported configuration (f32: head_dim 64 or 128; bf16: head_dim 128 and q_len % 128 == 0)";
     case TTT_E_ALIGN: return "pointer not 16-byte aligned";
     case TTT_E_WORKSPACE: return "workspace smaller than required";

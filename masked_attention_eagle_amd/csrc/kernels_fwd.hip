@@ -30,6 +30,7 @@ namespace ttt {
 constexpr int FD = 128;  // head dim
 constexpr int FBM = 128; // queries per workgroup
 constexpr int FBN = 64;  // keys per tile
+constexpr float kRescaleLog2 = 8.f;  // headroom of the unnormalised probabilities (base 2)
 
 template <bool FINAL>
 __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
@@ -109,16 +110,21 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
         rmax = fmaxf(rmax, sacc[st][15]);
       }
       rmax = half_max(rmax);
-      const float m_new = fmaxf(m, rmax);
-      const float mc = (m_new == kNegInf) ? 0.f : m_new * c2;
-      // Rescale the accumulator only when some row's running max moved (wave-uniform test).
-      if (__any(m_new > m)) {
-        const float alpha = exp2_fast(m * c2 - mc);
+      // The reference max m of a row moves only when the tile's max exceeds it by more than
+      // kRescaleLog2 in base-2 units.  Until then the tile's probabilities exp2((s - m) c2)
+      // stay below 2^kRescaleLog2, which fp32 sums and bf16 P carry with the same relative
+      // precision as values below 1, so the accumulator is rescaled only on the rare tiles
+      // where some row's logits jump that far (always on a row's first visible key).
+      const bool grow = rmax * c2 > m * c2 + kRescaleLog2;
+      if (__any(grow)) {
+        const float m_new = grow ? rmax : m;
+        const float alpha = grow ? exp2_fast((m - m_new) * c2) : 1.f;
         l *= alpha;
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[u] *= alpha;
+        m = m_new;
       }
-      m = m_new;
+      const float mc = (m == kNegInf) ? 0.f : m * c2;
       float lsum = 0.f;
       bf16x8 pf[4];
       if (full) {

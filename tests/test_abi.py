@@ -64,7 +64,8 @@ def test_workspace_sizes():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), -2), (dict(Hq=30), -2), (dict(step=-1), -2), (dict(L=-4), -2),
-    (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2),
+    (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2), (dict(scale=0.0), -2),
+    (dict(scale=-0.088), -2),
     (dict(d=64), -3), (dict(L=4000), -3), (dict(dtype=7), -3),
     (dict(dtype=A.TTT_DTYPE_F32, d=96), -3), (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10), -2),
 ])
