@@ -138,6 +138,14 @@ __device__ __forceinline__ void store_vec(T* p, const float* in) {
   }
 }
 
+// A pointer the whole wave agrees on, moved to scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+
 // Asynchronous global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
 // lane l of the wave writes lds_base + 16 * l; lds_base must be the same for the whole wave.
 __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
@@ -186,8 +194,15 @@ __device__ __forceinline__ void load_tile(const bf16* g, int ld, bf16* lds, int 
   static_assert(NWAVES % 4 == 0, "swizzle term must be constant per wave");
   const int rl = lane >> 4;
   const unsigned lane_off = (unsigned)(rl * ld + (((lane & 15) ^ ((rl << 2) | (wave & 3))) << 3));
+  // Scalar base + 32-bit per-lane byte offset: the copies use the saddr form and hold no
+  // 64-bit per-lane addresses in vector registers.
+  const char* base = reinterpret_cast<const char*>(uniform_ptr(g));
 #pragma unroll
-  for (int i = wave; i < NROWS / 4; i += NWAVES) g2lds16(g + (size_t)(4 * i) * ld + lane_off, lds + i * 512);
+  for (int i = wave; i < NROWS / 4; i += NWAVES) {
+    unsigned off = 2u * ((unsigned)(4 * i * ld) + lane_off);
+    asm volatile("" : "+v"(off));  // keeps the 32-bit offset form (no 64-bit copies to hold)
+    g2lds16(base + off, lds + i * 512);
+  }
 }
 
 // Buffer descriptor over `bytes` bytes at `base` (raw buffer: no stride, no format; reads past
@@ -230,41 +245,41 @@ __device__ __forceinline__ void load_tile_buf(const bf16* g, bf16* lds, int wave
 // Index of the calling wave inside its workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// Per-lane byte offsets of the matrix-core operand reads from a swizzled tile.  They depend
-// on the lane only; tile base, 32-row block and 16-row chunk add compile-time constants, so
-// every read is one VGPR offset plus an immediate.  The offsets are made opaque to the
-// compiler so that it keeps exactly these 16 registers instead of rebuilding an address per
-// (tile, fragment).
+// Per-lane byte offsets of the matrix-core operand reads from a swizzled tile.  With the
+// swizzle above, the offset of chunk pair t of a row read is row0 ^ 32t and that of column
+// block u of a column read is col0[k] ^ 64u (the swizzle only flips bits 5-7 of a byte
+// offset that has no carries into them), so three registers describe every read; tile base,
+// 32-row block and 16-row chunk add multiples of 256 bytes.
 struct FragOffsets {
-  int row[8];     // frag_row of row l32 (+ any multiple of 16), chunk 2t + hi: t = 0..7
-  int col[4][2];  // frag_col of column block 32u, rows 4h.. (k = 0) and 4h + 8.. (k = 1)
+  int row0;     // row l32, chunk hi (t = 0)
+  int col0[2];  // column block 0, rows 4h.. (k = 0) and 4h + 8.. (k = 1)
 };
 
 __device__ __forceinline__ FragOffsets make_frag_offsets(int lane) {
   FragOffsets f;
   const int l32 = lane & 31, hi = lane >> 5, sl = lane & 15;
+  f.row0 = 2 * (l32 * 128 + (((hi ^ swz(l32))) << 3));
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    f.row[t] = 2 * (l32 * 128 + ((((2 * t + hi) ^ swz(l32))) << 3));
-    asm volatile("" : "+v"(f.row[t]));
+  for (int k = 0; k < 2; ++k) {
+    const int r = 4 * hi + 8 * k + (sl >> 2);
+    const int col = 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+    f.col0[k] = 2 * tile_off(r, col);
   }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int r = 4 * hi + 8 * k + (sl >> 2);
-      const int col = 32 * u + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
-      f.col[u][k] = 2 * tile_off(r, col);
-      asm volatile("" : "+v"(f.col[u][k]));
-    }
-  }
+  return f;
+}
+
+// A copy of the offsets the compiler cannot see through: called at the top of a loop body,
+// it keeps the derived per-read offsets inside the body instead of hoisting them (and the
+// registers they would hold) out of the loop.
+__device__ __forceinline__ FragOffsets opaque(FragOffsets f) {
+  asm volatile("" : "+v"(f.row0), "+v"(f.col0[0]), "+v"(f.col0[1]));
   return f;
 }
 
 // Matrix-core operand with the contraction along the row (d) axis: rows rb + l32 (rb a
 // multiple of 32), elements 16t + 8*hi .. +7.
 __device__ __forceinline__ bf16x8 frag_row(const bf16* tile, int rb, int t, const FragOffsets& f) {
-  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile + rb * 128) + f.row[t]);
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile + rb * 128) + (f.row0 ^ (32 * t)));
 }
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
@@ -283,8 +298,8 @@ __device__ __forceinline__ bf16x4 lds_tr4(const void* p) {
 // its values.  Rows 16c.. share the swizzle of rows 0.., so c only moves the base.
 __device__ __forceinline__ bf16x8 frag_col(const bf16* tile, int c, int u, const FragOffsets& f) {
   const char* base = reinterpret_cast<const char*>(tile + 16 * c * 128);
-  const bf16x4 a = lds_tr4(base + f.col[u][0]);
-  const bf16x4 b = lds_tr4(base + f.col[u][1]);
+  const bf16x4 a = lds_tr4(base + (f.col0[0] ^ (64 * u)));
+  const bf16x4 b = lds_tr4(base + (f.col0[1] ^ (64 * u)));
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 

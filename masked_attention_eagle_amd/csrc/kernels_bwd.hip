@@ -45,7 +45,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 sQ1[KBM * BD];
   __shared__ __attribute__((aligned(1024))) bf16 sO1[KBM * BD];
   __shared__ __attribute__((aligned(256))) float sLD1[2 * KBM];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[KBN * BD];
 
   const int nkt = s.L / KBN;
   int unit, pair;
@@ -67,13 +66,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const int kw = k0 + wave * 32;
     const int my_key = kw + l32;
 
-    bf16x8 kf[8];
+    bf16x8 kf[8], vf[8];
     {
       const bf16* kr = k + ((size_t)bg * s.KV + my_key) * BD + 8 * hi;
+      const bf16* vr = v + ((size_t)bg * s.KV + my_key) * BD + 8 * hi;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(kr + 16 * t);
+      for (int t = 0; t < 8; ++t) {
+        kf[t] = *reinterpret_cast<const bf16x8*>(kr + 16 * t);
+        vf[t] = *reinterpret_cast<const bf16x8*>(vr + 16 * t);
+      }
     }
-    load_tile<KBN, 4>(v + ((size_t)bg * s.KV + k0) * BD, BD, sV, wave, lane);
     f32x16 dKacc[4], dVacc[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) dKacc[u] = dVacc[u] = f32x16{};
@@ -89,39 +91,49 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
       const size_t row0 = ((size_t)b * s.Hq + h) * s.L + q0;
       load_tile<KBM, 4>(q + row0 * BD, BD, dQ, wave, lane);
       load_tile<KBM, 4>(dO + row0 * BD, BD, dOt, wave, lane);
-      if (wave == 0) g2lds4(lane < KBM ? lse + row0 + lane : Dd + row0 + (lane - KBM), dLD);
+      if (wave == 0) {  // lse of the 32 rows to dLD[0, 32), D to dLD[32, 64)
+        unsigned off = 4u * (lane & (KBM - 1));
+        asm volatile("" : "+v"(off));
+        if (lane < KBM)
+          g2lds4(reinterpret_cast<const char*>(uniform_ptr(lse + row0)) + off, dLD);
+        else
+          g2lds4(reinterpret_cast<const char*>(uniform_ptr(Dd + row0)) + off, dLD);
+      }
     };
 
     auto body = [&](int it, const bf16* cQ, const bf16* cO, const float* cLD, bf16* nQ, bf16* nO,
                     float* nLD) {
-      if (it + 1 < total) issue(it + 1, nQ, nO, nLD);
+      const FragOffsets fl = opaque(fo);
       const int q0 = q_first + (it % nq) * KBM;
-      if (kw < T && q0 + KBM - 1 >= kw) {
-        // S, then P (kept in bf16 only), then dP: one accumulator tile live at a time.
+      const bool live = kw < T && q0 + KBM - 1 >= kw;
+      if (!live && it + 1 < total) issue(it + 1, nQ, nO, nLD);
+      if (live) {
+        // S, then P (kept in bf16 only), then dP: one accumulator tile live at a time.  The
+        // next tile's copy is issued after the S products, so that nothing waited for before
+        // them (K fragments the allocator parks in scratch) waits for that copy too.
         f32x16 acc = f32x16{};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc = mfma32(frag_row(cQ, 0, t, fo), kf[t], acc);
+        for (int t = 0; t < 8; ++t) acc = mfma32(frag_row(cQ, 0, t, fl), kf[t], acc);
+        if (it + 1 < total) issue(it + 1, nQ, nO, nLD);
         const bool full = (kw + 31 <= q0) && (kw + 32 <= T);
+        // key > query row q0 + acc_row(i, hi)  <=>  dkey > 8 * (i / 4) + i % 4 (a constant)
+        const int dkey = my_key >= T ? KBM : my_key - q0 - 4 * hi;
         bf16x8 pb[2], dsb[2];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int r0 = 8 * i4 + 4 * hi;
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&cLD[r0]);
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&cLD[8 * i4 + 4 * hi]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
             float pv = exp2_fast(__builtin_fmaf(acc[i], c2, -L4[e] * kLog2e));
-            if (!full) {
-              const int qq = q0 + r0 + e;
-              if (my_key > qq || my_key >= T) pv = 0.f;
-            }
+            if (!full && dkey > 8 * i4 + e) pv = 0.f;
             pb[i >> 3][i & 7] = (bf16)pv;
           }
         }
         acc = f32x16{};
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          acc = mfma32(frag_row(cO, 0, t, fo), frag_row(sV, wave * 32, t, fo), acc);
+          acc = mfma32(frag_row(cO, 0, t, fl), vf[t], acc);
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const f32x4 D4 = *reinterpret_cast<const f32x4*>(&cLD[KBM + 8 * i4 + 4 * hi]);
@@ -135,14 +147,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
           for (int c = 0; c < 2; ++c)
-            dVacc[u] = mfma32(pb[c], frag_col(cO, c, u, fo), dVacc[u]);
+            dVacc[u] = mfma32(pb[c], frag_col(cO, c, u, fl), dVacc[u]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
           for (int c = 0; c < 2; ++c)
-            dKacc[u] = mfma32(dsb[c], frag_col(cQ, c, u, fo), dKacc[u]);
+            dKacc[u] = mfma32(dsb[c], frag_col(cQ, c, u, fl), dKacc[u]);
         }
       }
       wait_vmem();
@@ -157,26 +169,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
       if (it + 1 < total) body(it + 1, sQ1, sO1, sLD1, sQ0, sO0, sLD0);
     }
 
-    // lane owns d = 32u + l32 of key rows kw + acc_row(i, hi)
+    // lane owns d = 32u + l32 of key rows kw + acc_row(i, hi).  The lane index goes through
+    // an opaque copy so that the output offsets are formed here rather than hoisted out of
+    // the tile loop, where they would hold registers.
+    int lo = lane;
+    asm volatile("" : "+v"(lo));
+    const int ohi = lo >> 5, ol32 = lo & 31;
     if (nsplit == 1) {
+      bf16* dkp = dk + ((size_t)bg * s.KV + kw) * BD;
+      bf16* dvp = dv + ((size_t)bg * s.KV + kw) * BD;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const size_t o = ((size_t)bg * s.KV + kw + acc_row(i, hi)) * BD + 32 * u + l32;
-          dk[o] = (bf16)(dKacc[u][i] * s.scale);
-          dv[o] = (bf16)dVacc[u][i];
+          const int o = acc_row(i, ohi) * BD + 32 * u + ol32;
+          dkp[o] = (bf16)(dKacc[u][i] * s.scale);
+          dvp[o] = (bf16)dVacc[u][i];
         }
       }
     } else {
       const size_t plane = (size_t)s.B * s.Hkv * s.L * BD;
-      float* pk = part + (size_t)split * 2 * plane;
+      float* pk = part + (size_t)split * 2 * plane + ((size_t)bg * s.L + kw) * BD;
       float* pv = pk + plane;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const size_t o = ((size_t)bg * s.L + kw + acc_row(i, hi)) * BD + 32 * u + l32;
+          const int o = acc_row(i, ohi) * BD + 32 * u + ol32;
           pk[o] = dKacc[u][i] * s.scale;
           pv[o] = dVacc[u][i];
         }
@@ -284,6 +303,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
   };
 
   auto body = [&](int j, const bf16* cK, const bf16* cV, bf16* nK, bf16* nV) {
+    const FragOffsets fl = opaque(fo);
     if (j + 1 < ntiles) issue(j + 1, nK, nV);
     const int k0 = j * QBN;
     if (k0 <= qw + 31) {
@@ -292,8 +312,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
       for (int t = 0; t < 8; ++t) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          sacc[st] = mfma32(frag_row(cK, st * 32, t, fo), qf[t], sacc[st]);
-          pacc[st] = mfma32(frag_row(cV, st * 32, t, fo), df[t], pacc[st]);
+          sacc[st] = mfma32(frag_row(cK, st * 32, t, fl), qf[t], sacc[st]);
+          pacc[st] = mfma32(frag_row(cV, st * 32, t, fl), df[t], pacc[st]);
         }
       }
       const bool full = (k0 + QBN - 1 <= qw) && (k0 + QBN <= T);
@@ -314,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          acc[u] = mfma32(frag_col(cK, c, u, fo), dsb[c], acc[u]);
+          acc[u] = mfma32(frag_col(cK, c, u, fl), dsb[c], acc[u]);
       }
     }
     wait_vmem();

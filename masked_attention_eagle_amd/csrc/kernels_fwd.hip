@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
 
   // One tile: prefetch tile j + 1 into (nK, nV) while computing tile j from (cK, cV).
   auto body = [&](int j, const bf16* cK, const bf16* cV, bf16* nK, bf16* nV) {
+    const FragOffsets fl = opaque(fo);
     if (j + 1 < ntiles) issue(j + 1, nK, nV);
     const int k0 = j * FBN;
     if (k0 <= qw + 31) {  // some query of this wave can see a key of the tile
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
       for (int t = 0; t < 8; ++t) {
 #pragma unroll
         for (int st = 0; st < 2; ++st)
-          sacc[st] = mfma32(frag_row(cK, st * 32, t, fo), qf[t], sacc[st]);
+          sacc[st] = mfma32(frag_row(cK, st * 32, t, fl), qf[t], sacc[st]);
       }
       const bool full = (k0 + FBN - 1 <= qw) && (k0 + FBN <= T);
       if (!full) {
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            acc[u] = mfma32(frag_col(cV, c, u, fo), pf[c], acc[u]);
+            acc[u] = mfma32(frag_col(cV, c, u, fl), pf[c], acc[u]);
         }
       } else {  // P = hi + lo in bf16: both parts go through the same V operands
         bf16x8 pl[4];
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const bf16x8 a = frag_col(cV, c, u, fo);
+            const bf16x8 a = frag_col(cV, c, u, fl);
             acc[u] = mfma32(a, pf[c], acc[u]);
             acc[u] = mfma32(a, pl[c], acc[u]);
           }
