@@ -14,6 +14,13 @@ tensor):
   * per-sequence valid lengths of the padding-heavy workload:
     ``[cfg, 99, 4]``, integers uniform on [256, 2048] inclusive.
   * values are N(0, 1) in fp32, rounded to nearest-even bf16 for bf16 workloads.
+
+Inputs of the in-place masked softmax-loss gradient (``loss_case``), one stream
+``[seed, 200, slot]`` per tensor: logits z = 2 * N(0, 1) (slot 0); target
+distribution p = a row of Gamma(0.05) draws divided by its sum (a peaked,
+sparse-looking distribution, slot 1); per-row upstream weight g = mask / (number
+of unmasked rows) with 10% of the rows masked (slot 2).  z and p are rounded to
+bf16 for bf16 cases.
 """
 from __future__ import annotations
 
@@ -110,3 +117,28 @@ def make_case(seed: int, B: int, Hq: int, Hkv: int, d: int, L: int, step: int, T
     v = _normal([seed, step, 12], (B, Hkv, (step + 1) * L, d), dtype)
     do = _normal([seed, step, 13], (B, Hq, L, d), dtype)
     return q, k, v, do, T
+
+
+# Loss-gradient workload: the draft LM head of one TTT step of the Llama-3.1-8B-shaped
+# layer (B * Q_LEN = 2 * 4096 tokens) over a 32,000-entry draft vocabulary.
+LOSS_WORKLOADS = {
+    "llama3.1-8b-draft-lmhead N8192 V32000": (8192, 32000),
+}
+
+
+def loss_case(seed: int, N: int, V: int, dtype: str, mask_frac: float = 0.1):
+    """z [N, V], p [N, V] (fp32 arrays, bf16-rounded for bf16) and g [N] fp32."""
+    z = _normal([seed, 200, 0], (N, V), "f32") * np.float32(2.0)
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 200, 1]))
+    w = rng.gamma(0.05, size=(N, V)).astype(np.float64)
+    w += 1e-30
+    p = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 200, 2]))
+    keep = rng.uniform(size=N) >= mask_frac
+    keep[0] = True
+    if N > 1:
+        keep[-1] = False
+    g = (keep / keep.sum()).astype(np.float32)
+    if dtype == "bf16":
+        z, p = round_to_bf16(z), round_to_bf16(p)
+    return z, p, g
