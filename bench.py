@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload number (2: the 8B draft layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--loss", action="store_true",
+                    help="measure the in-place masked softmax-loss gradient on the draft LM head "
+                         "of one TTT step (N = 8192 tokens, V = 32000, bf16) instead")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run one plain device-to-device copy of MIB MiB (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -114,6 +117,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.loss:
+        bench_loss(args)
         return
     lib = A.load()
     dev = torch.device("cuda", 0)
@@ -251,6 +257,87 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, T, steps)
     print(json.dumps(out))
+
+
+def bench_loss(args):
+    """One step = one in-place loss-gradient call over the whole [N, V] logits of a TTT step.
+    value = algorithmic HBM bytes (read z and p, write z; read g, write the loss) / time."""
+    import torch
+    from masked_attention_eagle_amd import inputs
+    from masked_attention_eagle_amd import ttt_attn as A
+    name = "llama3.1-8b-draft-lmhead N8192 V32000"
+    N, V = inputs.LOSS_WORKLOADS[name]
+    A.load()
+    z, p, g = inputs.loss_case_device(11, N, V, "bf16")
+    loss = torch.empty((N,), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        A.loss_grad_inplace(z, p, g, loss)
+    torch.cuda.synchronize()
+    timing = not args.no_kernel_timing
+    if timing:
+        A.timing_reset()
+        A.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        A.loss_grad_inplace(z, p, g, loss)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    kernels = {}
+    if timing:
+        A.timing_enable(False)
+        kernels = A.timing_read()
+    alg = 3 * N * V * 2 + 2 * N * 4
+    roofline = None
+    if "loss_grad" in kernels:
+        n, ms = kernels["loss_grad"]
+        avg = ms / n / 1e3
+        gbs = alg / avg / 1e9
+        roofline = {"kernel": "loss_grad", "bound": "hbm", "achieved": round(gbs, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "traffic": measured_traffic_loss("loss_grad")}
+    out = {"metric": "in-place masked softmax-loss gradient, algorithmic HBM GB/s", "value": round(alg / sec / 1e9, 1),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(sec * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": name, "rows": N, "vocab": V}, "alg_bytes_per_step": alg,
+           "roofline": roofline}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_loss(V)
+    print(json.dumps(out))
+
+
+def measured_traffic_loss(name):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entry = json.load(f)["lmhead_loss"]["kernels"][name]
+    except (OSError, KeyError, ValueError):
+        return None
+    import hashlib
+    h = hashlib.sha256()
+    for fn in ("kernels_loss.hip", "common.cuh"):
+        with open(os.path.join(CSRC, fn), "rb") as f:
+            h.update(f.read())
+    return int(entry["bytes_per_launch"]) if h.hexdigest()[:16] == entry.get("source_sha256_16") else None
+
+
+def cpu_baseline_loss(V):
+    """The fp64 oracle on 1024 rows of the same shape, in the same unit (GB/s of the kernel's
+    algorithmic bytes for those rows)."""
+    from masked_attention_eagle_amd import inputs
+    from oracle import loss_oracle as LO
+    rows = 1024
+    z, p, g = inputs.loss_case(11, rows, V, "bf16")
+    t0 = time.perf_counter()
+    LO.loss_and_grad(z, p, g)
+    sec = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    return {"value": round((3 * rows * V * 2 + 2 * rows * 4) / sec / 1e9, 4), "unit": "GB/s",
+            "cores": cores, "kind": "oracle", "seconds": round(sec, 3),
+            "sample": f"loss and gradient of {rows} rows x {V} columns"}
 
 
 def cpu_baseline(w, T, steps):

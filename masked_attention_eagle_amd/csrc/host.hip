@@ -6,6 +6,7 @@
 
 #include "launch.h"
 #include "ttt_attn.h"
+#include "ttt_loss.h"
 
 namespace ttt {
 
@@ -289,6 +290,26 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
       e = launch_bwd_suffix<float>(s, qf, kf, vf, dof, lse, Dd, seq_T, dqacc, (float*)dq,
                                    (float*)dk, (float*)dv, st);
   }
+  return hip_status(e);
+}
+
+int ttt_loss_grad_inplace(const ttt_loss_params* p, void* z, const void* target, const float* g,
+                          float* loss, void* stream) {
+  if (!p) return TTT_E_NULL;
+  if (p->rows < 1 || p->vocab < 1 || p->rows >= (1ll << 31) ||
+      p->rows * (int64_t)p->vocab >= (1ll << 40))
+    return TTT_E_SHAPE;
+  if (p->vocab % 8 != 0 || (p->dtype != TTT_DTYPE_BF16 && p->dtype != TTT_DTYPE_F32))
+    return TTT_E_UNSUPPORTED;
+  if (!z || !target || !g) return TTT_E_NULL;
+  if (!aligned16(z) || !aligned16(target) || ((uintptr_t)g & 3) || ((uintptr_t)loss & 3))
+    return TTT_E_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (p->dtype == TTT_DTYPE_BF16)
+    e = launch_loss_grad<bf16>(p->rows, p->vocab, (bf16*)z, (const bf16*)target, g, loss, st);
+  else
+    e = launch_loss_grad<float>(p->rows, p->vocab, (float*)z, (const float*)target, g, loss, st);
   return hip_status(e);
 }
 

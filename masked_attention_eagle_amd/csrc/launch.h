@@ -55,4 +55,9 @@ hipError_t launch_bwd_suffix(const Shape& s, const T* q, const T* k, const T* v,
                              const float* lse, const float* Dd, const int32_t* seq_T,
                              const float* dq_acc, T* dq, T* dk, T* dv, hipStream_t st);
 
+// In-place masked softmax-loss gradient.
+template <typename T>
+hipError_t launch_loss_grad(int64_t rows, int V, T* z, const T* p, const float* g, float* loss,
+                            hipStream_t st);
+
 }  // namespace ttt

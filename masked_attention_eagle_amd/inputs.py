@@ -17,8 +17,8 @@ tensor):
 
 Inputs of the in-place masked softmax-loss gradient (``loss_case``), one stream
 ``[seed, 200, slot]`` per tensor: logits z = 2 * N(0, 1) (slot 0); target
-distribution p = a row of Gamma(0.05) draws divided by its sum (a peaked,
-sparse-looking distribution, slot 1); per-row upstream weight g = mask / (number
+distribution p = a row of E**6 draws (E standard exponential) divided by its sum
+(a peaked distribution: a few columns carry most of the mass, slot 1); per-row upstream weight g = mask / (number
 of unmasked rows) with 10% of the rows masked (slot 2).  z and p are rounded to
 bf16 for bf16 cases.
 """
@@ -130,9 +130,11 @@ def loss_case(seed: int, N: int, V: int, dtype: str, mask_frac: float = 0.1):
     """z [N, V], p [N, V] (fp32 arrays, bf16-rounded for bf16) and g [N] fp32."""
     z = _normal([seed, 200, 0], (N, V), "f32") * np.float32(2.0)
     rng = np.random.default_rng(np.random.SeedSequence([seed, 200, 1]))
-    w = rng.gamma(0.05, size=(N, V)).astype(np.float64)
-    w += 1e-30
-    p = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    p = np.empty((N, V), dtype=np.float32)
+    for r0 in range(0, N, 256):  # row chunks bound the fp64 temporaries (same stream)
+        r1 = min(N, r0 + 256)
+        w = rng.standard_exponential(size=(r1 - r0, V), dtype=np.float32) ** 6
+        p[r0:r1] = w / w.sum(axis=1, keepdims=True, dtype=np.float64)
     rng = np.random.default_rng(np.random.SeedSequence([seed, 200, 2]))
     keep = rng.uniform(size=N) >= mask_frac
     keep[0] = True
@@ -142,3 +144,25 @@ def loss_case(seed: int, N: int, V: int, dtype: str, mask_frac: float = 0.1):
     if dtype == "bf16":
         z, p = round_to_bf16(z), round_to_bf16(p)
     return z, p, g
+
+
+def loss_case_device(seed: int, N: int, V: int, dtype: str, device="cuda", mask_frac: float = 0.1):
+    """The loss_case recipe drawn with torch's seeded generator on the device (for the full-size
+    workload, where the host draws take tens of seconds).  Returns torch tensors z, p (dtype)
+    and g (fp32); tests copy the rows they check to the host before the in-place call."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1000003 + 200)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    z = (2.0 * torch.randn((N, V), generator=gen, device=device)).to(dt)
+    p = torch.empty((N, V), dtype=dt, device=device)
+    for r0 in range(0, N, 1024):
+        r1 = min(N, r0 + 1024)
+        w = torch.empty((r1 - r0, V), device=device).exponential_(generator=gen) ** 6
+        p[r0:r1] = (w / w.sum(dim=1, keepdim=True, dtype=torch.float64).float()).to(dt)
+    keep = torch.rand((N,), generator=gen, device=device) >= mask_frac
+    keep[0] = True
+    if N > 1:
+        keep[-1] = False
+    g = (keep.float() / keep.sum().float()).contiguous()
+    return z.contiguous(), p.contiguous(), g

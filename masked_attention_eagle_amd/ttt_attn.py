@@ -1,4 +1,5 @@
-"""Python binding of the C ABI in ``include/ttt_attn.h`` (ctypes; argument marshalling only).
+"""Python binding of the C ABI in ``include/ttt_attn.h`` and ``include/ttt_loss.h`` (ctypes;
+argument marshalling only).
 
 Every step of the computation runs in the HIP library ``libttt_attn.so``; this module only
 checks tensor metadata, allocates outputs and workspace with torch, and passes pointers and
@@ -28,6 +29,7 @@ EXPORTS = (
     "ttt_attn_status_string", "ttt_attn_version", "ttt_attn_timing_enable",
     "ttt_attn_timing_read", "ttt_attn_timing_reset",
 )
+LOSS_EXPORTS = ("ttt_loss_grad_inplace",)
 
 
 class TTTError(RuntimeError):
@@ -42,6 +44,10 @@ class Params(ctypes.Structure):
         ("q_len", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ttt_step", ctypes.c_int32),
         ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
     ]
+
+
+class LossParams(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("vocab", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class KernelTime(ctypes.Structure):
@@ -79,6 +85,8 @@ def load() -> ctypes.CDLL:
     lib.ttt_attn_timing_read.restype = ctypes.c_int
     lib.ttt_attn_timing_reset.argtypes = []
     lib.ttt_attn_timing_reset.restype = None
+    lib.ttt_loss_grad_inplace.argtypes = [ctypes.POINTER(LossParams), vp, vp, vp, vp, vp]
+    lib.ttt_loss_grad_inplace.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -244,3 +252,22 @@ def ttt_attention(q, k, v, seq_T, scale: Optional[float] = None):
 
 fwd = ttt_attn_fwd
 bwd = ttt_attn_bwd
+
+
+def loss_grad_inplace(z, target, g, loss=None, want_loss: bool = True):
+    """In-place masked softmax-loss gradient (``ttt_loss_grad_inplace``): z [N, V] logits are
+    overwritten with -(p g - softmax(z) s), s = g sum(p); returns the per-row loss [N] fp32
+    (or None when ``want_loss`` is False and no ``loss`` tensor is given)."""
+    import torch
+    _require(z, "z")
+    N, V = z.shape
+    _require(target, "target", z.dtype, (N, V))
+    _require(g, "g", torch.float32, (N,))
+    if loss is None and want_loss:
+        loss = torch.empty((N,), dtype=torch.float32, device=z.device)
+    if loss is not None:
+        _require(loss, "loss", torch.float32, (N,))
+    p = LossParams(N, V, _dtype_code(z))
+    _check(load().ttt_loss_grad_inplace(ctypes.byref(p), z.data_ptr(), target.data_ptr(), g.data_ptr(),
+                                        loss.data_ptr() if loss is not None else None, _stream()))
+    return loss

@@ -8,13 +8,14 @@ import pytest
 
 from masked_attention_eagle_amd import ttt_attn as A
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ttt_attn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "ttt_attn.h")
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(name="ttt_attn.h", prefix="ttt_attn_"):
+    text = open(os.path.join(INCLUDE, name)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ttt_attn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(" + prefix + r"\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -24,6 +25,31 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert lib.ttt_attn_version() == 100
+    loss_declared = header_functions("ttt_loss.h", "ttt_loss_")
+    assert set(loss_declared) == set(A.LOSS_EXPORTS)
+    for name in loss_declared:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("rows,vocab,dtype,code", [
+    (0, 32000, A.TTT_DTYPE_BF16, -2), (8, 0, A.TTT_DTYPE_BF16, -2), (1 << 20, 1 << 21, A.TTT_DTYPE_F32, -2),
+    (8, 32004, A.TTT_DTYPE_BF16, -3), (8, 32000, 5, -3),
+])
+def test_loss_validation_errors(rows, vocab, dtype, code):
+    lib = A.load()
+    p = A.LossParams(rows, vocab, dtype)
+    f = ctypes.c_void_p(16)
+    assert lib.ttt_loss_grad_inplace(ctypes.byref(p), f, f, f, f, None) == code
+
+
+def test_loss_null_and_align_errors():
+    lib = A.load()
+    p = A.LossParams(8, 32000, A.TTT_DTYPE_BF16)
+    good, odd = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 8)
+    assert lib.ttt_loss_grad_inplace(None, good, good, good, good, None) == -1
+    assert lib.ttt_loss_grad_inplace(ctypes.byref(p), None, good, good, good, None) == -1
+    assert lib.ttt_loss_grad_inplace(ctypes.byref(p), good, good, None, good, None) == -1
+    assert lib.ttt_loss_grad_inplace(ctypes.byref(p), good, odd, good, good, None) == -4
 
 
 def test_status_strings():
