@@ -9,12 +9,15 @@
 //
 // One workgroup per row.  The cached variant keeps the row's z and p in registers between
 // the statistics and the write, so HBM sees one read of z and p and one write of z (the
-// minimum); the streaming variant (vocabularies too long to hold) reads the row twice.
+// minimum); the streaming variant (vocabularies too long to hold) reads the row twice.  The
+// cached variant is held to 128 registers so that two rows (16 waves) share a CU: one row's
+// reductions and exponentials overlap the other's memory traffic.
 #include "launch.h"
 
 namespace ttt {
 
 constexpr int LT = 512;  // threads per row
+constexpr int NW = LT / 64;  // waves per row
 
 // 8 consecutive elements of a row, kept in their storage type (bf16: 4 registers).
 template <typename T> struct Vec8;
@@ -34,7 +37,7 @@ template <> struct Vec8<float> {
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const float* in) { store_vec<T, 8>(p, in); }
 
-// Block-wide reductions over the LT threads (8 waves): wave shuffles, then one LDS round.
+// Block-wide reductions over the LT threads (NW waves): wave shuffles, then one LDS round.
 __device__ __forceinline__ float block_max(float x, float* red) {
   x = wave_max(x);
   const int w = threadIdx.x >> 6;
@@ -42,7 +45,7 @@ __device__ __forceinline__ float block_max(float x, float* red) {
   __syncthreads();
   float r = red[0];
 #pragma unroll
-  for (int i = 1; i < LT / 64; ++i) r = fmaxf(r, red[i]);
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, red[i]);
   __syncthreads();
   return r;
 }
@@ -54,16 +57,16 @@ __device__ __forceinline__ void block_sum3(float& a, float& b, float& c, float* 
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     red[w] = a;
-    red[8 + w] = b;
-    red[16 + w] = c;
+    red[NW + w] = b;
+    red[2 * NW + w] = c;
   }
   __syncthreads();
   a = b = c = 0.f;
 #pragma unroll
-  for (int i = 0; i < LT / 64; ++i) {
+  for (int i = 0; i < NW; ++i) {
     a += red[i];
-    b += red[8 + i];
-    c += red[16 + i];
+    b += red[NW + i];
+    c += red[2 * NW + i];
   }
   __syncthreads();
 }
@@ -89,11 +92,11 @@ __device__ __forceinline__ RowStats finish_row(float m, float sum_e, float sum_p
 
 // NV vectors of 8 elements per thread stay in registers (V <= LT * 8 * NV).
 template <typename T, int NV>
-__global__ __launch_bounds__(LT) void loss_grad_cached_kernel(T* __restrict__ z,
+__global__ __launch_bounds__(LT, 4) void loss_grad_cached_kernel(T* __restrict__ z,
                                                               const T* __restrict__ p,
                                                               const float* __restrict__ g,
                                                               float* __restrict__ loss, int V) {
-  __shared__ float red[24];
+  __shared__ float red[3 * NW];
   const size_t row = blockIdx.x;
   T* zr = z + row * (size_t)V;
   const T* pr = p + row * (size_t)V;
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(LT) void loss_grad_stream_kernel(T* __restrict__ z,
                                                               const T* __restrict__ p,
                                                               const float* __restrict__ g,
                                                               float* __restrict__ loss, int V) {
-  __shared__ float red[24];
+  __shared__ float red[3 * NW];
   const size_t row = blockIdx.x;
   T* zr = z + row * (size_t)V;
   const T* pr = p + row * (size_t)V;
