@@ -309,7 +309,7 @@ def bench_loss(args):
 def measured_traffic_loss(name):
     try:
         with open(TRAFFIC_FILE) as f:
-            entry = json.load(f)["lmhead_loss"]["kernels"][name]
+            entry = json.load(f)["lmhead"]["kernels"][name]
     except (OSError, KeyError, ValueError):
         return None
     import hashlib

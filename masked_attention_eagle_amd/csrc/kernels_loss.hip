@@ -10,8 +10,9 @@
 // One workgroup per row.  The cached variant keeps the row's z and p in registers between
 // the statistics and the write, so HBM sees one read of z and p and one write of z (the
 // minimum); the streaming variant (vocabularies too long to hold) reads the row twice.  The
-// cached variant is held to 128 registers so that two rows (16 waves) share a CU: one row's
-// reductions and exponentials overlap the other's memory traffic.
+// cached variant is held to 128 registers (bf16 rows up to 32768 columns, fp32 up to 16384) so that
+// two rows (16 waves) share a CU: one row's reductions and exponentials overlap the other's
+// memory traffic; longer rows get 256 registers and one row per CU.
 #include "launch.h"
 
 namespace ttt {
@@ -92,7 +93,7 @@ __device__ __forceinline__ RowStats finish_row(float m, float sum_e, float sum_p
 
 // NV vectors of 8 elements per thread stay in registers (V <= LT * 8 * NV).
 template <typename T, int NV>
-__global__ __launch_bounds__(LT, 4) void loss_grad_cached_kernel(T* __restrict__ z,
+__global__ __launch_bounds__(LT, NV * sizeof(T) <= 16 ? 4 : 2) void loss_grad_cached_kernel(T* __restrict__ z,
                                                               const T* __restrict__ p,
                                                               const float* __restrict__ g,
                                                               float* __restrict__ loss, int V) {
