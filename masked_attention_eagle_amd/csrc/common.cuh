@@ -303,13 +303,21 @@ __device__ __forceinline__ bf16x8 frag_col(const bf16* tile, int c, int u, const
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Splits a grid of units * ranks workgroups into (unit, rank).  A unit is an
-// independent slice of work (a head, a KV group); rank 0 is its heaviest piece.  The
-// dispatcher deals workgroups to the 8 XCDs round robin, so when units % 8 == 0 each
-// XCD is given a contiguous range of units (their shared K/V stay in that XCD's L2)
-// and every XCD starts on its heaviest ranks.
-__device__ __forceinline__ void map_block(int bid, int units, int& unit, int& rank) {
-  if (units % 8 == 0) {
+// Splits a grid of units * ranks workgroups into (unit, rank).  A unit is an independent
+// slice of work (a head, a KV group share); rank 0 is its heaviest piece.  Units come in
+// groups of `per_group` that read the same K/V (the heads or head splits of one KV group).
+// The dispatcher deals workgroups to the 8 XCDs round robin, so when the number of groups is
+// a multiple of 8 each XCD is given every 8th group: a group's K/V stay in one XCD's L2, and
+// every XCD gets groups of every sequence, so sequences of different lengths load the XCDs
+// evenly.  Every XCD starts on its heaviest ranks.
+__device__ __forceinline__ void map_block(int bid, int units, int per_group, int& unit, int& rank) {
+  const int groups = units / per_group;
+  if (groups % 8 == 0) {
+    const int x = bid % 8, slot = bid / 8, ux = units / 8;
+    rank = slot / ux;
+    const int k = slot % ux;  // unit index within XCD x
+    unit = (x + 8 * (k / per_group)) * per_group + k % per_group;
+  } else if (units % 8 == 0) {
     const int x = bid % 8, slot = bid / 8, ux = units / 8;
     rank = slot / ux;
     unit = x * ux + slot % ux;

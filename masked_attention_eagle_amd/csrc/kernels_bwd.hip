@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
 
   const int nkt = s.L / KBN;
   int unit, pair;
-  map_block(blockIdx.x, s.B * s.Hkv * nsplit, unit, pair);
+  map_block(blockIdx.x, s.B * s.Hkv * nsplit, nsplit, unit, pair);
   const int split = unit % nsplit, bg = unit / nsplit;
   const int b = bg / s.Hkv;
   const int T = clamp_T(seq_T, b, s.L);
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
 
   const int n_qt = s.L / QBM;
   int bh, rank;
-  map_block(blockIdx.x, s.B * s.Hq, bh, rank);
+  map_block(blockIdx.x, s.B * s.Hq, s.G, bh, rank);
   const int qtile = n_qt - 1 - rank;
   const int b = bh / s.Hq, h = bh % s.Hq, g = h / s.G;
   const int bg = b * s.Hkv + g;

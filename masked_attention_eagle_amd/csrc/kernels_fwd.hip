@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
 
   const int n_qt = s.L / FBM;
   int bh, rank;
-  map_block(blockIdx.x, s.B * s.Hq, bh, rank);
+  map_block(blockIdx.x, s.B * s.Hq, s.G, bh, rank);
   const int qt = n_qt - 1 - rank;  // the last query tile sees the most keys: run it first
   const int b = bh / s.Hq, h = bh % s.Hq, g = h / s.G;
   const int T = clamp_T(seq_T, b, s.L);
