@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload number (2: the 8B draft layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--dq-mode", choices=("stored", "recompute"), default="stored",
+                    help="backward workspace: full (dS handed to the dQ kernel) or minimum "
+                         "(the dQ kernel recomputes S and dP)")
     ap.add_argument("--loss", action="store_true",
                     help="measure the in-place masked softmax-loss gradient on the draft LM head "
                          "of one TTT step (N = 8192 tokens, V = 32000, bf16) instead")
@@ -149,7 +152,8 @@ def main():
     dks = [torch.empty_like(kv[i][0]) for i in range(K)]
     dvs = [torch.empty_like(kv[i][1]) for i in range(K)]
     params = [A.make_params(w.B, w.Hq, w.Hkv, w.L, w.d, k, w.scale, A.TTT_DTYPE_BF16) for k in steps]
-    ws_bytes = max(max(A.fwd_workspace_size(p), A.bwd_workspace_size(p)) for p in params)
+    bwd_ws = A.bwd_workspace_size if args.dq_mode == "stored" else A.bwd_workspace_size_min
+    ws_bytes = max(max(A.fwd_workspace_size(p), bwd_ws(p)) for p in params)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
@@ -207,7 +211,7 @@ def main():
     # algorithmic matrix-core flops per launch of each causal kernel: dK/dV kernel does the
     # S, dP, dV and dK products (8d per pair), dQ kernel the dQ product (2d), forward 4d.
     alg = {"bwd_dkdv_mfma": 8 * w.d * causal, "bwd_dq_mfma": 2 * w.d * causal,
-           "fwd_causal_mfma": 4 * w.d * causal}
+           "bwd_dq_ds": 2 * w.d * causal, "fwd_causal_mfma": 4 * w.d * causal}
     roofline = None
     if kstats:
         mfma = {n: s for n, s in kstats.items() if n in alg}
@@ -232,6 +236,16 @@ def main():
                          rows_q * (w.d * 2 + 4) for k in kk])
             gbs = b / (kstats["fwd_suffix"]["avg_ms"] / 1e3) / 1e9
             kstats["fwd_suffix"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+        if "bwd_dq_ds" in kstats:
+            # stored-dS dQ kernel (HBM-bound): the 2 KB dS blocks it reads (key block kb <= query
+            # block qb, 32 kb < T), K of block 0 once per KV group, dQ written (fp32 accumulator
+            # for k >= 1, bf16 at k = 0), averaged over the steps
+            L32 = w.L // 32
+            blocks = w.Hq * sum(min(qb + 1, -(-int(t) // 32)) for t in T for qb in range(L32))
+            b = np.mean([blocks * 2048 + w.B * w.Hkv * w.L * w.d * 2 + rows_q * w.d * (4 if k else 2)
+                         for k in steps])
+            gbs = b / (kstats["bwd_dq_ds"]["avg_ms"] / 1e3) / 1e9
+            kstats["bwd_dq_ds"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
         if kk and "bwd_suffix" in kstats:
             b = np.mean([2 * live_q * w.d * 2 + 2 * live_q * 4 + rows_q * w.d * 4 + rows_q * w.d * 2 +
                          live_kv * k * 2 * w.d * 2 + w.B * w.Hkv * k * w.L * 2 * w.d * 2 for k in kk])
@@ -247,6 +261,7 @@ def main():
                    "T": [int(t) for t in T] if w.T_fixed is None else w.T_fixed,
                    "ttt_steps": f"k=0..{steps[-1]}", "global_batch": w.B, "seq_len": w.L,
                    "parallelism": "single GPU"},
+        "dq_mode": args.dq_mode,
         "tokens_per_s": round(tokens, 1),
         "unmasked_flop_per_step": flops,
         "roofline": roofline,

@@ -83,6 +83,17 @@ size_t ttt_attn_fwd_workspace_size(const ttt_attn_params* p);
 size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p);
 
 /*
+ * Smallest workspace ttt_attn_bwd accepts (0 when the params are invalid).  For bf16 the
+ * full size of ttt_attn_bwd_workspace_size adds room for the dS tiles of block 0
+ * (B * Hq * n(n+1)/2 blocks of 2 KB, n = Q_LEN / 32; 1.08 GB at B 2, Hq 32, Q_LEN 4096):
+ * the dK/dV kernel stores dS there and dQ = scale * dS K costs one matrix product per tile.
+ * Given at least this minimum but less than the full size, ttt_attn_bwd recomputes S and
+ * dP in the dQ kernel instead.  Both give the same gradients up to rounding; dk/dv are
+ * bitwise the same.  For f32 both sizes are equal.
+ */
+size_t ttt_attn_bwd_workspace_size_min(const ttt_attn_params* p);
+
+/*
  * Forward: o = softmax_M(scale * q k^T) v and lse = log sum_{j in M} exp(scale * q.k_j).
  * Streaming softmax (the review's §3 "Sparse Tree Attention": computed flash-style so the
  * logits are never stored): the causal block 0 runs as tiled MFMA with fully masked

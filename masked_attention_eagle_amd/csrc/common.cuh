@@ -159,6 +159,25 @@ __device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
                                    (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
 }
 
+// 16-byte load from global memory at base + off (base wave-uniform, off per lane), kept a
+// global_load for the same reason as the store below.
+__device__ __forceinline__ bf16x8 load16_global(const void* base, unsigned off) {
+  typedef const __attribute__((address_space(1))) char gchar;
+  typedef const __attribute__((address_space(1))) bf16x8 gvec;
+  return *(gvec*)((gchar*)base + off);
+}
+
+// 16-byte streaming store to global memory at base + off (base wave-uniform, off per lane).
+// The explicit global address space keeps it a global_store: a flat store could alias LDS,
+// and the compiler would first wait for every copy into LDS still in flight.  The
+// non-temporal hint keeps data that is read back only by a later kernel from displacing
+// the caller's working set in the caches.
+__device__ __forceinline__ void store16_global_nt(void* base, unsigned off, const bf16x8& v) {
+  typedef __attribute__((address_space(1))) char gchar;
+  typedef __attribute__((address_space(1))) bf16x8 gvec;
+  __builtin_nontemporal_store(v, (gvec*)((gchar*)base + off));
+}
+
 // Wait until this wave's outstanding vector-memory operations (incl. global -> LDS copies)
 // have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
@@ -197,8 +216,10 @@ __device__ __forceinline__ void load_tile(const bf16* g, int ld, bf16* lds, int 
   // Scalar base + 32-bit per-lane byte offset: the copies use the saddr form and hold no
   // 64-bit per-lane addresses in vector registers.
   const char* base = reinterpret_cast<const char*>(uniform_ptr(g));
+  static_assert((NROWS / 4) % NWAVES == 0, "whole 4-row groups per wave");
 #pragma unroll
-  for (int i = wave; i < NROWS / 4; i += NWAVES) {
+  for (int r = 0; r < NROWS / 4 / NWAVES; ++r) {  // a fixed count: no branches per copy
+    const int i = wave + r * NWAVES;
     unsigned off = 2u * ((unsigned)(4 * i * ld) + lane_off);
     asm volatile("" : "+v"(off));  // keeps the 32-bit offset form (no 64-bit copies to hold)
     g2lds16(base + off, lds + i * 512);

@@ -135,9 +135,11 @@ FwdLayout fwd_layout(const Shape& s, int /*dtype*/) {
 }
 
 struct BwdLayout {
-  size_t Dd = 0, dqacc = 0, part = 0, total = 0;
+  size_t Dd = 0, dqacc = 0, part = 0, ds = 0, total = 0, total_min = 0;
   int nsplit = 1;
 };
+// `total_min` covers the recomputing dQ kernel; `total` adds the dS blocks (bf16 path) that
+// let the dQ kernel run one product per tile instead of three.
 BwdLayout bwd_layout(const Shape& s, int dtype) {
   BwdLayout w;
   size_t off = 0;
@@ -154,6 +156,12 @@ BwdLayout bwd_layout(const Shape& s, int dtype) {
       w.part = off;
       off += round_up((size_t)w.nsplit * 2 * s.B * s.Hkv * s.L * s.D * 4);
     }
+  }
+  w.total_min = off;
+  if (dtype == TTT_DTYPE_BF16) {
+    const size_t n = s.L / 32;
+    w.ds = off;
+    off += round_up((size_t)s.B * s.Hq * (n * (n + 1) / 2) * 32 * 32 * 2);
   }
   w.total = off;
   return w;
@@ -191,6 +199,11 @@ size_t ttt_attn_fwd_workspace_size(const ttt_attn_params* p) {
 size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p) {
   if (validate(p) != TTT_OK) return 0;
   return bwd_layout(make_shape(p), p->dtype).total;
+}
+
+size_t ttt_attn_bwd_workspace_size_min(const ttt_attn_params* p) {
+  if (validate(p) != TTT_OK) return 0;
+  return bwd_layout(make_shape(p), p->dtype).total_min;
 }
 
 int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
@@ -243,8 +256,9 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
   if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
   const Shape s = make_shape(p);
   const BwdLayout w = bwd_layout(s, p->dtype);
-  if (w.total > 0 && !workspace) return TTT_E_NULL;
-  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
+  if (w.total_min > 0 && !workspace) return TTT_E_NULL;
+  if (workspace_bytes < w.total_min) return TTT_E_WORKSPACE;
+  const bool stored_ds = workspace_bytes >= w.total && w.total > w.total_min;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || !aligned16(workspace))
@@ -261,16 +275,20 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
     const bf16* vb = (const bf16*)v;
     const bf16* dob = (const bf16*)dout;
     float* part = w.nsplit > 1 ? (float*)(ws + w.part) : nullptr;
+    bf16* dsb = stored_ds ? (bf16*)(ws + w.ds) : nullptr;
+    void* dq_causal = final_causal ? dq : (void*)dqacc;
     if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, st)) != hipSuccess) return TTT_E_HIP;
     if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
-                                  w.nsplit, st)) != hipSuccess)
+                                  w.nsplit, dsb, st)) != hipSuccess)
       return TTT_E_HIP;
     if (w.nsplit > 1 &&
         (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
       return TTT_E_HIP;
-    if ((e = launch_bwd_dq_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T,
-                                final_causal ? dq : (void*)dqacc, final_causal, st)) != hipSuccess)
-      return TTT_E_HIP;
+    if (stored_ds)
+      e = launch_bwd_dq_ds(s, kb, dsb, seq_T, dq_causal, final_causal, st);
+    else
+      e = launch_bwd_dq_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T, dq_causal, final_causal, st);
+    if (e != hipSuccess) return TTT_E_HIP;
     if (!final_causal)
       e = launch_bwd_suffix<bf16>(s, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq, (bf16*)dk,
                                   (bf16*)dv, st);

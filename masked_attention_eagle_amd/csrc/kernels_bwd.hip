@@ -30,6 +30,34 @@ constexpr int BD = 128;  // head dim of the matrix-core path
 constexpr int KBN = 128;  // keys per tile
 constexpr int KBM = 32;   // queries per tile
 
+// dS hand-over between the dK/dV kernel and the dQ kernel.  dS of one head is kept in
+// 32 x 32 blocks (32 query rows x 32 keys of block 0); only blocks on or below the diagonal
+// exist, packed row after row (query block r holds key blocks 0..r).
+__device__ __forceinline__ size_t ds_block_index(const Shape& s, int bh, int qb, int kb) {
+  const int n = s.L / 32;
+  return (size_t)bh * ((size_t)n * (n + 1) / 2) + (size_t)qb * (qb + 1) / 2 + kb;
+}
+// Inside a 2 KB block, the dK/dV lane holding key l32 and query rows acc_row(0..15, hi) has
+// its 16 values as 4-row pieces (8 bytes) in accumulator order; pieces 0-1 go to the first
+// KB and pieces 2-3 to the second, each as a 16-byte chunk at slot 2*l32 + hi (slot bit 3
+// flipped in the second KB).  Each of the two stores then fills one KB contiguously, and
+// the transposing reads below touch every LDS bank once per half wave.
+__device__ __forceinline__ unsigned ds_store_offset(int lane, int half) {
+  const int slot = 2 * (lane & 31) + (lane >> 5);
+  return (unsigned)(1024 * half + 16 * (slot ^ (8 * half)));
+}
+// Byte offset for lds_tr4 that gives lane (query n = lane % 32, half h) keys
+// 16c + 8r + 4h .. +3 of its row: in each 16-lane group, lane s addresses the piece of key
+// 16c + 8r + 4h + s/4 that holds queries 16(group % 2) + 4(s % 4) .. +3, i.e. piece
+// 2(group % 2) + (s % 4)/2 of the writer lane of that key in half (s % 4) % 2.
+__device__ __forceinline__ unsigned ds_read_offset(int lane, int c, int r) {
+  const int s16 = lane & 15, a = s16 & 3, j = s16 >> 2;
+  const int h = lane >> 5, qh = (lane >> 4) & 1;
+  const int key = 16 * c + 8 * r + 4 * h + j;
+  const int slot = 2 * key + (a & 1);
+  return (unsigned)(1024 * qh + 16 * (slot ^ (8 * qh)) + 8 * (a >> 1));
+}
+
 // Key tile kt is seen by every query row >= 128 * kt (padded rows see every key < T), so the
 // work of tile kt falls linearly with kt.  A workgroup takes the complementary pair
 // (p, n - 1 - p) of key tiles, which makes every workgroup's work equal.
@@ -37,7 +65,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, bf16* __restrict__ dk, bf16* __restrict__ dv,
-    float* __restrict__ part, int nsplit, Shape s) {
+    float* __restrict__ part, int nsplit, bf16* __restrict__ ds_out, Shape s) {
   // Two stages in distinct arrays (the copy into one never stalls reads of the other).
   __shared__ __attribute__((aligned(1024))) bf16 sQ0[KBM * BD];
   __shared__ __attribute__((aligned(1024))) bf16 sO0[KBM * BD];
@@ -143,6 +171,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
             dsb[i >> 3][i & 7] = (bf16)((float)pb[i >> 3][i & 7] * (acc[i] - D4[e]));
           }
         }
+        if (ds_out) {  // hand dS to the dQ kernel (layout: ds_store_offset)
+          const int h = h_begin + it / nq;
+          const size_t blk = ds_block_index(s, b * s.Hq + h, q0 / 32, kw / 32);
+          void* dst = const_cast<void*>(uniform_ptr(ds_out + blk * 1024));
+          unsigned off0 = ds_store_offset(lane, 0), off1 = ds_store_offset(lane, 1);
+          asm volatile("" : "+v"(off0), "+v"(off1));
+          store16_global_nt(dst, off0, dsb[0]);
+          store16_global_nt(dst, off1, dsb[1]);
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -207,10 +244,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
-                                int nsplit, hipStream_t st) {
+                                int nsplit, bf16* ds_out, hipStream_t st) {
   const dim3 grid(s.B * s.Hkv * nsplit * ((s.L / KBN + 1) / 2));
   LaunchTimer timer("bwd_dkdv_mfma", st);
-  bwd_dkdv_mfma_kernel<<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dk, dv, part, nsplit, s);
+  bwd_dkdv_mfma_kernel<<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dk, dv, part, nsplit,
+                                             ds_out, s);
   return hipGetLastError();
 }
 
@@ -386,6 +424,161 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, cons
     bwd_dq_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
   else
     bwd_dq_mfma_kernel<false><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------
+// dQ of block 0 from the dS blocks the dK/dV kernel stored: dQ = scale dS K, one product per
+// tile instead of three.  Workgroup = 4 waves x 32 queries of one head, 64-key tiles.
+//   dQ^T += K^T dS^T    (A = K columns through transposing LDS reads, B = dS^T through
+//                        transposing reads of the stored 4-query pieces)
+// The kernel streams dS from HBM once, so it is bound by how many bytes are in flight: K tiles
+// go global -> LDS through three stages and each wave's dS (4 KB per tile) through two
+// register sets, both two tiles ahead; the wave copies its dS into a private LDS slot right
+// before reading it transposed.  Every tile issues the same 8 loads per wave (indices past the
+// end are clamped to a valid tile), so "the loads of the tile after next may still be in
+// flight" is the constant wait vmcnt(8).
+// Only blocks the wave's rows can see enter the products: key block kb <= the wave's query
+// block and 32 kb < T; masked entries inside them were stored as zero.
+// ----------------------------------------------------------------------------------------
+template <bool FINAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const bf16* __restrict__ k,
+                                                           const bf16* __restrict__ ds,
+                                                           const int32_t* __restrict__ seq_T,
+                                                           void* __restrict__ dq_out, Shape s) {
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[QBN * BD];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[QBN * BD];
+  __shared__ __attribute__((aligned(1024))) bf16 sK2[QBN * BD];
+  __shared__ __attribute__((aligned(1024))) bf16 sS[4 * 2048];  // per wave: 2 blocks of a tile
+
+  const int n_qt = s.L / QBM;
+  int bh, rank;
+  map_block(blockIdx.x, s.B * s.Hq, s.G, bh, rank);
+  const int qtile = n_qt - 1 - rank;
+  const int b = bh / s.Hq, h = bh % s.Hq, g = h / s.G;
+  const int bg = b * s.Hkv + g;
+  const int T = clamp_T(seq_T, b, s.L);
+  const int q0 = qtile * QBM;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, hi = lane >> 5;
+  const int qb = (q0 >> 5) + wave;             // this wave's query block
+  const int nkb = min(qb + 1, (T + 31) >> 5);  // key blocks it reads
+  const char* srow = reinterpret_cast<const char*>(ds + ds_block_index(s, bh, qb, 0) * 1024);
+  const FragOffsets fo = make_frag_offsets(lane);
+  const unsigned rd0 = ds_read_offset(lane, 0, 0);
+  char* mine = reinterpret_cast<char*>(sS + wave * 2048);
+
+  const bf16* kb = k + (size_t)bg * s.KV * BD;
+  const int kv_end = min(q0 + QBM, T);
+  const int ntiles = (kv_end + QBN - 1) / QBN;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
+
+  auto issue_k = [&](int j, bf16* dst) {
+    load_tile<QBN, 4>(kb + (size_t)min(j, ntiles - 1) * QBN * BD, BD, dst, wave, lane);
+  };
+  // 4 KB of this wave's dS for tile j: blocks 2j and 2j + 1, 1 KB per load.
+  auto load_ds = [&](int j, bf16x8 (&r)[4]) {
+    unsigned off = 16u * lane;
+    asm volatile("" : "+v"(off));
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int blk = max(min(2 * j + (x >> 1), nkb - 1), 0);
+      r[x] = load16_global(uniform_ptr(srow + (size_t)blk * 2048 + (x & 1) * 1024), off);
+    }
+  };
+
+  auto body = [&](int j, const bf16* cK, bf16* nK, bf16x8 (&r)[4]) {
+    const FragOffsets fl = opaque(fo);
+    unsigned rd = rd0, wr = 16u * lane;
+    asm volatile("" : "+v"(rd), "+v"(wr));
+#pragma unroll
+    for (int x = 0; x < 4; ++x) *reinterpret_cast<bf16x8*>(mine + x * 1024 + wr) = r[x];
+    issue_k(j + 2, nK);
+    load_ds(j + 2, r);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      if (2 * j + cc < nkb) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const char* blk = mine + cc * 2048 + 512 * c2;
+          const bf16x4 x0 = lds_tr4(blk + rd);
+          const bf16x4 x1 = lds_tr4(blk + 256 + rd);
+          const bf16x8 bop = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] = mfma32(frag_col(cK, 2 * cc + c2, u, fl), bop, acc[u]);
+        }
+      }
+    }
+    wait_vmem_n<8>();  // tile j + 1 has landed; tile j + 2 may still be in flight
+    asm volatile("s_barrier" ::: "memory");
+  };
+
+  if (ntiles > 0) {
+    bf16x8 ra[4], rb[4];
+    issue_k(0, sK0);
+    load_ds(0, ra);
+    issue_k(1, sK1);
+    load_ds(1, rb);
+    wait_vmem_n<8>();
+    asm volatile("s_barrier" ::: "memory");
+    // Six tiles per trip (3 K stages x 2 register sets); the early exits keep the loop's
+    // back edge after the sixth tile only.
+    for (int j = 0;; j += 6) {
+      body(j, sK0, sK2, ra);
+      if (j + 1 >= ntiles) break;
+      body(j + 1, sK1, sK0, rb);
+      if (j + 2 >= ntiles) break;
+      body(j + 2, sK2, sK1, ra);
+      if (j + 3 >= ntiles) break;
+      body(j + 3, sK0, sK2, rb);
+      if (j + 4 >= ntiles) break;
+      body(j + 4, sK1, sK0, ra);
+      if (j + 5 >= ntiles) break;
+      body(j + 5, sK2, sK1, rb);
+      if (j + 6 >= ntiles) break;
+    }
+    wait_vmem();  // nothing stays in flight past the loop
+  }
+
+  // lane owns dQ[query][32u + 8*b4 + 4*hi + e] in acc[u][4*b4 + e]
+  const size_t row = (size_t)bh * s.L + q0 + 32 * wave + (lane & 31);
+  if constexpr (FINAL) {
+    bf16* orow = reinterpret_cast<bf16*>(dq_out) + row * BD + 4 * hi;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[u][4 * b4 + e] * s.scale);
+        *reinterpret_cast<bf16x4*>(orow + 32 * u + 8 * b4) = w;
+      }
+    }
+  } else {
+    float* orow = reinterpret_cast<float*>(dq_out) + row * BD + 4 * hi;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[u][4 * b4 + e] * s.scale;
+        *reinterpret_cast<f32x4*>(orow + 32 * u + 8 * b4) = w;
+      }
+    }
+  }
+}
+
+hipError_t launch_bwd_dq_ds(const Shape& s, const bf16* k, const bf16* ds, const int32_t* seq_T,
+                            void* dq, bool final_out, hipStream_t st) {
+  const dim3 grid(s.B * s.Hq * (s.L / QBM));
+  LaunchTimer timer("bwd_dq_ds", st);
+  if (final_out)
+    bwd_dq_ds_kernel<true><<<grid, 256, 0, st>>>(k, ds, seq_T, dq, s);
+  else
+    bwd_dq_ds_kernel<false><<<grid, 256, 0, st>>>(k, ds, seq_T, dq, s);
   return hipGetLastError();
 }
 

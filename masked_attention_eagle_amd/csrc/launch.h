@@ -36,12 +36,14 @@ hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* D
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
-                                int nsplit, hipStream_t st);
+                                int nsplit, bf16* ds_out, hipStream_t st);
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
                                   bf16* dv, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                               const bf16* dout, const float* lse, const float* Dd,
                               const int32_t* seq_T, void* dq, bool final_out, hipStream_t st);
+hipError_t launch_bwd_dq_ds(const Shape& s, const bf16* k, const bf16* ds, const int32_t* seq_T,
+                            void* dq, bool final_out, hipStream_t st);
 template <typename T>
 hipError_t launch_bwd_dkdv_valu(const Shape& s, const T* q, const T* k, const T* v,
                                 const T* dout, const float* lse, const float* Dd,

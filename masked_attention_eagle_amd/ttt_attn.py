@@ -25,7 +25,8 @@ STATUS = {
 
 # Every symbol the header declares.
 EXPORTS = (
-    "ttt_attn_fwd_workspace_size", "ttt_attn_bwd_workspace_size", "ttt_attn_fwd", "ttt_attn_bwd",
+    "ttt_attn_fwd_workspace_size", "ttt_attn_bwd_workspace_size",
+    "ttt_attn_bwd_workspace_size_min", "ttt_attn_fwd", "ttt_attn_bwd",
     "ttt_attn_status_string", "ttt_attn_version", "ttt_attn_timing_enable",
     "ttt_attn_timing_read", "ttt_attn_timing_reset",
 )
@@ -71,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.ttt_attn_fwd_workspace_size.restype = sz
     lib.ttt_attn_bwd_workspace_size.argtypes = [P]
     lib.ttt_attn_bwd_workspace_size.restype = sz
+    lib.ttt_attn_bwd_workspace_size_min.argtypes = [P]
+    lib.ttt_attn_bwd_workspace_size_min.restype = sz
     lib.ttt_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ttt_attn_fwd.restype = ctypes.c_int
     lib.ttt_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -148,6 +151,10 @@ def bwd_workspace_size(p: Params) -> int:
     return int(load().ttt_attn_bwd_workspace_size(ctypes.byref(p)))
 
 
+def bwd_workspace_size_min(p: Params) -> int:
+    return int(load().ttt_attn_bwd_workspace_size_min(ctypes.byref(p)))
+
+
 def _workspace(nbytes: int, device):
     import torch
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
@@ -181,8 +188,13 @@ def ttt_attn_fwd(q, k, v, seq_T, scale: Optional[float] = None, out=None, lse=No
 
 
 def ttt_attn_bwd(q, k, v, seq_T, o, lse, dout, scale: Optional[float] = None, dq=None, dk=None,
-                 dv=None, workspace=None):
-    """dq, dk, dv: gradients of sum(dout * o) for the o/lse of ttt_attn_fwd."""
+                 dv=None, workspace=None, dq_mode: str = "stored"):
+    """dq, dk, dv: gradients of sum(dout * o) for the o/lse of ttt_attn_fwd.
+
+    dq_mode "stored" gives the library its full workspace (the dK/dV kernel hands dS to the
+    dQ kernel); "recompute" gives it the minimum (the dQ kernel recomputes S and dP).  An
+    explicit ``workspace`` overrides both.
+    """
     import torch
     lib = load()
     p = _params_from(q, k, scale)
@@ -199,7 +211,9 @@ def ttt_attn_bwd(q, k, v, seq_T, o, lse, dout, scale: Optional[float] = None, dq
     _require(dq, "dq", q.dtype, q.shape)
     _require(dk, "dk", q.dtype, k.shape)
     _require(dv, "dv", q.dtype, k.shape)
-    need = bwd_workspace_size(p)
+    if dq_mode not in ("stored", "recompute"):
+        raise ValueError(f"dq_mode must be 'stored' or 'recompute', not {dq_mode!r}")
+    need = bwd_workspace_size(p) if dq_mode == "stored" else bwd_workspace_size_min(p)
     ws = _workspace(need, q.device) if workspace is None else workspace
     _check(lib.ttt_attn_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             seq_T.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),

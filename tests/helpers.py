@@ -27,7 +27,7 @@ def to_np(t):
     return t.detach().to(dtype=torch.float64).cpu().numpy()
 
 
-def gpu_fwd_bwd(lib, q, k, v, do, T, scale, dtype_name, with_bwd=True):
+def gpu_fwd_bwd(lib, q, k, v, do, T, scale, dtype_name, with_bwd=True, dq_mode="stored"):
     import torch
     dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
     qd, kd, vd, dod = (to_dev(x, dt) for x in (q, k, v, do))
@@ -35,7 +35,7 @@ def gpu_fwd_bwd(lib, q, k, v, do, T, scale, dtype_name, with_bwd=True):
     o, lse = lib.ttt_attn_fwd(qd, kd, vd, Td, scale)
     out = {"o": to_np(o), "lse": to_np(lse)}
     if with_bwd:
-        dq, dk, dv = lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, scale)
+        dq, dk, dv = lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, scale, dq_mode=dq_mode)
         out.update(dq=to_np(dq), dk=to_np(dk), dv=to_np(dv))
     torch.cuda.synchronize()
     return out

@@ -77,15 +77,27 @@ def test_workspace_sizes():
     # of the dK/dV kernel owns a pair of 128-key tiles, so 2 x 8 x 16 = 256 workgroups double
     # to 512 by splitting each KV group's 4 query heads in two.
     part = 2 * 2 * B * Hkv * L * d * 4
-    assert A.bwd_workspace_size(p) == rows * 4 + rows * d * 4 + part
-    assert A.bwd_workspace_size(P(step=0)) == rows * 4 + part
+    assert A.bwd_workspace_size_min(p) == rows * 4 + rows * d * 4 + part
+    assert A.bwd_workspace_size_min(P(step=0)) == rows * 4 + part
+    # the full size adds the bf16 dS blocks of block 0: n(n+1)/2 blocks of 32 x 32 per head,
+    # n = L / 32 (every offset above is a multiple of 256, so no padding)
+    def ds_bytes(B, Hq, L):
+        n = L // 32
+        return B * Hq * n * (n + 1) // 2 * 32 * 32 * 2
+    assert A.bwd_workspace_size(p) == A.bwd_workspace_size_min(p) + ds_bytes(B, Hq, L)
+    assert A.bwd_workspace_size(P(step=0)) == rows * 4 + part + ds_bytes(B, Hq, L)
     # 1 x 8 x 16 = 128 pair workgroups: heads split in four
     rows4 = 64 * L
-    assert A.bwd_workspace_size(P(B=1, Hq=64)) == rows4 * 4 + rows4 * d * 4 + 4 * 2 * 8 * L * d * 4
+    assert A.bwd_workspace_size_min(P(B=1, Hq=64)) == rows4 * 4 + rows4 * d * 4 + 4 * 2 * 8 * L * d * 4
     # 8 x 8 x 8 = 512 already: no split, no partials
     rows3 = 8 * 32 * 2048
-    assert A.bwd_workspace_size(P(B=8, L=2048)) == rows3 * 4 + rows3 * d * 4
+    assert A.bwd_workspace_size_min(P(B=8, L=2048)) == rows3 * 4 + rows3 * d * 4
+    assert A.bwd_workspace_size(P(B=8, L=2048)) == rows3 * 4 + rows3 * d * 4 + ds_bytes(8, 32, 2048)
+    # fp32 (vector-ALU path): no dS blocks, both sizes equal
+    pf = P(dtype=A.TTT_DTYPE_F32, L=4000)
+    assert A.bwd_workspace_size(pf) == A.bwd_workspace_size_min(pf) > 0
     assert A.fwd_workspace_size(P(Hq=30)) == 0  # invalid params -> 0
+    assert A.bwd_workspace_size_min(P(Hq=30)) == 0
 
 
 @pytest.mark.parametrize("kw,code", [

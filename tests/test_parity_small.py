@@ -11,11 +11,13 @@ from tests.helpers import check, gpu_fwd_bwd
 pytestmark = pytest.mark.gpu
 
 
-def run_case(lib, seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult=1.0, T_oracle=None, o_tol=1e-2):
+def run_case(lib, seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult=1.0, T_oracle=None, o_tol=1e-2,
+             dq_mode="stored"):
     q, k, v, do, Tarr = inputs.make_case(seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult)
     scale = 1.0 / np.sqrt(d)
-    print(f"case seed={seed} B={B} Hq={Hq} Hkv={Hkv} d={d} L={L} step={step} T={list(Tarr)} {dtype}", flush=True)
-    got = gpu_fwd_bwd(lib, q, k, v, do, Tarr, scale, dtype)
+    print(f"case seed={seed} B={B} Hq={Hq} Hkv={Hkv} d={d} L={L} step={step} T={list(Tarr)} {dtype} "
+          f"dq={dq_mode}", flush=True)
+    got = gpu_fwd_bwd(lib, q, k, v, do, Tarr, scale, dtype, dq_mode=dq_mode)
     To = Tarr if T_oracle is None else T_oracle
     o, lse = O.forward(q, k, v, To, scale)
     dq, dk, dv = O.backward(q, k, v, To, scale, do, o)
@@ -46,15 +48,36 @@ def test_fp32_edge_cases(gpu_lib, step, T, d, L):
 
 
 # ------------------------------------------------------------------ bf16 matrix-core path
+# dq_mode "stored": the dK/dV kernel hands dS to the dQ kernel (full workspace);
+# "recompute": the dQ kernel recomputes S and dP (minimum workspace).
+@pytest.mark.parametrize("dq_mode", ["stored", "recompute"])
 @pytest.mark.parametrize("step", [0, 1, 2, 3])
 @pytest.mark.parametrize("T", [(256, 256), (0, 256), (1, 255), (63, 64), (65, 127), (128, 129), (200, 17)])
-def test_bf16_tile_edges(gpu_lib, step, T):
-    run_case(gpu_lib, 7 + step, 2, 4, 2, 128, 256, step, T, "bf16")
+def test_bf16_tile_edges(gpu_lib, step, T, dq_mode):
+    run_case(gpu_lib, 7 + step, 2, 4, 2, 128, 256, step, T, "bf16", dq_mode=dq_mode)
 
 
+@pytest.mark.parametrize("dq_mode", ["stored", "recompute"])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2), (8, 2), (16, 2), (8, 1)])
-def test_bf16_gqa_groups(gpu_lib, Hq, Hkv):
-    run_case(gpu_lib, 20 + Hq, 2, Hq, Hkv, 128, 384, 2, (384, 300), "bf16")
+def test_bf16_gqa_groups(gpu_lib, Hq, Hkv, dq_mode):
+    run_case(gpu_lib, 20 + Hq, 2, Hq, Hkv, 128, 384, 2, (384, 300), "bf16", dq_mode=dq_mode)
+
+
+def test_bf16_dq_modes_agree(gpu_lib):
+    """Both dQ kernels see the same dK/dV kernel: dk, dv bitwise equal; dq equal up to the
+    rounding of dS (the stored one rounds P to bf16 before the product with dP - D)."""
+    import torch
+    from tests.helpers import to_dev
+    q, k, v, do, T = inputs.make_case(52, 2, 8, 2, 128, 640, 2, (640, 411), "bf16")
+    qd, kd, vd, dod = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+    Td = torch.as_tensor(T, device="cuda")
+    o, lse = gpu_lib.ttt_attn_fwd(qd, kd, vd, Td)
+    a = gpu_lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, dq_mode="stored")
+    b = gpu_lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, dq_mode="recompute")
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+    assert torch.equal(a[2].view(torch.int16), b[2].view(torch.int16))
+    den = float(b[0].float().abs().max())
+    assert float((a[0].float() - b[0].float()).abs().max()) <= 1e-2 * den
 
 
 def test_bf16_peaky_logits(gpu_lib):
