@@ -489,12 +489,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const bf16* __restric
     }
   };
 
-  auto body = [&](int j, const bf16* cK, bf16* nK, bf16x8 (&r)[4]) {
-    const FragOffsets fl = opaque(fo);
-    unsigned rd = rd0, wr = 16u * lane;
-    asm volatile("" : "+v"(rd), "+v"(wr));
+  auto put_ds = [&](const bf16x8 (&r)[4]) {  // this wave's dS of one tile into its LDS slot
+    unsigned wr = 16u * lane;
+    asm volatile("" : "+v"(wr));
 #pragma unroll
     for (int x = 0; x < 4; ++x) *reinterpret_cast<bf16x8*>(mine + x * 1024 + wr) = r[x];
+  };
+
+  // Tile j: its dS is already in the LDS slot and `r` (which held it) takes tile j + 2;
+  // `rn` holds tile j + 1 and goes to the slot once this tile's reads are issued (LDS
+  // operations of one wave complete in order).
+  auto body = [&](int j, const bf16* cK, bf16* nK, bf16x8 (&r)[4], const bf16x8 (&rn)[4]) {
+    const FragOffsets fl = opaque(fo);
+    unsigned rd = rd0;
+    asm volatile("" : "+v"(rd));
     issue_k(j + 2, nK);
     load_ds(j + 2, r);
 #pragma unroll
@@ -512,6 +520,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const bf16* __restric
       }
     }
     wait_vmem_n<8>();  // tile j + 1 has landed; tile j + 2 may still be in flight
+    put_ds(rn);
     asm volatile("s_barrier" ::: "memory");
   };
 
@@ -522,21 +531,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const bf16* __restric
     issue_k(1, sK1);
     load_ds(1, rb);
     wait_vmem_n<8>();
+    put_ds(ra);
     asm volatile("s_barrier" ::: "memory");
     // Six tiles per trip (3 K stages x 2 register sets); the early exits keep the loop's
     // back edge after the sixth tile only.
     for (int j = 0;; j += 6) {
-      body(j, sK0, sK2, ra);
+      body(j, sK0, sK2, ra, rb);
       if (j + 1 >= ntiles) break;
-      body(j + 1, sK1, sK0, rb);
+      body(j + 1, sK1, sK0, rb, ra);
       if (j + 2 >= ntiles) break;
-      body(j + 2, sK2, sK1, ra);
+      body(j + 2, sK2, sK1, ra, rb);
       if (j + 3 >= ntiles) break;
-      body(j + 3, sK0, sK2, rb);
+      body(j + 3, sK0, sK2, rb, ra);
       if (j + 4 >= ntiles) break;
-      body(j + 4, sK1, sK0, ra);
+      body(j + 4, sK1, sK0, ra, rb);
       if (j + 5 >= ntiles) break;
-      body(j + 5, sK2, sK1, rb);
+      body(j + 5, sK2, sK1, rb, ra);
       if (j + 6 >= ntiles) break;
     }
     wait_vmem();  // nothing stays in flight past the loop
