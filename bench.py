@@ -80,9 +80,12 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload number (2: the 8B draft layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--suffix", choices=("fused", "separate"), default="fused",
+                    help="forward: diagonal keys merged inside the causal kernel, or the standalone "
+                         "suffix kernel")
     ap.add_argument("--dq-mode", choices=("stored", "recompute"), default="stored",
-                    help="backward workspace: full (dS handed to the dQ kernel) or minimum "
-                         "(the dQ kernel recomputes S and dP)")
+                    help="dS handed from the dK/dV kernel to the dQ kernel through the workspace, "
+                         "or recomputed in the dQ kernel")
     ap.add_argument("--loss", action="store_true",
                     help="measure the in-place masked softmax-loss gradient on the draft LM head "
                          "of one TTT step (N = 8192 tokens, V = 32000, bf16) instead")
@@ -151,9 +154,9 @@ def main():
     dqs = [torch.empty_like(q) for q in qs]
     dks = [torch.empty_like(kv[i][0]) for i in range(K)]
     dvs = [torch.empty_like(kv[i][1]) for i in range(K)]
-    params = [A.make_params(w.B, w.Hq, w.Hkv, w.L, w.d, k, w.scale, A.TTT_DTYPE_BF16) for k in steps]
-    bwd_ws = A.bwd_workspace_size if args.dq_mode == "stored" else A.bwd_workspace_size_min
-    ws_bytes = max(max(A.fwd_workspace_size(p), bwd_ws(p)) for p in params)
+    params = [A.make_params(w.B, w.Hq, w.Hkv, w.L, w.d, k, w.scale, A.TTT_DTYPE_BF16,
+                            A.path_flags(args.suffix, args.dq_mode)) for k in steps]
+    ws_bytes = max(max(A.fwd_workspace_size(p), A.bwd_workspace_size(p)) for p in params)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
@@ -247,6 +250,8 @@ def main():
             gbs = b / (kstats["bwd_dq_ds"]["avg_ms"] / 1e3) / 1e9
             kstats["bwd_dq_ds"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
         if kk and "bwd_suffix" in kstats:
+            # q, dO, lse, D of the live rows, the fp32 dQ accumulator read and dq written, the
+            # diagonal K/V rows read and all dK/dV rows of blocks 1..k written
             b = np.mean([2 * live_q * w.d * 2 + 2 * live_q * 4 + rows_q * w.d * 4 + rows_q * w.d * 2 +
                          live_kv * k * 2 * w.d * 2 + w.B * w.Hkv * k * w.L * 2 * w.d * 2 for k in kk])
             gbs = b / (kstats["bwd_suffix"]["avg_ms"] / 1e3) / 1e9
@@ -261,7 +266,7 @@ def main():
                    "T": [int(t) for t in T] if w.T_fixed is None else w.T_fixed,
                    "ttt_steps": f"k=0..{steps[-1]}", "global_batch": w.B, "seq_len": w.L,
                    "parallelism": "single GPU"},
-        "dq_mode": args.dq_mode,
+        "dq_mode": args.dq_mode, "suffix": args.suffix,
         "tokens_per_s": round(tokens, 1),
         "unmasked_flop_per_step": flops,
         "roofline": roofline,

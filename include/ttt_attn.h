@@ -50,6 +50,25 @@ enum ttt_attn_dtype {
   TTT_DTYPE_BF16 = 1  /* bf16 tensors, bf16 MFMA with fp32 accumulation; lse in fp32 */
 };
 
+/*
+ * Path selection (ttt_attn_params.flags; bf16 only, the fp32 path ignores them).  All paths
+ * give the same result up to rounding.  0 = default:
+ *   - forward: the diagonal keys of blocks 1..k are merged inside the causal kernel, which
+ *     writes the final o and lse (no fp32 intermediate state);
+ *   - backward: the dK/dV kernel stores dS of block 0 (bf16, in the workspace) and the dQ
+ *     kernel computes dQ = scale * dS K from it, one matrix product per tile.
+ * TTT_FLAG_SEPARATE_SUFFIX: the forward's causal kernel writes an fp32 state (o_c, lse_c)
+ *   that the standalone bandwidth-bound suffix kernel merges (the fp32 path always does so).
+ * TTT_FLAG_RECOMPUTE_DQ: no stored dS (a much smaller backward workspace); the dQ kernel
+ *   recomputes S and dP, three products per tile.  dk/dv are bitwise the same either way.
+ * In the backward the suffix kernel always adds the diagonal keys' terms for k > 0.  The
+ * workspace sizes below depend on the flags.
+ */
+enum ttt_attn_flags {
+  TTT_FLAG_SEPARATE_SUFFIX = 1,
+  TTT_FLAG_RECOMPUTE_DQ = 2
+};
+
 enum ttt_attn_status {
   TTT_OK = 0,
   TTT_E_NULL = -1,        /* a required pointer is NULL                              */
@@ -76,6 +95,7 @@ typedef struct ttt_attn_params {
   int32_t ttt_step;  /* k >= 0; the KV length is (k+1)*Q_LEN */
   float scale;
   int32_t dtype;     /* enum ttt_attn_dtype                */
+  int32_t flags;     /* enum ttt_attn_flags; unknown bits -> TTT_E_UNSUPPORTED */
 } ttt_attn_params;
 
 /* Bytes of device workspace the call needs (0 when the params are invalid). */
@@ -83,15 +103,9 @@ size_t ttt_attn_fwd_workspace_size(const ttt_attn_params* p);
 size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p);
 
 /*
- * Smallest workspace ttt_attn_bwd accepts (0 when the params are invalid).  For bf16 the
- * full size of ttt_attn_bwd_workspace_size adds room for the dS tiles of block 0
- * (B * Hq * n(n+1)/2 blocks of 2 KB, n = Q_LEN / 32; 1.08 GB at B 2, Hq 32, Q_LEN 4096):
- * the dK/dV kernel stores dS there and dQ = scale * dS K costs one matrix product per tile.
- * Given at least this minimum but less than the full size, ttt_attn_bwd recomputes S and
- * dP in the dQ kernel instead.  Both give the same gradients up to rounding; dk/dv are
- * bitwise the same.  For f32 both sizes are equal.
+ * The default bf16 backward workspace holds the dS of block 0: B * Hq * n(n+1)/2 blocks of
+ * 2 KB, n = Q_LEN / 32 (1.08 GB at B 2, Hq 32, Q_LEN 4096); TTT_FLAG_RECOMPUTE_DQ avoids it.
  */
-size_t ttt_attn_bwd_workspace_size_min(const ttt_attn_params* p);
 
 /*
  * Forward: o = softmax_M(scale * q k^T) v and lse = log sum_{j in M} exp(scale * q.k_j).

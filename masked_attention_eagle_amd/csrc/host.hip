@@ -87,7 +87,18 @@ int validate(const ttt_attn_params* p) {
   } else {
     return TTT_E_UNSUPPORTED;
   }
+  if (p->flags & ~(TTT_FLAG_SEPARATE_SUFFIX | TTT_FLAG_RECOMPUTE_DQ)) return TTT_E_UNSUPPORTED;
   return TTT_OK;
+}
+
+// bf16 backward: the dQ kernel reads dS stored by the dK/dV kernel unless asked to recompute.
+bool stored_ds(const ttt_attn_params* p) {
+  return p->dtype == TTT_DTYPE_BF16 && !(p->flags & TTT_FLAG_RECOMPUTE_DQ);
+}
+// The forward merges the suffix inside the causal kernel unless asked for the separate
+// suffix kernel; the fp32 path always runs it.
+bool fused_fwd(const ttt_attn_params* p) {
+  return p->dtype == TTT_DTYPE_BF16 && !(p->flags & TTT_FLAG_SEPARATE_SUFFIX);
 }
 
 Shape make_shape(const ttt_attn_params* p) {
@@ -120,11 +131,11 @@ int dkdv_nsplit(const Shape& s) {
 struct FwdLayout {
   size_t oc = 0, lsec = 0, total = 0;
 };
-FwdLayout fwd_layout(const Shape& s, int /*dtype*/) {
+FwdLayout fwd_layout(const Shape& s, bool fused) {
   FwdLayout w;
   size_t off = 0;
   const size_t rows_q = (size_t)s.B * s.Hq * s.L;
-  if (s.step > 0) {
+  if (s.step > 0 && !fused) {
     w.oc = off;
     off += round_up(rows_q * s.D * 4);
     w.lsec = off;
@@ -135,21 +146,18 @@ FwdLayout fwd_layout(const Shape& s, int /*dtype*/) {
 }
 
 struct BwdLayout {
-  size_t Dd = 0, dqacc = 0, part = 0, ds = 0, total = 0, total_min = 0;
+  size_t Dd = 0, part = 0, ds = 0, dqacc = 0, total = 0;
   int nsplit = 1;
 };
-// `total_min` covers the recomputing dQ kernel; `total` adds the dS blocks (bf16 path) that
-// let the dQ kernel run one product per tile instead of three.
-BwdLayout bwd_layout(const Shape& s, int dtype) {
+// D; split dK/dV partials (bf16, heads of a group over several workgroups); the dS blocks of
+// block 0 when the dQ kernel reads them; for k > 0 the fp32 dQ accumulator that the suffix
+// kernel finalises.
+BwdLayout bwd_layout(const Shape& s, int dtype, bool with_ds) {
   BwdLayout w;
-  size_t off = 0;
   const size_t rows_q = (size_t)s.B * s.Hq * s.L;
+  size_t off = 0;
   w.Dd = off;
   off += round_up(rows_q * 4);
-  if (s.step > 0) {
-    w.dqacc = off;
-    off += round_up(rows_q * s.D * 4);
-  }
   if (dtype == TTT_DTYPE_BF16) {
     w.nsplit = dkdv_nsplit(s);
     if (w.nsplit > 1) {
@@ -157,11 +165,14 @@ BwdLayout bwd_layout(const Shape& s, int dtype) {
       off += round_up((size_t)w.nsplit * 2 * s.B * s.Hkv * s.L * s.D * 4);
     }
   }
-  w.total_min = off;
-  if (dtype == TTT_DTYPE_BF16) {
+  if (with_ds) {
     const size_t n = s.L / 32;
     w.ds = off;
     off += round_up((size_t)s.B * s.Hq * (n * (n + 1) / 2) * 32 * 32 * 2);
+  }
+  if (s.step > 0) {
+    w.dqacc = off;
+    off += round_up(rows_q * s.D * 4);
   }
   w.total = off;
   return w;
@@ -176,14 +187,14 @@ using namespace ttt;
 
 extern "C" {
 
-int ttt_attn_version(void) { return 100; }
+int ttt_attn_version(void) { return 101; }
 
 const char* ttt_attn_status_string(int status) {
   switch (status) {
     case TTT_OK: return "ok";
     case TTT_E_NULL: return "null pointer argument";
     case TTT_E_SHAPE: return "invalid shape (non-positive size, heads_q % heads_kv != 0, ttt_step < 0, scale not finite and positive, or size overflow)";
-    case TTT_E_UNSUPPORTED: return "unsupported configuration (f32: head_dim 64 or 128; bf16: head_dim 128 and q_len % 128 == 0)";
+    case TTT_E_UNSUPPORTED: return "unsupported configuration (f32: head_dim 64 or 128; bf16: head_dim 128 and q_len % 128 == 0; unknown flags)";
     case TTT_E_ALIGN: return "pointer not 16-byte aligned";
     case TTT_E_WORKSPACE: return "workspace smaller than required";
     case TTT_E_HIP: return "HIP kernel launch failed";
@@ -193,17 +204,12 @@ const char* ttt_attn_status_string(int status) {
 
 size_t ttt_attn_fwd_workspace_size(const ttt_attn_params* p) {
   if (validate(p) != TTT_OK) return 0;
-  return fwd_layout(make_shape(p), p->dtype).total;
+  return fwd_layout(make_shape(p), fused_fwd(p)).total;
 }
 
 size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p) {
   if (validate(p) != TTT_OK) return 0;
-  return bwd_layout(make_shape(p), p->dtype).total;
-}
-
-size_t ttt_attn_bwd_workspace_size_min(const ttt_attn_params* p) {
-  if (validate(p) != TTT_OK) return 0;
-  return bwd_layout(make_shape(p), p->dtype).total_min;
+  return bwd_layout(make_shape(p), p->dtype, stored_ds(p)).total;
 }
 
 int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
@@ -213,7 +219,8 @@ int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const v
   if (rc != TTT_OK) return rc;
   if (!q || !k || !v || !seq_T || !o || !lse) return TTT_E_NULL;
   const Shape s = make_shape(p);
-  const FwdLayout w = fwd_layout(s, p->dtype);
+  const bool fused = fused_fwd(p);
+  const FwdLayout w = fwd_layout(s, fused);
   if (w.total > 0 && !workspace) return TTT_E_NULL;
   if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
@@ -221,7 +228,7 @@ int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const v
     return TTT_E_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  const bool final_causal = s.step == 0;
+  const bool final_causal = s.step == 0 || fused;
   float* oc = final_causal ? nullptr : (float*)(ws + w.oc);
   float* lsec = final_causal ? lse : (float*)(ws + w.lsec);
   hipError_t e;
@@ -229,6 +236,7 @@ int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const v
     const bf16* qb = (const bf16*)q;
     const bf16* kb = (const bf16*)k;
     const bf16* vb = (const bf16*)v;
+    // final_causal with k > 0: the kernel merges the suffix keys itself
     e = launch_fwd_causal_mfma(s, qb, kb, vb, seq_T, final_causal ? o : (void*)oc, lsec,
                                final_causal, st);
     if (e != hipSuccess) return TTT_E_HIP;
@@ -255,10 +263,10 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
   if (rc != TTT_OK) return rc;
   if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
   const Shape s = make_shape(p);
-  const BwdLayout w = bwd_layout(s, p->dtype);
-  if (w.total_min > 0 && !workspace) return TTT_E_NULL;
-  if (workspace_bytes < w.total_min) return TTT_E_WORKSPACE;
-  const bool stored_ds = workspace_bytes >= w.total && w.total > w.total_min;
+  const bool with_ds = stored_ds(p);
+  const BwdLayout w = bwd_layout(s, p->dtype, with_ds);
+  if (w.total > 0 && !workspace) return TTT_E_NULL;
+  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || !aligned16(workspace))
@@ -275,7 +283,7 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
     const bf16* vb = (const bf16*)v;
     const bf16* dob = (const bf16*)dout;
     float* part = w.nsplit > 1 ? (float*)(ws + w.part) : nullptr;
-    bf16* dsb = stored_ds ? (bf16*)(ws + w.ds) : nullptr;
+    bf16* dsb = with_ds ? (bf16*)(ws + w.ds) : nullptr;
     void* dq_causal = final_causal ? dq : (void*)dqacc;
     if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, st)) != hipSuccess) return TTT_E_HIP;
     if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
@@ -284,7 +292,7 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
     if (w.nsplit > 1 &&
         (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
       return TTT_E_HIP;
-    if (stored_ds)
+    if (with_ds)
       e = launch_bwd_dq_ds(s, kb, dsb, seq_T, dq_causal, final_causal, st);
     else
       e = launch_bwd_dq_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T, dq_causal, final_causal, st);

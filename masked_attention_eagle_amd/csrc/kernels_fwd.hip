@@ -22,6 +22,9 @@ namespace ttt {
 // straddle the diagonal or the T edge evaluate the mask ("partial"); the rest are "full".
 // On partial tiles P is split into bf16 hi + lo parts so that rows with few keys (where one
 // rounding of P would show in O) keep fp32-level accuracy.
+// With FINAL and k > 0 the kernel also merges the suffix keys (one per block 1..k for rows
+// i < T) and writes the final o and lse; without FINAL it writes the fp32 causal state for
+// the standalone suffix kernel.
 //
 // K and V tiles are copied global -> LDS without passing through registers (two stages),
 // which keeps the wave under 256 registers: two workgroups share a CU and the matrix cores
@@ -174,6 +177,44 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
   };
 
   if (ntiles > 0) issue(0, sK0, sV0);
+  if (FINAL && s.step > 0 && my_q < T) {
+    // Suffix keys t*Q_LEN + my_q (t = 1..k), merged before the causal tiles (the softmax
+    // state is order-independent) while tile 0 is in flight.  Each lane takes the same half
+    // of the K row as of q (d = 16c + 8*hi ..) and the same half of the V row as of O
+    // (d = 32u + 8*b4 + 4*hi ..); the logit is the sum over the lane pair.  P stays fp32.
+    const bf16* kr = kb + (size_t)my_q * FD + 8 * hi;
+    const bf16* vr = vb + (size_t)my_q * FD + 4 * hi;
+    for (int t = 1; t <= s.step; ++t) {
+      const size_t off = (size_t)t * s.L * FD;
+      bf16x8 kk[8];
+      bf16x4 vv[16];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) kk[c] = *reinterpret_cast<const bf16x8*>(kr + off + 16 * c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4)
+          vv[4 * u + b4] = *reinterpret_cast<const bf16x4*>(vr + off + 32 * u + 8 * b4);
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = __builtin_fmaf((float)qf[c][e], (float)kk[c][e], dot);
+      dot = half_sum(dot);
+      const float m_new = fmaxf(m, dot);
+      const float alpha = exp2_fast((m - m_new) * c2);  // 0 while m = -inf
+      const float p = exp2_fast((dot - m_new) * c2);
+      l = l * alpha + p;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[u][4 * b4 + e] = __builtin_fmaf(acc[u][4 * b4 + e], alpha, p * (float)vv[4 * u + b4][e]);
+      m = m_new;
+    }
+  }
   wait_vmem();
   __syncthreads();
   for (int j = 0; j < ntiles; j += 2) {

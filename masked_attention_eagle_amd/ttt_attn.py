@@ -17,6 +17,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttt_attn
 
 TTT_DTYPE_F32 = 0
 TTT_DTYPE_BF16 = 1
+TTT_FLAG_SEPARATE_SUFFIX = 1
+TTT_FLAG_RECOMPUTE_DQ = 2
+SUFFIX_PATHS = {"fused": 0, "separate": TTT_FLAG_SEPARATE_SUFFIX}
+DQ_MODES = {"stored": 0, "recompute": TTT_FLAG_RECOMPUTE_DQ}
 
 STATUS = {
     0: "TTT_OK", -1: "TTT_E_NULL", -2: "TTT_E_SHAPE", -3: "TTT_E_UNSUPPORTED",
@@ -25,8 +29,7 @@ STATUS = {
 
 # Every symbol the header declares.
 EXPORTS = (
-    "ttt_attn_fwd_workspace_size", "ttt_attn_bwd_workspace_size",
-    "ttt_attn_bwd_workspace_size_min", "ttt_attn_fwd", "ttt_attn_bwd",
+    "ttt_attn_fwd_workspace_size", "ttt_attn_bwd_workspace_size", "ttt_attn_fwd", "ttt_attn_bwd",
     "ttt_attn_status_string", "ttt_attn_version", "ttt_attn_timing_enable",
     "ttt_attn_timing_read", "ttt_attn_timing_reset",
 )
@@ -43,7 +46,7 @@ class Params(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
         ("q_len", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ttt_step", ctypes.c_int32),
-        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
     ]
 
 
@@ -72,8 +75,6 @@ def load() -> ctypes.CDLL:
     lib.ttt_attn_fwd_workspace_size.restype = sz
     lib.ttt_attn_bwd_workspace_size.argtypes = [P]
     lib.ttt_attn_bwd_workspace_size.restype = sz
-    lib.ttt_attn_bwd_workspace_size_min.argtypes = [P]
-    lib.ttt_attn_bwd_workspace_size_min.restype = sz
     lib.ttt_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ttt_attn_fwd.restype = ctypes.c_int
     lib.ttt_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -103,8 +104,19 @@ def _check(code: int) -> None:
         raise TTTError(code, status_string(code))
 
 
-def make_params(B: int, Hq: int, Hkv: int, L: int, d: int, step: int, scale: float, dtype: int) -> Params:
-    return Params(B, Hq, Hkv, L, d, step, float(scale), dtype)
+def make_params(B: int, Hq: int, Hkv: int, L: int, d: int, step: int, scale: float, dtype: int,
+                flags: int = 0) -> Params:
+    return Params(B, Hq, Hkv, L, d, step, float(scale), dtype, flags)
+
+
+def path_flags(suffix: str = "fused", dq_mode: str = "stored") -> int:
+    """ttt_attn_params.flags for a forward suffix path ("fused" | "separate") and a backward
+    dQ mode ("stored": dS handed from the dK/dV kernel to the dQ kernel | "recompute")."""
+    if suffix not in SUFFIX_PATHS:
+        raise ValueError(f"suffix must be one of {sorted(SUFFIX_PATHS)}, not {suffix!r}")
+    if dq_mode not in DQ_MODES:
+        raise ValueError(f"dq_mode must be one of {sorted(DQ_MODES)}, not {dq_mode!r}")
+    return SUFFIX_PATHS[suffix] | DQ_MODES[dq_mode]
 
 
 def _dtype_code(t) -> int:
@@ -116,14 +128,14 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
-def _params_from(q, k, scale) -> Params:
+def _params_from(q, k, scale, flags: int = 0) -> Params:
     B, Hq, L, d = q.shape
     Bk, Hkv, KV, dk = k.shape
     if Bk != B or dk != d or KV % L != 0:
         raise ValueError(f"k shape {tuple(k.shape)} does not match q shape {tuple(q.shape)}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    return make_params(B, Hq, Hkv, L, d, KV // L - 1, scale, _dtype_code(q))
+    return make_params(B, Hq, Hkv, L, d, KV // L - 1, scale, _dtype_code(q), flags)
 
 
 def _require(t, name, dtype=None, shape=None):
@@ -151,24 +163,22 @@ def bwd_workspace_size(p: Params) -> int:
     return int(load().ttt_attn_bwd_workspace_size(ctypes.byref(p)))
 
 
-def bwd_workspace_size_min(p: Params) -> int:
-    return int(load().ttt_attn_bwd_workspace_size_min(ctypes.byref(p)))
-
-
 def _workspace(nbytes: int, device):
     import torch
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
 def ttt_attn_fwd(q, k, v, seq_T, scale: Optional[float] = None, out=None, lse=None,
-                 workspace=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+                 workspace=None, suffix: str = "fused") -> Tuple["torch.Tensor", "torch.Tensor"]:
     """o, lse = masked attention of q [B,Hq,L,d] over k, v [B,Hkv,(step+1)L,d].
 
-    seq_T: int32 [B] on the GPU.  The TTT step is k.shape[2] // L - 1.
+    seq_T: int32 [B] on the GPU.  The TTT step is k.shape[2] // L - 1.  suffix "fused"
+    merges the diagonal keys of blocks 1..k inside the causal kernel (bf16); "separate" runs
+    the standalone suffix kernel on an fp32 causal state.
     """
     import torch
     lib = load()
-    p = _params_from(q, k, scale)
+    p = _params_from(q, k, scale, path_flags(suffix))
     _require(q, "q")
     _require(k, "k", q.dtype)
     _require(v, "v", q.dtype, k.shape)
@@ -191,13 +201,13 @@ def ttt_attn_bwd(q, k, v, seq_T, o, lse, dout, scale: Optional[float] = None, dq
                  dv=None, workspace=None, dq_mode: str = "stored"):
     """dq, dk, dv: gradients of sum(dout * o) for the o/lse of ttt_attn_fwd.
 
-    dq_mode "stored" gives the library its full workspace (the dK/dV kernel hands dS to the
-    dQ kernel); "recompute" gives it the minimum (the dQ kernel recomputes S and dP).  An
-    explicit ``workspace`` overrides both.
+    dq_mode "stored": the dK/dV kernel hands dS of block 0 to the dQ kernel through the
+    workspace (one matrix product per tile there); "recompute": a small workspace, and the dQ
+    kernel recomputes S and dP.
     """
     import torch
     lib = load()
-    p = _params_from(q, k, scale)
+    p = _params_from(q, k, scale, path_flags("fused", dq_mode))
     _require(q, "q")
     _require(k, "k", q.dtype)
     _require(v, "v", q.dtype, k.shape)
@@ -211,9 +221,7 @@ def ttt_attn_bwd(q, k, v, seq_T, o, lse, dout, scale: Optional[float] = None, dq
     _require(dq, "dq", q.dtype, q.shape)
     _require(dk, "dk", q.dtype, k.shape)
     _require(dv, "dv", q.dtype, k.shape)
-    if dq_mode not in ("stored", "recompute"):
-        raise ValueError(f"dq_mode must be 'stored' or 'recompute', not {dq_mode!r}")
-    need = bwd_workspace_size(p) if dq_mode == "stored" else bwd_workspace_size_min(p)
+    need = bwd_workspace_size(p)
     ws = _workspace(need, q.device) if workspace is None else workspace
     _check(lib.ttt_attn_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             seq_T.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),

@@ -27,12 +27,13 @@ def to_np(t):
     return t.detach().to(dtype=torch.float64).cpu().numpy()
 
 
-def gpu_fwd_bwd(lib, q, k, v, do, T, scale, dtype_name, with_bwd=True, dq_mode="stored"):
+def gpu_fwd_bwd(lib, q, k, v, do, T, scale, dtype_name, with_bwd=True, dq_mode="stored",
+                suffix="fused"):
     import torch
     dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
     qd, kd, vd, dod = (to_dev(x, dt) for x in (q, k, v, do))
     Td = torch.as_tensor(np.asarray(T, dtype=np.int32), device="cuda")
-    o, lse = lib.ttt_attn_fwd(qd, kd, vd, Td, scale)
+    o, lse = lib.ttt_attn_fwd(qd, kd, vd, Td, scale, suffix=suffix)
     out = {"o": to_np(o), "lse": to_np(lse)}
     if with_bwd:
         dq, dk, dv = lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, scale, dq_mode=dq_mode)

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(A.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.ttt_attn_version() == 100
+    assert lib.ttt_attn_version() == 101
     loss_declared = header_functions("ttt_loss.h", "ttt_loss_")
     assert set(loss_declared) == set(A.LOSS_EXPORTS)
     for name in loss_declared:
@@ -59,45 +59,57 @@ def test_status_strings():
 
 
 def P(**kw):
-    base = dict(B=2, Hq=32, Hkv=8, L=4096, d=128, step=3, scale=0.088, dtype=A.TTT_DTYPE_BF16)
+    base = dict(B=2, Hq=32, Hkv=8, L=4096, d=128, step=3, scale=0.088, dtype=A.TTT_DTYPE_BF16,
+                flags=0)
     base.update(kw)
     return A.make_params(base["B"], base["Hq"], base["Hkv"], base["L"], base["d"], base["step"],
-                         base["scale"], base["dtype"])
+                         base["scale"], base["dtype"], base["flags"])
 
 
 def test_workspace_sizes():
     p = P()
     B, Hq, Hkv, L, d = 2, 32, 8, 4096, 128
     rows = B * Hq * L
-    # fp32 causal state (o_c, lse_c) for step > 0; nothing at step 0
-    assert A.fwd_workspace_size(p) == rows * d * 4 + rows * 4
-    assert A.fwd_workspace_size(P(step=0)) == 0
+    # forward: nothing on the fused path; with the separate suffix kernel (and always for
+    # fp32) the fp32 causal state (o_c, lse_c) for step > 0
+    sep = A.TTT_FLAG_SEPARATE_SUFFIX
+    assert A.fwd_workspace_size(p) == 0
+    assert A.fwd_workspace_size(P(flags=sep)) == rows * d * 4 + rows * 4
+    assert A.fwd_workspace_size(P(flags=sep, step=0)) == 0
     assert A.fwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, step=0)) == 0
+    assert A.fwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, L=4000)) == 2 * 32 * 4000 * (d * 4 + 4)
     # D rows + fp32 dQ accumulator for step > 0 + fp32 dK/dV partial planes: each workgroup
     # of the dK/dV kernel owns a pair of 128-key tiles, so 2 x 8 x 16 = 256 workgroups double
     # to 512 by splitting each KV group's 4 query heads in two.
     part = 2 * 2 * B * Hkv * L * d * 4
-    assert A.bwd_workspace_size_min(p) == rows * 4 + rows * d * 4 + part
-    assert A.bwd_workspace_size_min(P(step=0)) == rows * 4 + part
-    # the full size adds the bf16 dS blocks of block 0: n(n+1)/2 blocks of 32 x 32 per head,
-    # n = L / 32 (every offset above is a multiple of 256, so no padding)
+    dqacc = rows * d * 4
+    # bf16 default: dS blocks of block 0 (n(n+1)/2 blocks of 32 x 32 per head, n = L / 32)
+    # and, for step > 0, the fp32 dQ accumulator the suffix kernel finalises; every offset is
+    # a multiple of 256, so no padding.  The forward's suffix path does not change it.
     def ds_bytes(B, Hq, L):
         n = L // 32
         return B * Hq * n * (n + 1) // 2 * 32 * 32 * 2
-    assert A.bwd_workspace_size(p) == A.bwd_workspace_size_min(p) + ds_bytes(B, Hq, L)
+    sep, rec = A.TTT_FLAG_SEPARATE_SUFFIX, A.TTT_FLAG_RECOMPUTE_DQ
+    assert A.bwd_workspace_size(p) == rows * 4 + part + ds_bytes(B, Hq, L) + dqacc
+    assert A.bwd_workspace_size(P(flags=sep)) == A.bwd_workspace_size(p)
     assert A.bwd_workspace_size(P(step=0)) == rows * 4 + part + ds_bytes(B, Hq, L)
+    # recomputing dQ kernel: no dS blocks
+    assert A.bwd_workspace_size(P(flags=rec)) == rows * 4 + part + dqacc
+    assert A.bwd_workspace_size(P(flags=rec | sep)) == rows * 4 + part + dqacc
+    assert A.bwd_workspace_size(P(flags=rec, step=0)) == rows * 4 + part
     # 1 x 8 x 16 = 128 pair workgroups: heads split in four
     rows4 = 64 * L
-    assert A.bwd_workspace_size_min(P(B=1, Hq=64)) == rows4 * 4 + rows4 * d * 4 + 4 * 2 * 8 * L * d * 4
+    assert A.bwd_workspace_size(P(B=1, Hq=64, flags=rec)) == rows4 * 4 + rows4 * d * 4 + 4 * 2 * 8 * L * d * 4
     # 8 x 8 x 8 = 512 already: no split, no partials
     rows3 = 8 * 32 * 2048
-    assert A.bwd_workspace_size_min(P(B=8, L=2048)) == rows3 * 4 + rows3 * d * 4
-    assert A.bwd_workspace_size(P(B=8, L=2048)) == rows3 * 4 + rows3 * d * 4 + ds_bytes(8, 32, 2048)
-    # fp32 (vector-ALU path): no dS blocks, both sizes equal
-    pf = P(dtype=A.TTT_DTYPE_F32, L=4000)
-    assert A.bwd_workspace_size(pf) == A.bwd_workspace_size_min(pf) > 0
+    assert A.bwd_workspace_size(P(B=8, L=2048, flags=rec)) == rows3 * 4 + rows3 * d * 4
+    assert A.bwd_workspace_size(P(B=8, L=2048)) == rows3 * 4 + ds_bytes(8, 32, 2048) + rows3 * d * 4
+    # fp32 (vector-ALU path): flags ignored; D + dQ accumulator
+    rowsf = 2 * 32 * 4000
+    for f in (0, sep, rec):
+        assert A.bwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, L=4000, flags=f)) == rowsf * 4 + rowsf * d * 4
     assert A.fwd_workspace_size(P(Hq=30)) == 0  # invalid params -> 0
-    assert A.bwd_workspace_size_min(P(Hq=30)) == 0
+    assert A.bwd_workspace_size(P(Hq=30)) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -106,6 +118,7 @@ def test_workspace_sizes():
     (dict(scale=-0.088), -2),
     (dict(d=64), -3), (dict(L=4000), -3), (dict(dtype=7), -3),
     (dict(dtype=A.TTT_DTYPE_F32, d=96), -3), (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10), -2),
+    (dict(flags=4), -3), (dict(flags=-1), -3),
 ])
 def test_validation_errors(kw, code):
     lib = A.load()
@@ -118,8 +131,10 @@ def test_validation_errors(kw, code):
 
 
 def test_null_align_workspace_errors():
+    # every call below must fail validation before anything is launched: the separate-suffix
+    # forward needs a workspace at step 3, so a null or short one is an error
     lib = A.load()
-    p = P()
+    p = P(flags=A.TTT_FLAG_SEPARATE_SUFFIX)
     good = ctypes.c_void_p(1 << 20)
     odd = ctypes.c_void_p((1 << 20) + 8)
     assert lib.ttt_attn_fwd(None, good, good, good, good, good, good, good, 1 << 40, None) == -1

@@ -21,7 +21,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 CASES = [(2, 0), (2, 6), (3, 0), (3, 6), (4, 6), (5, 3), (5, 12)]
 
 
-def _run(lib, w, step, dq_mode="stored"):
+def _run(lib, w, step, dq_mode="stored", suffix="fused"):
     import torch
     q = inputs.q_at(w, step)
     k, v = inputs.kv_stack(w, step)
@@ -29,21 +29,23 @@ def _run(lib, w, step, dq_mode="stored"):
     T = inputs.seq_lengths(w)
     qd, kd, vd, dod = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
     Td = torch.as_tensor(T, device="cuda")
-    o, lse = lib.ttt_attn_fwd(qd, kd, vd, Td, w.scale)
+    o, lse = lib.ttt_attn_fwd(qd, kd, vd, Td, w.scale, suffix=suffix)
     dq, dk, dv = lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, w.scale, dq_mode=dq_mode)
     torch.cuda.synchronize()
     return (q, k, v, do, T), (qd, kd, vd, dod, Td), (o, lse, dq, dk, dv)
 
 
-# The default backward hands dS from the dK/dV kernel to the dQ kernel; the last two cases
-# run the minimum-workspace backward, whose dQ kernel recomputes S and dP.
-@pytest.mark.parametrize("cfg,step,dq_mode", [c + ("stored",) for c in CASES] +
-                         [(2, 6, "recompute"), (3, 6, "recompute")])
-def test_workload_sampled_group_and_properties(gpu_lib, cfg, step, dq_mode):
+# The default path merges the suffix inside the causal forward kernel and hands dS from the
+# dK/dV kernel to the dQ kernel; the extra cases run the backward whose dQ kernel recomputes
+# S and dP (small workspace) and the forward's standalone suffix kernel.
+@pytest.mark.parametrize("cfg,step,dq_mode,suffix", [c + ("stored", "fused") for c in CASES] +
+                         [(2, 6, "recompute", "fused"), (3, 6, "recompute", "fused"),
+                          (2, 6, "stored", "separate"), (5, 12, "stored", "separate")])
+def test_workload_sampled_group_and_properties(gpu_lib, cfg, step, dq_mode, suffix):
     import torch
     w = inputs.WORKLOADS[cfg]
-    print(f"workload {w.name} step {step} dq {dq_mode}", flush=True)
-    (q, k, v, do, T), dev, (o, lse, dq, dk, dv) = _run(gpu_lib, w, step, dq_mode)
+    print(f"workload {w.name} step {step} dq {dq_mode} suffix {suffix}", flush=True)
+    (q, k, v, do, T), dev, (o, lse, dq, dk, dv) = _run(gpu_lib, w, step, dq_mode, suffix)
     G, L = w.Hq // w.Hkv, w.L
 
     # properties over every KV group (fp64 on the GPU)

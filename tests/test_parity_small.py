@@ -12,12 +12,12 @@ pytestmark = pytest.mark.gpu
 
 
 def run_case(lib, seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult=1.0, T_oracle=None, o_tol=1e-2,
-             dq_mode="stored"):
+             dq_mode="stored", suffix="fused"):
     q, k, v, do, Tarr = inputs.make_case(seed, B, Hq, Hkv, d, L, step, T, dtype, q_mult)
     scale = 1.0 / np.sqrt(d)
     print(f"case seed={seed} B={B} Hq={Hq} Hkv={Hkv} d={d} L={L} step={step} T={list(Tarr)} {dtype} "
-          f"dq={dq_mode}", flush=True)
-    got = gpu_fwd_bwd(lib, q, k, v, do, Tarr, scale, dtype, dq_mode=dq_mode)
+          f"dq={dq_mode} suffix={suffix}", flush=True)
+    got = gpu_fwd_bwd(lib, q, k, v, do, Tarr, scale, dtype, dq_mode=dq_mode, suffix=suffix)
     To = Tarr if T_oracle is None else T_oracle
     o, lse = O.forward(q, k, v, To, scale)
     dq, dk, dv = O.backward(q, k, v, To, scale, do, o)
@@ -48,19 +48,46 @@ def test_fp32_edge_cases(gpu_lib, step, T, d, L):
 
 
 # ------------------------------------------------------------------ bf16 matrix-core path
-# dq_mode "stored": the dK/dV kernel hands dS to the dQ kernel (full workspace);
-# "recompute": the dQ kernel recomputes S and dP (minimum workspace).
-@pytest.mark.parametrize("dq_mode", ["stored", "recompute"])
+# Paths of the bf16 library: dq_mode "stored" (the dK/dV kernel hands dS to the dQ kernel
+# through the workspace) or "recompute" (the dQ kernel recomputes S and dP); suffix "fused"
+# (diagonal keys merged inside the causal forward kernel) or "separate" (the forward's
+# standalone suffix kernel on an fp32 state).
+PATHS = [("stored", "fused"), ("recompute", "fused"), ("stored", "separate")]
+
+
+@pytest.mark.parametrize("dq_mode,suffix", PATHS)
 @pytest.mark.parametrize("step", [0, 1, 2, 3])
 @pytest.mark.parametrize("T", [(256, 256), (0, 256), (1, 255), (63, 64), (65, 127), (128, 129), (200, 17)])
-def test_bf16_tile_edges(gpu_lib, step, T, dq_mode):
-    run_case(gpu_lib, 7 + step, 2, 4, 2, 128, 256, step, T, "bf16", dq_mode=dq_mode)
+def test_bf16_tile_edges(gpu_lib, step, T, dq_mode, suffix):
+    run_case(gpu_lib, 7 + step, 2, 4, 2, 128, 256, step, T, "bf16", dq_mode=dq_mode, suffix=suffix)
 
 
-@pytest.mark.parametrize("dq_mode", ["stored", "recompute"])
+@pytest.mark.parametrize("dq_mode,suffix", PATHS)
 @pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2), (8, 2), (16, 2), (8, 1)])
-def test_bf16_gqa_groups(gpu_lib, Hq, Hkv, dq_mode):
-    run_case(gpu_lib, 20 + Hq, 2, Hq, Hkv, 128, 384, 2, (384, 300), "bf16", dq_mode=dq_mode)
+def test_bf16_gqa_groups(gpu_lib, Hq, Hkv, dq_mode, suffix):
+    run_case(gpu_lib, 20 + Hq, 2, Hq, Hkv, 128, 384, 2, (384, 300), "bf16", dq_mode=dq_mode,
+             suffix=suffix)
+
+
+@pytest.mark.parametrize("step", [5, 12])
+def test_bf16_long_ttt(gpu_lib, step):
+    """Many suffix blocks (the long-TTT workload runs to k = 12): fused and separate paths."""
+    for suffix in ("fused", "separate"):
+        run_case(gpu_lib, 60 + step, 1, 4, 1, 128, 256, step, 201, "bf16", suffix=suffix)
+
+
+def test_bf16_suffix_paths_agree(gpu_lib):
+    """Fused and separate forward suffix paths agree within the sum of their bounds against
+    the oracle (o 1e-2 each, lse 1e-3 each)."""
+    import torch
+    from tests.helpers import to_dev
+    q, k, v, do, T = inputs.make_case(53, 2, 8, 2, 128, 640, 3, (640, 411), "bf16")
+    qd, kd, vd = (to_dev(x, torch.bfloat16) for x in (q, k, v))
+    Td = torch.as_tensor(T, device="cuda")
+    of, lf = gpu_lib.ttt_attn_fwd(qd, kd, vd, Td, suffix="fused")
+    os_, ls = gpu_lib.ttt_attn_fwd(qd, kd, vd, Td, suffix="separate")
+    assert float((of.float() - os_.float()).abs().max()) <= 2e-2
+    assert float((lf - ls).abs().max()) <= 2e-3
 
 
 def test_bf16_dq_modes_agree(gpu_lib):
@@ -80,13 +107,15 @@ def test_bf16_dq_modes_agree(gpu_lib):
     assert float((a[0].float() - b[0].float()).abs().max()) <= 1e-2 * den
 
 
-def test_bf16_peaky_logits(gpu_lib):
+@pytest.mark.parametrize("suffix", ["fused", "separate"])
+def test_bf16_peaky_logits(gpu_lib, suffix):
     """q x 4 makes the softmax peaky, so the running max is overtaken often (online rescaling).
 
     Outside the N(0,1) workloads, so the o bound is derived here: with nearly one-hot rows the
     bf16 rounding of P (relative 2^-9) moves o by up to 2^-9 * max|v| ~ 0.009 (|v| <= 4.6 at
     these sizes) on top of the bf16 output half-ulp 0.0078 for |o| in [2, 4): 2e-2."""
-    run_case(gpu_lib, 31, 2, 4, 1, 128, 512, 3, (512, 333), "bf16", q_mult=4.0, o_tol=2e-2)
+    run_case(gpu_lib, 31, 2, 4, 1, 128, 512, 3, (512, 333), "bf16", q_mult=4.0, o_tol=2e-2,
+             suffix=suffix)
 
 
 def test_bf16_out_of_range_lengths_are_clamped(gpu_lib):
