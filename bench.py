@@ -80,9 +80,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload number (2: the 8B draft layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
-    ap.add_argument("--suffix", choices=("fused", "separate"), default="fused",
-                    help="forward: diagonal keys merged inside the causal kernel, or the standalone "
-                         "suffix kernel")
+    ap.add_argument("--suffix", choices=("fused", "separate", "dense"), default="fused",
+                    help="forward: diagonal keys merged inside the causal kernel, the standalone "
+                         "suffix kernel, or (measurement variant) masked diagonal matrix-core tiles")
     ap.add_argument("--dq-mode", choices=("stored", "recompute"), default="stored",
                     help="dS handed from the dK/dV kernel to the dQ kernel through the workspace, "
                          "or recomputed in the dQ kernel")

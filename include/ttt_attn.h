@@ -61,12 +61,18 @@ enum ttt_attn_dtype {
  *   that the standalone bandwidth-bound suffix kernel merges (the fp32 path always does so).
  * TTT_FLAG_RECOMPUTE_DQ: no stored dS (a much smaller backward workspace); the dQ kernel
  *   recomputes S and dP, three products per tile.  dk/dv are bitwise the same either way.
+ * TTT_FLAG_DENSE_DIAGONAL (a measurement variant of the forward, not for production): the
+ *   diagonal keys go through the matrix cores as masked 64-key tiles (two per block t per
+ *   128-query tile), the way a block-sparse mask (FlexAttention's BlockMask) would evaluate
+ *   them, instead of the per-row gather.  Cannot be combined with TTT_FLAG_SEPARATE_SUFFIX;
+ *   the backward ignores it.
  * In the backward the suffix kernel always adds the diagonal keys' terms for k > 0.  The
  * workspace sizes below depend on the flags.
  */
 enum ttt_attn_flags {
   TTT_FLAG_SEPARATE_SUFFIX = 1,
-  TTT_FLAG_RECOMPUTE_DQ = 2
+  TTT_FLAG_RECOMPUTE_DQ = 2,
+  TTT_FLAG_DENSE_DIAGONAL = 4
 };
 
 enum ttt_attn_status {

@@ -87,7 +87,10 @@ int validate(const ttt_attn_params* p) {
   } else {
     return TTT_E_UNSUPPORTED;
   }
-  if (p->flags & ~(TTT_FLAG_SEPARATE_SUFFIX | TTT_FLAG_RECOMPUTE_DQ)) return TTT_E_UNSUPPORTED;
+  if (p->flags & ~(TTT_FLAG_SEPARATE_SUFFIX | TTT_FLAG_RECOMPUTE_DQ | TTT_FLAG_DENSE_DIAGONAL))
+    return TTT_E_UNSUPPORTED;
+  if ((p->flags & TTT_FLAG_SEPARATE_SUFFIX) && (p->flags & TTT_FLAG_DENSE_DIAGONAL))
+    return TTT_E_UNSUPPORTED;
   return TTT_OK;
 }
 
@@ -194,7 +197,7 @@ const char* ttt_attn_status_string(int status) {
     case TTT_OK: return "ok";
     case TTT_E_NULL: return "null pointer argument";
     case TTT_E_SHAPE: return "invalid shape (non-positive size, heads_q % heads_kv != 0, ttt_step < 0, scale not finite and positive, or size overflow)";
-    case TTT_E_UNSUPPORTED: return "unsupported configuration (f32: head_dim 64 or 128; bf16: head_dim 128 and q_len % 128 == 0; unknown flags)";
+    case TTT_E_UNSUPPORTED: return "unsupported configuration (f32: head_dim 64 or 128; bf16: head_dim 128 and q_len % 128 == 0; unknown or conflicting flags)";
     case TTT_E_ALIGN: return "pointer not 16-byte aligned";
     case TTT_E_WORKSPACE: return "workspace smaller than required";
     case TTT_E_HIP: return "HIP kernel launch failed";
@@ -238,7 +241,7 @@ int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const v
     const bf16* vb = (const bf16*)v;
     // final_causal with k > 0: the kernel merges the suffix keys itself
     e = launch_fwd_causal_mfma(s, qb, kb, vb, seq_T, final_causal ? o : (void*)oc, lsec,
-                               final_causal, st);
+                               final_causal, (p->flags & TTT_FLAG_DENSE_DIAGONAL) != 0, st);
     if (e != hipSuccess) return TTT_E_HIP;
     if (!final_causal)
       e = launch_fwd_suffix<bf16>(s, qb, kb, vb, seq_T, oc, lsec, (bf16*)o, lse, st);

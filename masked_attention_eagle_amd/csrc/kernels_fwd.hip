@@ -35,7 +35,12 @@ constexpr int FBM = 128; // queries per workgroup
 constexpr int FBN = 64;  // keys per tile
 constexpr float kRescaleLog2 = 8.f;  // headroom of the unnormalised probabilities (base 2)
 
-template <bool FINAL>
+// DIAG (measurement variant, with FINAL): instead of the per-lane gather, the diagonal keys
+// of blocks 1..k go through the matrix cores the way a BlockMask-driven kernel handles them:
+// block t's key rows [t*Q_LEN + q0, t*Q_LEN + q0 + 128) form two extra 64-key tiles after the
+// causal ones, processed as partial tiles whose mask keeps key row t*Q_LEN + i for query i.
+// Each such tile meets the queries of two of the four waves; the other two skip it.
+template <bool FINAL, bool DIAG>
 __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ seq_T, void* __restrict__ o_out, float* __restrict__ lse_out,
@@ -68,7 +73,15 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
   const bf16* vb = v + (size_t)(b * s.Hkv + g) * s.KV * FD;
 
   const int kv_end = min(q0 + FBM, T);
-  const int ntiles = (kv_end + FBN - 1) / FBN;
+  const int ncausal = (kv_end + FBN - 1) / FBN;
+  // DIAG: two diagonal tiles per block t = 1..k, unless no row of this workgroup is live
+  const int ntiles = ncausal + ((DIAG && q0 < T) ? 2 * s.step : 0);
+  // first key row of tile j in k/v, and its first key index in block-local coordinates
+  auto tile_row = [&](int j) -> size_t {
+    if (!DIAG || j < ncausal) return (size_t)j * FBN;
+    const int d = j - ncausal;
+    return (size_t)(1 + d / 2) * s.L + q0 + FBN * (d & 1);
+  };
 
   f32x16 acc[4];
 #pragma unroll
@@ -78,16 +91,18 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
   const FragOffsets fo = make_frag_offsets(lane);
 
   auto issue = [&](int j, bf16* dK, bf16* dV) {
-    load_tile<FBN, 4>(kb + (size_t)j * FBN * FD, FD, dK, wave, lane);
-    load_tile<FBN, 4>(vb + (size_t)j * FBN * FD, FD, dV, wave, lane);
+    load_tile<FBN, 4>(kb + tile_row(j) * FD, FD, dK, wave, lane);
+    load_tile<FBN, 4>(vb + tile_row(j) * FD, FD, dV, wave, lane);
   };
 
   // One tile: prefetch tile j + 1 into (nK, nV) while computing tile j from (cK, cV).
   auto body = [&](int j, const bf16* cK, const bf16* cV, bf16* nK, bf16* nV) {
     const FragOffsets fl = opaque(fo);
     if (j + 1 < ntiles) issue(j + 1, nK, nV);
-    const int k0 = j * FBN;
-    if (k0 <= qw + 31) {  // some query of this wave can see a key of the tile
+    const bool diag = DIAG && j >= ncausal;  // a diagonal tile of block t >= 1
+    // block-local index of the tile's first key
+    const int k0 = diag ? q0 + FBN * ((j - ncausal) & 1) : j * FBN;
+    if (diag ? (k0 <= qw + 31 && qw <= k0 + FBN - 1) : (k0 <= qw + 31)) {  // the wave sees a key
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -95,8 +110,17 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
         for (int st = 0; st < 2; ++st)
           sacc[st] = mfma32(frag_row(cK, st * 32, t, fl), qf[t], sacc[st]);
       }
-      const bool full = (k0 + FBN - 1 <= qw) && (k0 + FBN <= T);
-      if (!full) {
+      const bool full = !diag && (k0 + FBN - 1 <= qw) && (k0 + FBN <= T);
+      if (diag) {  // key row t*Q_LEN + key serves query key only, and only for rows < T
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + st * 32 + acc_row(i, hi);
+            if (key != my_q || my_q >= T) sacc[st][i] = kNegInf;
+          }
+        }
+      } else if (!full) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -177,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
   };
 
   if (ntiles > 0) issue(0, sK0, sV0);
-  if (FINAL && s.step > 0 && my_q < T) {
+  if (FINAL && !DIAG && s.step > 0 && my_q < T) {
     // Suffix keys t*Q_LEN + my_q (t = 1..k), merged before the causal tiles (the softmax
     // state is order-independent) while tile 0 is in flight.  Each lane takes the same half
     // of the K row as of q (d = 16c + 8*hi ..) and the same half of the V row as of O
@@ -256,13 +280,18 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
 
 hipError_t launch_fwd_causal_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                   const int32_t* seq_T, void* o, float* lse, bool final_out,
-                                  hipStream_t st) {
+                                  bool dense_diagonal, hipStream_t st) {
   const dim3 grid(s.B * s.Hq * (s.L / FBM));
+  if (dense_diagonal && final_out && s.step > 0) {
+    LaunchTimer timer("fwd_dense_diag_mfma", st);
+    fwd_causal_mfma_kernel<true, true><<<grid, 256, 0, st>>>(q, k, v, seq_T, o, lse, s);
+    return hipGetLastError();
+  }
   LaunchTimer timer("fwd_causal_mfma", st);
   if (final_out)
-    fwd_causal_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, v, seq_T, o, lse, s);
+    fwd_causal_mfma_kernel<true, false><<<grid, 256, 0, st>>>(q, k, v, seq_T, o, lse, s);
   else
-    fwd_causal_mfma_kernel<false><<<grid, 256, 0, st>>>(q, k, v, seq_T, o, lse, s);
+    fwd_causal_mfma_kernel<false, false><<<grid, 256, 0, st>>>(q, k, v, seq_T, o, lse, s);
   return hipGetLastError();
 }
 

@@ -18,11 +18,12 @@ struct LaunchTimer {
 };
 
 // Forward.
-// final_out: o (bf16) and lse are final; for k > 0 the kernel merges the suffix keys itself.
-// Otherwise it writes the fp32 causal state (o_c, lse_c) for the suffix kernel.
+// final_out: o (bf16) and lse are final; for k > 0 the kernel merges the suffix keys itself
+// (per-lane gather, or with dense_diagonal as masked matrix-core tiles).  Otherwise it writes
+// the fp32 causal state (o_c, lse_c) for the suffix kernel.
 hipError_t launch_fwd_causal_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                   const int32_t* seq_T, void* o, float* lse, bool final_out,
-                                  hipStream_t st);
+                                  bool dense_diagonal, hipStream_t st);
 template <typename T>
 hipError_t launch_fwd_causal_valu(const Shape& s, const T* q, const T* k, const T* v,
                                   const int32_t* seq_T, void* o, float* lse, bool final_out,

@@ -19,7 +19,8 @@ TTT_DTYPE_F32 = 0
 TTT_DTYPE_BF16 = 1
 TTT_FLAG_SEPARATE_SUFFIX = 1
 TTT_FLAG_RECOMPUTE_DQ = 2
-SUFFIX_PATHS = {"fused": 0, "separate": TTT_FLAG_SEPARATE_SUFFIX}
+TTT_FLAG_DENSE_DIAGONAL = 4
+SUFFIX_PATHS = {"fused": 0, "separate": TTT_FLAG_SEPARATE_SUFFIX, "dense": TTT_FLAG_DENSE_DIAGONAL}
 DQ_MODES = {"stored": 0, "recompute": TTT_FLAG_RECOMPUTE_DQ}
 
 STATUS = {
@@ -110,7 +111,7 @@ def make_params(B: int, Hq: int, Hkv: int, L: int, d: int, step: int, scale: flo
 
 
 def path_flags(suffix: str = "fused", dq_mode: str = "stored") -> int:
-    """ttt_attn_params.flags for a forward suffix path ("fused" | "separate") and a backward
+    """ttt_attn_params.flags for a forward suffix path ("fused" | "separate" | "dense") and a backward
     dQ mode ("stored": dS handed from the dK/dV kernel to the dQ kernel | "recompute")."""
     if suffix not in SUFFIX_PATHS:
         raise ValueError(f"suffix must be one of {sorted(SUFFIX_PATHS)}, not {suffix!r}")
@@ -174,7 +175,8 @@ def ttt_attn_fwd(q, k, v, seq_T, scale: Optional[float] = None, out=None, lse=No
 
     seq_T: int32 [B] on the GPU.  The TTT step is k.shape[2] // L - 1.  suffix "fused"
     merges the diagonal keys of blocks 1..k inside the causal kernel (bf16); "separate" runs
-    the standalone suffix kernel on an fp32 causal state.
+    the standalone suffix kernel on an fp32 causal state; "dense" (measurement variant) runs
+    them through the matrix cores as masked diagonal tiles.
     """
     import torch
     lib = load()

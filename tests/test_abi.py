@@ -118,7 +118,7 @@ def test_workspace_sizes():
     (dict(scale=-0.088), -2),
     (dict(d=64), -3), (dict(L=4000), -3), (dict(dtype=7), -3),
     (dict(dtype=A.TTT_DTYPE_F32, d=96), -3), (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10), -2),
-    (dict(flags=4), -3), (dict(flags=-1), -3),
+    (dict(flags=8), -3), (dict(flags=-1), -3), (dict(flags=5), -3),
 ])
 def test_validation_errors(kw, code):
     lib = A.load()

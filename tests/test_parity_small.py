@@ -69,10 +69,18 @@ def test_bf16_gqa_groups(gpu_lib, Hq, Hkv, dq_mode, suffix):
              suffix=suffix)
 
 
+@pytest.mark.parametrize("step", [1, 3])
+@pytest.mark.parametrize("T", [(256, 256), (0, 256), (1, 255), (65, 127), (200, 17)])
+def test_bf16_dense_diagonal_forward(gpu_lib, step, T):
+    """The measurement variant that runs the diagonal keys through masked matrix-core tiles
+    (forward only; the backward ignores the flag)."""
+    run_case(gpu_lib, 70 + step, 2, 4, 2, 128, 256, step, T, "bf16", suffix="dense")
+
+
 @pytest.mark.parametrize("step", [5, 12])
 def test_bf16_long_ttt(gpu_lib, step):
     """Many suffix blocks (the long-TTT workload runs to k = 12): fused and separate paths."""
-    for suffix in ("fused", "separate"):
+    for suffix in ("fused", "separate", "dense"):
         run_case(gpu_lib, 60 + step, 1, 4, 1, 128, 256, step, 201, "bf16", suffix=suffix)
 
 
