@@ -83,6 +83,9 @@ def parse():
     ap.add_argument("--suffix", choices=("fused", "separate", "dense"), default="fused",
                     help="forward: diagonal keys merged inside the causal kernel, the standalone "
                          "suffix kernel, or (measurement variant) masked diagonal matrix-core tiles")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the whole-TTT calls (one forward and one backward call over one KV "
+                         "cache, dK/dV summed over the steps) instead of the per-step calls")
     ap.add_argument("--dq-mode", choices=("stored", "recompute"), default="stored",
                     help="dS handed from the dK/dV kernel to the dQ kernel through the workspace, "
                          "or recomputed in the dQ kernel")
@@ -106,6 +109,49 @@ def calibrate_copy(mib: int) -> None:
     dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_mib": mib, "bytes": 2 * n}))
+
+
+def sweep_step(args, w, T, blocks, lib, A, dev, t_setup):
+    """Resident inputs of the whole-TTT calls: one KV cache [B, Hkv, K*L, d], step-major q
+    and dO; returns the step function (forward sweep, then backward sweep)."""
+    import torch
+    bf = torch.bfloat16
+    steps = list(w.steps)
+    K = len(steps)
+    kc = torch.cat([torch.from_numpy(b[0]) for b in blocks], 2).to(dev, bf)
+    vc = torch.cat([torch.from_numpy(b[1]) for b in blocks], 2).to(dev, bf)
+    qa = torch.stack([torch.from_numpy(inputs_mod().q_at(w, k)) for k in steps]).to(dev, bf)
+    da = torch.stack([torch.from_numpy(inputs_mod().do_at(w, k)) for k in steps]).to(dev, bf)
+    Td = torch.as_tensor(T, device=dev)
+    oa, la = torch.empty_like(qa), torch.empty(qa.shape[:4], dtype=torch.float32, device=dev)
+    dqa, dkc, dvc = torch.empty_like(qa), torch.empty_like(kc), torch.empty_like(vc)
+    p = A.make_params(w.B, w.Hq, w.Hkv, w.L, w.d, steps[-1], w.scale, A.TTT_DTYPE_BF16,
+                      A.path_flags(args.suffix, args.dq_mode))
+    nb = max(int(lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(p))),
+             int(lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(p))))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    fa = (ctypes.byref(p), qa.data_ptr(), kc.data_ptr(), vc.data_ptr(), Td.data_ptr(),
+          oa.data_ptr(), la.data_ptr(), ws.data_ptr(), nb, sp)
+    ba = (ctypes.byref(p), qa.data_ptr(), kc.data_ptr(), vc.data_ptr(), Td.data_ptr(),
+          oa.data_ptr(), la.data_ptr(), da.data_ptr(), dqa.data_ptr(), dkc.data_ptr(),
+          dvc.data_ptr(), ws.data_ptr(), nb, sp)
+    keep = (kc, vc, qa, da, Td, oa, la, dqa, dkc, dvc, ws, p)
+
+    def one_step():
+        _ = keep
+        for fn, a in ((lib.ttt_attn_fwd_sweep, fa), (lib.ttt_attn_bwd_sweep, ba)):
+            rc = fn(*a)
+            if rc:
+                raise A.TTTError(rc, A.status_string(rc))
+    return one_step, setup_s
+
+
+def inputs_mod():
+    from masked_attention_eagle_amd import inputs
+    return inputs
 
 
 def main():
@@ -140,46 +186,50 @@ def main():
     t_setup = time.time()
     bf = torch.bfloat16
     blocks = [inputs.kv_block(w, t) for t in range(K)]
+    if args.sweep:
+        one_step, setup_s = sweep_step(args, w, T, blocks, lib, A, dev, t_setup)
+        blocks = []
     kv = []
-    for k in steps:
+    for k in (steps if not args.sweep else []):
         kk = np.concatenate([blocks[t][0] for t in range(k + 1)], axis=2)
         vv = np.concatenate([blocks[t][1] for t in range(k + 1)], axis=2)
         kv.append((torch.from_numpy(kk).to(dev, bf), torch.from_numpy(vv).to(dev, bf)))
         del kk, vv
-    qs = [torch.from_numpy(inputs.q_at(w, k)).to(dev, bf) for k in steps]
-    dos = [torch.from_numpy(inputs.do_at(w, k)).to(dev, bf) for k in steps]
-    Td = torch.as_tensor(T, device=dev)
-    os_ = [torch.empty_like(q) for q in qs]
-    lses = [torch.empty(q.shape[:3], dtype=torch.float32, device=dev) for q in qs]
-    dqs = [torch.empty_like(q) for q in qs]
-    dks = [torch.empty_like(kv[i][0]) for i in range(K)]
-    dvs = [torch.empty_like(kv[i][1]) for i in range(K)]
-    params = [A.make_params(w.B, w.Hq, w.Hkv, w.L, w.d, k, w.scale, A.TTT_DTYPE_BF16,
-                            A.path_flags(args.suffix, args.dq_mode)) for k in steps]
-    ws_bytes = max(max(A.fwd_workspace_size(p), A.bwd_workspace_size(p)) for p in params)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    setup_s = time.time() - t_setup
+    if not args.sweep:
+        qs = [torch.from_numpy(inputs.q_at(w, k)).to(dev, bf) for k in steps]
+        dos = [torch.from_numpy(inputs.do_at(w, k)).to(dev, bf) for k in steps]
+        Td = torch.as_tensor(T, device=dev)
+        os_ = [torch.empty_like(q) for q in qs]
+        lses = [torch.empty(q.shape[:3], dtype=torch.float32, device=dev) for q in qs]
+        dqs = [torch.empty_like(q) for q in qs]
+        dks = [torch.empty_like(kv[i][0]) for i in range(K)]
+        dvs = [torch.empty_like(kv[i][1]) for i in range(K)]
+        params = [A.make_params(w.B, w.Hq, w.Hkv, w.L, w.d, k, w.scale, A.TTT_DTYPE_BF16,
+                                A.path_flags(args.suffix, args.dq_mode)) for k in steps]
+        ws_bytes = max(max(A.fwd_workspace_size(p), A.bwd_workspace_size(p)) for p in params)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        setup_s = time.time() - t_setup
 
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    fwd_args = [(ctypes.byref(params[i]), qs[i].data_ptr(), kv[i][0].data_ptr(), kv[i][1].data_ptr(),
-                 Td.data_ptr(), os_[i].data_ptr(), lses[i].data_ptr(), ws.data_ptr(), ws_bytes, sp)
-                for i in range(K)]
-    bwd_args = [(ctypes.byref(params[i]), qs[i].data_ptr(), kv[i][0].data_ptr(), kv[i][1].data_ptr(),
-                 Td.data_ptr(), os_[i].data_ptr(), lses[i].data_ptr(), dos[i].data_ptr(),
-                 dqs[i].data_ptr(), dks[i].data_ptr(), dvs[i].data_ptr(), ws.data_ptr(), ws_bytes, sp)
-                for i in range(K)]
+        stream = torch.cuda.current_stream()
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        fwd_args = [(ctypes.byref(params[i]), qs[i].data_ptr(), kv[i][0].data_ptr(), kv[i][1].data_ptr(),
+                     Td.data_ptr(), os_[i].data_ptr(), lses[i].data_ptr(), ws.data_ptr(), ws_bytes, sp)
+                    for i in range(K)]
+        bwd_args = [(ctypes.byref(params[i]), qs[i].data_ptr(), kv[i][0].data_ptr(), kv[i][1].data_ptr(),
+                     Td.data_ptr(), os_[i].data_ptr(), lses[i].data_ptr(), dos[i].data_ptr(),
+                     dqs[i].data_ptr(), dks[i].data_ptr(), dvs[i].data_ptr(), ws.data_ptr(), ws_bytes, sp)
+                    for i in range(K)]
 
-    def one_step():
-        for i in range(K):
-            rc = lib.ttt_attn_fwd(*fwd_args[i])
-            if rc:
-                raise A.TTTError(rc, A.status_string(rc))
-        for i in reversed(range(K)):
-            rc = lib.ttt_attn_bwd(*bwd_args[i])
-            if rc:
-                raise A.TTTError(rc, A.status_string(rc))
+        def one_step():
+            for i in range(K):
+                rc = lib.ttt_attn_fwd(*fwd_args[i])
+                if rc:
+                    raise A.TTTError(rc, A.status_string(rc))
+            for i in reversed(range(K)):
+                rc = lib.ttt_attn_bwd(*bwd_args[i])
+                if rc:
+                    raise A.TTTError(rc, A.status_string(rc))
 
     for _ in range(args.warmup):
         one_step()
@@ -267,6 +317,7 @@ def main():
                    "ttt_steps": f"k=0..{steps[-1]}", "global_batch": w.B, "seq_len": w.L,
                    "parallelism": "single GPU"},
         "dq_mode": args.dq_mode, "suffix": args.suffix,
+        "api": "sweep" if args.sweep else "per-step",
         "tokens_per_s": round(tokens, 1),
         "unmasked_flop_per_step": flops,
         "roofline": roofline,

@@ -136,6 +136,30 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/*
+ * Whole TTT sweep (bf16 only): the K = p->ttt_step + 1 steps of one TTT unroll over a single
+ * KV cache, without per-step copies of the cache.  Layouts (contiguous):
+ *   q, o, dout, dq   [K, B, Hq, Q_LEN, d]     step-major: step k's tensors of the per-step API
+ *   lse              [K, B, Hq, Q_LEN]
+ *   k, v, dk, dv     [B, Hkv, K*Q_LEN, d]     the cache: block t = rows [t*Q_LEN, (t+1)*Q_LEN)
+ * Step k attends rows [0, (k+1)*Q_LEN) of the cache under the mask above (block 0 causal,
+ * blocks 1..k diagonal).  The forward writes o and lse of every step.  The backward writes dq
+ * of every step and the total gradient of the cache, dk/dv = sum over the steps k of step
+ * k's dK/dV (block t receives the diagonal gradients of every step k >= t, block 0 the causal
+ * gradient of all of them); the sum is kept in fp32 inside the workspace and rounded to bf16
+ * once.  The steps run in order on `stream`; flags select the paths as for the per-step calls.
+ * Same error codes; fp32 data returns TTT_E_UNSUPPORTED.
+ */
+size_t ttt_attn_fwd_sweep_workspace_size(const ttt_attn_params* p);
+size_t ttt_attn_bwd_sweep_workspace_size(const ttt_attn_params* p);
+int ttt_attn_fwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                       const int32_t* seq_T, void* o, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                       const int32_t* seq_T, const void* o, const float* lse, const void* dout,
+                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* Static text for a status code. */
 const char* ttt_attn_status_string(int status);
 

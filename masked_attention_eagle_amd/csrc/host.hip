@@ -2,6 +2,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "launch.h"
@@ -215,22 +216,16 @@ size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p) {
   return bwd_layout(make_shape(p), p->dtype, stored_ds(p)).total;
 }
 
-int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
-                 const int32_t* seq_T, void* o, float* lse, void* workspace,
-                 size_t workspace_bytes, void* stream) {
-  int rc = validate(p);
-  if (rc != TTT_OK) return rc;
-  if (!q || !k || !v || !seq_T || !o || !lse) return TTT_E_NULL;
-  const Shape s = make_shape(p);
+}  // extern "C"
+
+namespace ttt {
+namespace {
+
+// One forward step on validated arguments (s.KV is the row stride of k and v per KV group).
+int run_fwd(const ttt_attn_params* p, const Shape& s, const void* q, const void* k,
+            const void* v, const int32_t* seq_T, void* o, float* lse, char* ws, hipStream_t st) {
   const bool fused = fused_fwd(p);
   const FwdLayout w = fwd_layout(s, fused);
-  if (w.total > 0 && !workspace) return TTT_E_NULL;
-  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
-      !aligned16(lse) || !aligned16(workspace))
-    return TTT_E_ALIGN;
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
   const bool final_causal = s.step == 0 || fused;
   float* oc = final_causal ? nullptr : (float*)(ws + w.oc);
   float* lsec = final_causal ? lse : (float*)(ws + w.lsec);
@@ -258,24 +253,14 @@ int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const v
   return hip_status(e);
 }
 
-int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
-                 const int32_t* seq_T, const void* o, const float* lse, const void* dout,
-                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                 void* stream) {
-  int rc = validate(p);
-  if (rc != TTT_OK) return rc;
-  if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
-  const Shape s = make_shape(p);
+// One backward step on validated arguments.  With ga.dk set (bf16 only) the dK/dV rows of
+// this step go to the fp32 sums instead of dk/dv.
+int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void* k,
+            const void* v, const int32_t* seq_T, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, char* ws, GradAcc ga,
+            hipStream_t st) {
   const bool with_ds = stored_ds(p);
   const BwdLayout w = bwd_layout(s, p->dtype, with_ds);
-  if (w.total > 0 && !workspace) return TTT_E_NULL;
-  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
-      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
-      !aligned16(dv) || !aligned16(workspace))
-    return TTT_E_ALIGN;
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
   float* Dd = (float*)(ws + w.Dd);
   const bool final_causal = s.step == 0;
   float* dqacc = final_causal ? nullptr : (float*)(ws + w.dqacc);
@@ -290,10 +275,10 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
     void* dq_causal = final_causal ? dq : (void*)dqacc;
     if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, st)) != hipSuccess) return TTT_E_HIP;
     if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
-                                  w.nsplit, dsb, st)) != hipSuccess)
+                                  w.nsplit, dsb, ga, st)) != hipSuccess)
       return TTT_E_HIP;
     if (w.nsplit > 1 &&
-        (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
+        (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, ga, st)) != hipSuccess)
       return TTT_E_HIP;
     if (with_ds)
       e = launch_bwd_dq_ds(s, kb, dsb, seq_T, dq_causal, final_causal, st);
@@ -302,7 +287,7 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
     if (e != hipSuccess) return TTT_E_HIP;
     if (!final_causal)
       e = launch_bwd_suffix<bf16>(s, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq, (bf16*)dk,
-                                  (bf16*)dv, st);
+                                  (bf16*)dv, ga, st);
   } else {
     const float* qf = (const float*)q;
     const float* kf = (const float*)k;
@@ -317,9 +302,138 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
       return TTT_E_HIP;
     if (!final_causal)
       e = launch_bwd_suffix<float>(s, qf, kf, vf, dof, lse, Dd, seq_T, dqacc, (float*)dq,
-                                   (float*)dk, (float*)dv, st);
+                                   (float*)dk, (float*)dv, GradAcc{}, st);
   }
   return hip_status(e);
+}
+
+// Whole-TTT sweep: p->ttt_step = K - 1, K steps over one cache of K*Q_LEN rows per KV group.
+// Shape of step k: its own step index and the cache's row stride.
+Shape sweep_shape(const ttt_attn_params* p, int k) {
+  Shape s = make_shape(p);
+  s.step = k;  // s.KV stays (K) * Q_LEN: the row stride of the cache
+  return s;
+}
+size_t sweep_fwd_ws(const ttt_attn_params* p) {
+  size_t m = 0;
+  for (int k = 0; k <= p->ttt_step; ++k) m = std::max(m, fwd_layout(sweep_shape(p, k), fused_fwd(p)).total);
+  return m;
+}
+size_t sweep_bwd_step_ws(const ttt_attn_params* p) {
+  size_t m = 0;
+  for (int k = 0; k <= p->ttt_step; ++k)
+    m = std::max(m, bwd_layout(sweep_shape(p, k), p->dtype, stored_ds(p)).total);
+  return m;
+}
+size_t sweep_grad_elems(const ttt_attn_params* p) {  // elements of dk (or dv)
+  return (size_t)p->batch * p->heads_kv * (size_t)(p->ttt_step + 1) * p->q_len * p->head_dim;
+}
+
+}  // namespace
+}  // namespace ttt
+
+extern "C" {
+
+int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                 const int32_t* seq_T, void* o, float* lse, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  int rc = validate(p);
+  if (rc != TTT_OK) return rc;
+  if (!q || !k || !v || !seq_T || !o || !lse) return TTT_E_NULL;
+  const Shape s = make_shape(p);
+  const FwdLayout w = fwd_layout(s, fused_fwd(p));
+  if (w.total > 0 && !workspace) return TTT_E_NULL;
+  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(workspace))
+    return TTT_E_ALIGN;
+  return run_fwd(p, s, q, k, v, seq_T, o, lse, (char*)workspace, (hipStream_t)stream);
+}
+
+int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                 const int32_t* seq_T, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  int rc = validate(p);
+  if (rc != TTT_OK) return rc;
+  if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
+  const Shape s = make_shape(p);
+  const BwdLayout w = bwd_layout(s, p->dtype, stored_ds(p));
+  if (w.total > 0 && !workspace) return TTT_E_NULL;
+  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(workspace))
+    return TTT_E_ALIGN;
+  return run_bwd(p, s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, (char*)workspace, GradAcc{},
+                 (hipStream_t)stream);
+}
+
+size_t ttt_attn_fwd_sweep_workspace_size(const ttt_attn_params* p) {
+  if (validate(p) != TTT_OK || p->dtype != TTT_DTYPE_BF16) return 0;
+  return sweep_fwd_ws(p);
+}
+
+size_t ttt_attn_bwd_sweep_workspace_size(const ttt_attn_params* p) {
+  if (validate(p) != TTT_OK || p->dtype != TTT_DTYPE_BF16) return 0;
+  return round_up(sweep_bwd_step_ws(p)) + 2 * round_up(sweep_grad_elems(p) * 4);
+}
+
+int ttt_attn_fwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                       const int32_t* seq_T, void* o, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int rc = validate(p);
+  if (rc != TTT_OK) return rc;
+  if (p->dtype != TTT_DTYPE_BF16) return TTT_E_UNSUPPORTED;
+  if (!q || !k || !v || !seq_T || !o || !lse) return TTT_E_NULL;
+  const size_t need = sweep_fwd_ws(p);
+  if (need > 0 && !workspace) return TTT_E_NULL;
+  if (workspace_bytes < need) return TTT_E_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(workspace))
+    return TTT_E_ALIGN;
+  const size_t qel = (size_t)p->batch * p->heads_q * p->q_len * p->head_dim;  // per step
+  const size_t rows = (size_t)p->batch * p->heads_q * p->q_len;
+  for (int kk = 0; kk <= p->ttt_step; ++kk) {
+    rc = run_fwd(p, sweep_shape(p, kk), (const bf16*)q + kk * qel, k, v, seq_T,
+                 (bf16*)o + kk * qel, lse + kk * rows, (char*)workspace, (hipStream_t)stream);
+    if (rc != TTT_OK) return rc;
+  }
+  return TTT_OK;
+}
+
+int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                       const int32_t* seq_T, const void* o, const float* lse, const void* dout,
+                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int rc = validate(p);
+  if (rc != TTT_OK) return rc;
+  if (p->dtype != TTT_DTYPE_BF16) return TTT_E_UNSUPPORTED;
+  if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
+  if (!workspace) return TTT_E_NULL;
+  const size_t step_ws = round_up(sweep_bwd_step_ws(p));
+  const size_t gbytes = round_up(sweep_grad_elems(p) * 4);
+  if (workspace_bytes < step_ws + 2 * gbytes) return TTT_E_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(workspace))
+    return TTT_E_ALIGN;
+  char* ws = (char*)workspace;
+  GradAcc ga;
+  ga.dk = (float*)(ws + step_ws);
+  ga.dv = (float*)(ws + step_ws + gbytes);
+  const size_t qel = (size_t)p->batch * p->heads_q * p->q_len * p->head_dim;
+  const size_t rows = (size_t)p->batch * p->heads_q * p->q_len;
+  hipStream_t st = (hipStream_t)stream;
+  // Last step first: it covers every row of the cache and so initialises the fp32 sums.
+  for (int kk = p->ttt_step; kk >= 0; --kk) {
+    ga.add = kk < p->ttt_step;
+    rc = run_bwd(p, sweep_shape(p, kk), (const bf16*)q + kk * qel, k, v, seq_T,
+                 (const bf16*)o + kk * qel, lse + kk * rows, (const bf16*)dout + kk * qel,
+                 (bf16*)dq + kk * qel, dk, dv, ws, ga, st);
+    if (rc != TTT_OK) return rc;
+  }
+  return hip_status(launch_grad_convert(ga.dk, ga.dv, (bf16*)dk, (bf16*)dv, sweep_grad_elems(p), st));
 }
 
 int ttt_loss_grad_inplace(const ttt_loss_params* p, void* z, const void* target, const float* g,

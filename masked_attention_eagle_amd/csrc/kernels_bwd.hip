@@ -30,6 +30,26 @@ constexpr int BD = 128;  // head dim of the matrix-core path
 constexpr int KBN = 128;  // keys per tile
 constexpr int KBM = 32;   // queries per tile
 
+// One dK or dV row slice of a suffix key: bf16 output, or (TTT sweep) the fp32 sum.
+template <typename T, int E>
+__device__ __forceinline__ void put_grad_row(T* out, float* acc, int add, size_t idx,
+                                             const float* x) {
+  if (acc) {
+    float a[E];
+    if (add) {
+      load_vec<float, E>(acc + idx, a);
+#pragma unroll
+      for (int e = 0; e < E; ++e) a[e] += x[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) a[e] = x[e];
+    }
+    store_vec<float, E>(acc + idx, a);
+  } else {
+    store_vec<T, E>(out + idx, x);
+  }
+}
+
 // dS hand-over between the dK/dV kernel and the dQ kernel.  dS of one head is kept in
 // 32 x 32 blocks (32 query rows x 32 keys of block 0); only blocks on or below the diagonal
 // exist, packed row after row (query block r holds key blocks 0..r).
@@ -65,7 +85,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, bf16* __restrict__ dk, bf16* __restrict__ dv,
-    float* __restrict__ part, int nsplit, bf16* __restrict__ ds_out, Shape s) {
+    float* __restrict__ part, int nsplit, bf16* __restrict__ ds_out, GradAcc ga, Shape s) {
   // Two stages in distinct arrays (the copy into one never stalls reads of the other).
   __shared__ __attribute__((aligned(1024))) bf16 sQ0[KBM * BD];
   __shared__ __attribute__((aligned(1024))) bf16 sO0[KBM * BD];
@@ -212,7 +232,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     int lo = lane;
     asm volatile("" : "+v"(lo));
     const int ohi = lo >> 5, ol32 = lo & 31;
-    if (nsplit == 1) {
+    if (nsplit == 1 && ga.dk) {  // sweep: fp32 sums over the TTT steps
+      float* akp = ga.dk + ((size_t)bg * s.KV + kw) * BD;
+      float* avp = ga.dv + ((size_t)bg * s.KV + kw) * BD;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int o = acc_row(i, ohi) * BD + 32 * u + ol32;
+          const float xk = dKacc[u][i] * s.scale, xv = dVacc[u][i];
+          akp[o] = ga.add ? akp[o] + xk : xk;
+          avp[o] = ga.add ? avp[o] + xv : xv;
+        }
+      }
+    } else if (nsplit == 1) {
       bf16* dkp = dk + ((size_t)bg * s.KV + kw) * BD;
       bf16* dvp = dv + ((size_t)bg * s.KV + kw) * BD;
 #pragma unroll
@@ -244,18 +277,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
-                                int nsplit, bf16* ds_out, hipStream_t st) {
+                                int nsplit, bf16* ds_out, GradAcc ga, hipStream_t st) {
   const dim3 grid(s.B * s.Hkv * nsplit * ((s.L / KBN + 1) / 2));
   LaunchTimer timer("bwd_dkdv_mfma", st);
   bwd_dkdv_mfma_kernel<<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dk, dv, part, nsplit,
-                                             ds_out, s);
+                                             ds_out, ga, s);
   return hipGetLastError();
 }
 
 // Sum of the nsplit partial dK/dV planes, in split order, into block 0 of dk/dv.
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
                                                           int nsplit, bf16* __restrict__ dk,
-                                                          bf16* __restrict__ dv, Shape s) {
+                                                          bf16* __restrict__ dv, GradAcc ga,
+                                                          Shape s) {
   const size_t plane = (size_t)s.B * s.Hkv * s.L * BD;
   const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e0 >= 2 * plane) return;
@@ -265,6 +299,11 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
   for (int sp = 1; sp < nsplit; ++sp)
     acc += *reinterpret_cast<const f32x4*>(part + (size_t)sp * 2 * plane + (is_v ? plane : 0) + e);
   const size_t bg = e / ((size_t)s.L * BD), rem = e % ((size_t)s.L * BD);
+  if (ga.dk) {  // sweep: fp32 sums over the TTT steps
+    f32x4* a = reinterpret_cast<f32x4*>((is_v ? ga.dv : ga.dk) + bg * s.KV * BD + rem);
+    *a = ga.add ? *a + acc : acc;
+    return;
+  }
   bf16x4 w;
 #pragma unroll
   for (int j = 0; j < 4; ++j) w[j] = (bf16)acc[j];
@@ -272,11 +311,35 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
 }
 
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
-                                  bf16* dv, hipStream_t st) {
+                                  bf16* dv, GradAcc ga, hipStream_t st) {
   const size_t n4 = (size_t)s.B * s.Hkv * s.L * BD * 2 / 4;
   const dim3 grid((unsigned)((n4 + 255) / 256));
   LaunchTimer timer("bwd_dkdv_reduce", st);
-  dkdv_reduce_kernel<<<grid, 256, 0, st>>>(part, nsplit, dk, dv, s);
+  dkdv_reduce_kernel<<<grid, 256, 0, st>>>(part, nsplit, dk, dv, ga, s);
+  return hipGetLastError();
+}
+
+// dk, dv = bf16 of the fp32 sums of a TTT sweep.
+__global__ __launch_bounds__(256) void grad_convert_kernel(const float* __restrict__ ak,
+                                                           const float* __restrict__ av,
+                                                           bf16* __restrict__ dk,
+                                                           bf16* __restrict__ dv, size_t n) {
+  const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= 2 * n) return;
+  const bool is_v = e >= n;
+  const size_t i = is_v ? e - n : e;
+  const f32x4 x = *reinterpret_cast<const f32x4*>((is_v ? av : ak) + i);
+  bf16x4 w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = (bf16)x[j];
+  *reinterpret_cast<bf16x4*>((is_v ? dv : dk) + i) = w;
+}
+
+hipError_t launch_grad_convert(const float* ak, const float* av, bf16* dk, bf16* dv, size_t n,
+                               hipStream_t st) {
+  const dim3 grid((unsigned)((2 * n / 4 + 255) / 256));
+  LaunchTimer timer("grad_convert", st);
+  grad_convert_kernel<<<grid, 256, 0, st>>>(ak, av, dk, dv, n);
   return hipGetLastError();
 }
 
@@ -774,7 +837,7 @@ __global__ __launch_bounds__(256) void bwd_suffix_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, const float* __restrict__ dq_acc, T* __restrict__ dq,
-    T* __restrict__ dk, T* __restrict__ dv, Shape s) {
+    T* __restrict__ dk, T* __restrict__ dv, GradAcc ga, Shape s) {
   constexpr int E = D / 16;
   const int sub = threadIdx.x & 15;
   const int blocks_per_bg = (s.L + 15) / 16;
@@ -850,8 +913,10 @@ __global__ __launch_bounds__(256) void bwd_suffix_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[e] *= s.scale;
     }
-    store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, aK);
-    store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, aV);
+    if (live || !ga.add) {  // dead rows: zero, or nothing to add
+      put_grad_row<T, E>(dk, ga.dk, ga.add, kv_base + (size_t)t * s.L * D, aK);
+      put_grad_row<T, E>(dv, ga.dv, ga.add, kv_base + (size_t)t * s.L * D, aV);
+    }
   }
 }
 
@@ -863,7 +928,7 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, const float* __restrict__ dq_acc, T* __restrict__ dq,
-    T* __restrict__ dk, T* __restrict__ dv, Shape s) {
+    T* __restrict__ dk, T* __restrict__ dv, GradAcc ga, Shape s) {
   constexpr int E = D / 16;
   const int sub = threadIdx.x & 15;
   const int blocks_per_bg = (s.L + 15) / 16;
@@ -925,8 +990,8 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[e] *= s.scale;
-      store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, aK);
-      store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, aV);
+      put_grad_row<T, E>(dk, ga.dk, ga.add, kv_base + (size_t)t * s.L * D, aK);
+      put_grad_row<T, E>(dv, ga.dv, ga.add, kv_base + (size_t)t * s.L * D, aV);
       if (t < s.step) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -935,13 +1000,13 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
         }
       }
     }
-  } else {
+  } else if (!ga.add) {  // rows no query sees: zero (nothing to add in a sweep's later steps)
     float z[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) z[e] = 0.f;
     for (int t = 1; t <= s.step; ++t) {
-      store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, z);
-      store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, z);
+      put_grad_row<T, E>(dk, ga.dk, 0, kv_base + (size_t)t * s.L * D, z);
+      put_grad_row<T, E>(dv, ga.dv, 0, kv_base + (size_t)t * s.L * D, z);
     }
   }
 #pragma unroll
@@ -959,13 +1024,13 @@ template <typename T, int D>
 static hipError_t bwd_suffix_dispatch(const Shape& s, dim3 grid, hipStream_t st, const T* q,
                                       const T* k, const T* v, const T* dout, const float* lse,
                                       const float* Dd, const int32_t* seq_T, const float* dq_acc,
-                                      T* dq, T* dk, T* dv) {
+                                      T* dq, T* dk, T* dv, GradAcc ga) {
   switch (s.G) {
-    case 1: bwd_suffix_g_kernel<T, D, 1><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
-    case 2: bwd_suffix_g_kernel<T, D, 2><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
-    case 4: bwd_suffix_g_kernel<T, D, 4><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
-    case 8: bwd_suffix_g_kernel<T, D, 8><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
-    default: bwd_suffix_kernel<T, D><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 1: bwd_suffix_g_kernel<T, D, 1><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
+    case 2: bwd_suffix_g_kernel<T, D, 2><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
+    case 4: bwd_suffix_g_kernel<T, D, 4><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
+    case 8: bwd_suffix_g_kernel<T, D, 8><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
+    default: bwd_suffix_kernel<T, D><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
   }
   return hipGetLastError();
 }
@@ -973,20 +1038,21 @@ static hipError_t bwd_suffix_dispatch(const Shape& s, dim3 grid, hipStream_t st,
 template <typename T>
 hipError_t launch_bwd_suffix(const Shape& s, const T* q, const T* k, const T* v, const T* dout,
                              const float* lse, const float* Dd, const int32_t* seq_T,
-                             const float* dq_acc, T* dq, T* dk, T* dv, hipStream_t st) {
+                             const float* dq_acc, T* dq, T* dk, T* dv, GradAcc ga,
+                             hipStream_t st) {
   const dim3 grid(s.B * s.Hkv * ((s.L + 15) / 16));
   LaunchTimer timer("bwd_suffix", st);
   if (s.D == 64)
-    return bwd_suffix_dispatch<T, 64>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv);
-  return bwd_suffix_dispatch<T, 128>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv);
+    return bwd_suffix_dispatch<T, 64>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga);
+  return bwd_suffix_dispatch<T, 128>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga);
 }
 template hipError_t launch_bwd_suffix<float>(const Shape&, const float*, const float*,
                                              const float*, const float*, const float*,
                                              const float*, const int32_t*, const float*, float*,
-                                             float*, float*, hipStream_t);
+                                             float*, float*, GradAcc, hipStream_t);
 template hipError_t launch_bwd_suffix<bf16>(const Shape&, const bf16*, const bf16*, const bf16*,
                                             const bf16*, const float*, const float*,
                                             const int32_t*, const float*, bf16*, bf16*, bf16*,
-                                            hipStream_t);
+                                            GradAcc, hipStream_t);
 
 }  // namespace ttt

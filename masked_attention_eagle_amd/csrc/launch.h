@@ -33,15 +33,27 @@ hipError_t launch_fwd_suffix(const Shape& s, const T* q, const T* k, const T* v,
                              const int32_t* seq_T, const float* oc, const float* lsec, T* o,
                              float* lse, hipStream_t st);
 
+// fp32 accumulation of dK/dV over the steps of a TTT sweep: with dk non-null the backward
+// kernels store (add == 0) or add (add != 0) their dK/dV rows there instead of writing the
+// bf16 outputs.  Rows a step does not own are left alone.
+struct GradAcc {
+  float* dk = nullptr;
+  float* dv = nullptr;
+  int add = 0;
+};
+
 // Backward.
 template <typename T>
 hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* Dd, hipStream_t st);
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
-                                int nsplit, bf16* ds_out, hipStream_t st);
+                                int nsplit, bf16* ds_out, GradAcc ga, hipStream_t st);
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
-                                  bf16* dv, hipStream_t st);
+                                  bf16* dv, GradAcc ga, hipStream_t st);
+// dk, dv (bf16) = the fp32 sums of a sweep (n elements each).
+hipError_t launch_grad_convert(const float* ak, const float* av, bf16* dk, bf16* dv, size_t n,
+                               hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                               const bf16* dout, const float* lse, const float* Dd,
                               const int32_t* seq_T, void* dq, bool final_out, hipStream_t st);
@@ -58,7 +70,8 @@ hipError_t launch_bwd_dq_valu(const Shape& s, const T* q, const T* k, const T* v
 template <typename T>
 hipError_t launch_bwd_suffix(const Shape& s, const T* q, const T* k, const T* v, const T* dout,
                              const float* lse, const float* Dd, const int32_t* seq_T,
-                             const float* dq_acc, T* dq, T* dk, T* dv, hipStream_t st);
+                             const float* dq_acc, T* dq, T* dk, T* dv, GradAcc ga,
+                             hipStream_t st);
 
 // In-place masked softmax-loss gradient.
 template <typename T>

@@ -31,6 +31,8 @@ STATUS = {
 # Every symbol the header declares.
 EXPORTS = (
     "ttt_attn_fwd_workspace_size", "ttt_attn_bwd_workspace_size", "ttt_attn_fwd", "ttt_attn_bwd",
+    "ttt_attn_fwd_sweep_workspace_size", "ttt_attn_bwd_sweep_workspace_size",
+    "ttt_attn_fwd_sweep", "ttt_attn_bwd_sweep",
     "ttt_attn_status_string", "ttt_attn_version", "ttt_attn_timing_enable",
     "ttt_attn_timing_read", "ttt_attn_timing_reset",
 )
@@ -80,6 +82,14 @@ def load() -> ctypes.CDLL:
     lib.ttt_attn_fwd.restype = ctypes.c_int
     lib.ttt_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ttt_attn_bwd.restype = ctypes.c_int
+    lib.ttt_attn_fwd_sweep_workspace_size.argtypes = [P]
+    lib.ttt_attn_fwd_sweep_workspace_size.restype = sz
+    lib.ttt_attn_bwd_sweep_workspace_size.argtypes = [P]
+    lib.ttt_attn_bwd_sweep_workspace_size.restype = sz
+    lib.ttt_attn_fwd_sweep.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ttt_attn_fwd_sweep.restype = ctypes.c_int
+    lib.ttt_attn_bwd_sweep.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ttt_attn_bwd_sweep.restype = ctypes.c_int
     lib.ttt_attn_status_string.argtypes = [ctypes.c_int]
     lib.ttt_attn_status_string.restype = ctypes.c_char_p
     lib.ttt_attn_version.argtypes = []
@@ -229,6 +239,61 @@ def ttt_attn_bwd(q, k, v, seq_T, o, lse, dout, scale: Optional[float] = None, dq
                             seq_T.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
                             _stream()))
+    return dq, dk, dv
+
+
+def _sweep_params(q, k, scale, flags: int) -> Params:
+    """Params of a whole-TTT sweep: q [K, B, Hq, L, d] over the cache k [B, Hkv, K*L, d]."""
+    if q.dim() != 5:
+        raise ValueError(f"q must be [K, B, Hq, L, d], got {tuple(q.shape)}")
+    K = q.shape[0]
+    if k.dim() != 4 or k.shape[2] != K * q.shape[3]:
+        raise ValueError(f"k must be [B, Hkv, K*L, d] with K = {K}, got {tuple(k.shape)}")
+    return _params_from(q[0], k, scale, flags)
+
+
+def ttt_attn_fwd_sweep(q, k, v, seq_T, scale: Optional[float] = None, suffix: str = "fused",
+                       workspace=None):
+    """o [K,B,Hq,L,d], lse [K,B,Hq,L] of the K steps of a TTT unroll: step k's queries q[k]
+    attend rows [0, (k+1)L) of the cache k, v [B,Hkv,K*L,d] (bf16)."""
+    import torch
+    lib = load()
+    p = _sweep_params(q, k, scale, path_flags(suffix))
+    _require(q, "q")
+    _require(k, "k", q.dtype)
+    _require(v, "v", q.dtype, k.shape)
+    _require(seq_T, "seq_T", torch.int32, (q.shape[1],))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:4], dtype=torch.float32, device=q.device)
+    need = int(lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(p)))
+    ws = _workspace(need, q.device) if workspace is None else workspace
+    _check(lib.ttt_attn_fwd_sweep(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  seq_T.data_ptr(), o.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                                  ws.numel(), _stream()))
+    return o, lse
+
+
+def ttt_attn_bwd_sweep(q, k, v, seq_T, o, lse, dout, scale: Optional[float] = None,
+                       dq_mode: str = "stored", workspace=None):
+    """dq [K,B,Hq,L,d] of every step and dk, dv [B,Hkv,K*L,d]: the gradient of the cache
+    summed over the steps (fp32 inside, rounded once)."""
+    import torch
+    lib = load()
+    p = _sweep_params(q, k, scale, path_flags("fused", dq_mode))
+    _require(q, "q")
+    _require(k, "k", q.dtype)
+    _require(v, "v", q.dtype, k.shape)
+    _require(seq_T, "seq_T", torch.int32, (q.shape[1],))
+    _require(o, "o", q.dtype, q.shape)
+    _require(lse, "lse", torch.float32, q.shape[:4])
+    _require(dout, "dout", q.dtype, q.shape)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = int(lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(p)))
+    ws = _workspace(need, q.device) if workspace is None else workspace
+    _check(lib.ttt_attn_bwd_sweep(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  seq_T.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                  ws.numel(), _stream()))
     return dq, dk, dv
 
 

@@ -164,3 +164,29 @@ def test_oracle_is_not_imported_by_the_product():
         for f in files:
             if f.endswith((".py", ".hip", ".cuh", ".h", ".cpp")):
                 assert not pat.search(open(os.path.join(root, f)).read()), f
+
+
+def test_sweep_workspace_and_errors():
+    """The sweep's backward workspace is the largest per-step workspace plus the two fp32
+    gradient sums of the cache; fp32 data is not supported; errors come before any launch."""
+    lib = A.load()
+    B, Hq, Hkv, L, d, K = 2, 32, 8, 4096, 128, 7
+    p = P(step=K - 1)
+    per_step = max(A.bwd_workspace_size(P(step=s)) for s in range(K))
+    sums = 2 * B * Hkv * K * L * d * 4
+    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(p)) == per_step + sums
+    assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(p)) == 0  # fused forward
+    sep = P(step=K - 1, flags=A.TTT_FLAG_SEPARATE_SUFFIX)
+    assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(sep)) == A.fwd_workspace_size(sep)
+    pf = P(step=2, dtype=A.TTT_DTYPE_F32)
+    assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(pf)) == 0
+    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(pf)) == 0
+    good = ctypes.c_void_p(1 << 20)
+    args = [good] * 11
+    assert lib.ttt_attn_fwd_sweep(ctypes.byref(pf), *args[:7], 1 << 40, None) == -3
+    assert lib.ttt_attn_bwd_sweep(ctypes.byref(pf), *args, 1 << 40, None) == -3
+    assert lib.ttt_attn_bwd_sweep(ctypes.byref(p), *args, 16, None) == -5
+    args[9] = None
+    assert lib.ttt_attn_bwd_sweep(ctypes.byref(p), *args, 1 << 40, None) == -1
+    # a separate-suffix forward sweep needs a workspace: a short one fails before launching
+    assert lib.ttt_attn_fwd_sweep(ctypes.byref(sep), *([good] * 7), 16, None) == -5
