@@ -41,15 +41,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // Row of the 32x32 accumulator that element i of lane-half h holds.
 __device__ __forceinline__ constexpr int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
-// Within each group of 16 positions along a contraction axis, the accumulator of a
-// 32x32 tile hands element j of lane-half h (k-chunk c) the logical index
-// 16c + 8*(j/4) + 4h + j%4.  Operands staged in memory along that axis are stored with
-// bits 2 and 3 of the in-group index swapped, so that lane-half h finds its 8 values
-// contiguous at 16c + 8h.  The map is its own inverse.
-__device__ __forceinline__ constexpr int swap23(int x) {
-  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -224,43 +215,6 @@ __device__ __forceinline__ void load_tile(const bf16* g, int ld, bf16* lds, int 
     asm volatile("" : "+v"(off));  // keeps the 32-bit offset form (no 64-bit copies to hold)
     g2lds16(base + off, lds + i * 512);
   }
-}
-
-// Buffer descriptor over `bytes` bytes at `base` (raw buffer: no stride, no format; reads past
-// the end return zero).  The address stays in scalar registers, so a copy costs each lane only
-// a 32-bit offset.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-// Asynchronous buffer -> LDS copy of 16 (or 4) bytes per lane: lane l writes lds_base +
-// SIZE * l from byte voff + soff of the buffer.
-template <int SIZE>
-__device__ __forceinline__ void buf2lds(__amdgpu_buffer_rsrc_t r, void* lds_base, unsigned voff, int soff) {
-  static_assert(SIZE == 16 || SIZE == 4, "copy size");
-  if constexpr (SIZE == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                             voff, soff, 0, 0);
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4,
-                                             voff, soff, 0, 0);
-}
-
-// Per-lane byte offset used by load_tile_buf (depends on the lane and on wave % 4 only).
-__device__ __forceinline__ unsigned tile_lane_offset(int wave, int lane) {
-  const int rl = lane >> 4;
-  return (unsigned)(rl * 128 + (((lane & 15) ^ ((rl << 2) | (wave & 3))) << 3)) * 2u;
-}
-
-// load_tile for a [NROWS][128] bf16 block starting at `g`, through a buffer descriptor: the
-// same swizzled layout, each wave instruction moving 4 rows (1 KB).  `lane_off` comes from
-// tile_lane_offset(wave, lane).
-template <int NROWS, int NWAVES>
-__device__ __forceinline__ void load_tile_buf(const bf16* g, bf16* lds, int wave, unsigned lane_off) {
-  static_assert(NWAVES % 4 == 0, "swizzle term must be constant per wave");
-  const __amdgpu_buffer_rsrc_t r = buffer_rsrc(g, NROWS * 256);
-#pragma unroll
-  for (int i = wave; i < NROWS / 4; i += NWAVES) buf2lds<16>(r, lds + i * 512, lane_off, i * 1024);
 }
 
 // Index of the calling wave inside its workgroup, as a wave-uniform (scalar) value.
