@@ -9,6 +9,8 @@ launches kernels.
 
 value = unmasked TFLOP/s = sum over steps of 14 * d * |M| * B * Hq (4d forward + 10d backward
 per unmasked (query, key) pair) / step time.  tokens/s = B * Q_LEN / step time.
+pct_roofline = t_roof / step time, t_roof = causal flops at the bf16 matrix-core peak plus the
+suffix's marginal K/V bytes and the backward preprocessing bytes at the HBM peak.
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build measures one GPU.
 """
@@ -240,12 +242,18 @@ def main():
     if timing:
         A.timing_reset()
         A.timing_enable(True)
+    # events between the steps (on the stream every kernel is launched on) give the per-step
+    # spread; the value itself is the wall clock over all timed steps
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         one_step()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     kernels = {}
     if timing:
         A.timing_enable(False)
@@ -307,6 +315,16 @@ def main():
             gbs = b / (kstats["bwd_suffix"]["avg_ms"] / 1e3) / 1e9
             kstats["bwd_suffix"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
 
+    # % roofline of the whole sweep: the time the causal flops would take at the matrix-core
+    # peak, plus the suffix's marginal bytes (diagonal K/V rows read by the forward, read and
+    # their dK/dV written by the backward) and the backward preprocessing (read o and dO, write
+    # D) at the HBM peak, over the measured step time
+    live_kv_rows = int(sum(int(t) for t in T)) * w.Hkv
+    f_causal = sum(14 * w.d * causal for _ in steps)
+    b_suffix = sum(3 * live_kv_rows * k * 2 * w.d * 2 for k in steps)
+    b_pre = len(steps) * w.B * w.Hq * w.L * (2 * w.d * 2 + 4)
+    t_roof = f_causal / (PEAK_BF16_TFLOPS * 1e12) + (b_suffix + b_pre) / (PEAK_HBM_GBS * 1e9)
+
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
@@ -319,6 +337,10 @@ def main():
         "dq_mode": args.dq_mode, "suffix": args.suffix,
         "api": "sweep" if args.sweep else "per-step",
         "tokens_per_s": round(tokens, 1),
+        "pct_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof / sec, 4),
+                         "causal_flop": f_causal, "suffix_bytes": b_suffix, "preprocess_bytes": b_pre},
+        "step_ms": {"median": round(float(np.median(step_ms)), 4), "min": round(step_ms[0], 4),
+                    "max": round(step_ms[-1], 4)},
         "unmasked_flop_per_step": flops,
         "roofline": roofline,
         "kernels": kstats,
@@ -411,31 +433,43 @@ def cpu_baseline_loss(V):
             "sample": f"loss and gradient of {rows} rows x {V} columns"}
 
 
+CPU_SAMPLE_SECONDS = 25.0
+
+
 def cpu_baseline(w, T, steps):
     """The CPU oracle (fp64 NumPy, dense masked) on a bounded sample of the same workload:
-    forward + backward of one KV group (all of its query heads) of sequence 0 at the last TTT
-    step.  Reported in the same unit (unmasked TFLOP/s over the sample's own pairs)."""
+    forward + backward of one KV group (all of its query heads) of sequence 0 at TTT steps
+    0, 1, 2, ... in order, stopping after the step during which the elapsed time passes
+    CPU_SAMPLE_SECONDS.  Reported in the same unit (unmasked TFLOP/s over the sample's own
+    pairs)."""
     from masked_attention_eagle_amd import inputs
     from oracle import ttt_oracle as O
-    k = steps[-1]
     G = w.Hq // w.Hkv
-    q = inputs.q_at(w, k)[0:1, 0:G]
-    kk, vv = inputs.kv_stack(w, k)
-    kk, vv = kk[0:1, 0:1], vv[0:1, 0:1]
-    do = inputs.do_at(w, k)[0:1, 0:G]
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    o, _ = O.forward(q, kk, vv, T[0:1], w.scale)
-    O.backward(q, kk, vv, T[0:1], w.scale, do, o)
-    sec = time.perf_counter() - t0
-    flops = 14 * w.d * total_pairs(w.L, k, int(T[0])) * G
+    sec, flops, done, ks, vs = 0.0, 0, [], [], []
+    for k in steps:
+        q = inputs.q_at(w, k)[0:1, 0:G]
+        kb, vb = inputs.kv_block(w, k)  # block k of the cache, KV group 0 of sequence 0
+        ks.append(kb[0:1, 0:1])
+        vs.append(vb[0:1, 0:1])
+        kk, vv = np.concatenate(ks, axis=2), np.concatenate(vs, axis=2)
+        do = inputs.do_at(w, k)[0:1, 0:G]
+        t0 = time.perf_counter()
+        o, _ = O.forward(q, kk, vv, T[0:1], w.scale)
+        O.backward(q, kk, vv, T[0:1], w.scale, do, o)
+        sec += time.perf_counter() - t0
+        flops += 14 * w.d * total_pairs(w.L, k, int(T[0])) * G
+        done.append(k)
+        if sec > CPU_SAMPLE_SECONDS:
+            break
     return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": round(sec, 2),
-            "sample": f"fwd+bwd of KV group 0 ({G} query heads) of sequence 0 at TTT step {k}"}
+            "sample": f"fwd+bwd of KV group 0 ({G} query heads) of sequence 0 at TTT steps "
+                      f"{done[0]}..{done[-1]}"}
 
 
 if __name__ == "__main__":
