@@ -133,10 +133,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const int nq = (s.L - q_first) / KBM;
     const int total = nq * hpg;
 
-    auto issue = [&](int it, bf16* dQ, bf16* dOt, float* dLD) {
-      const int h = h_begin + it / nq;
-      const int q0 = q_first + (it % nq) * KBM;
-      const size_t row0 = ((size_t)b * s.Hq + h) * s.L + q0;
+    // Tile `it` is (head h_begin + it / nq, query rows q_first + (it % nq) * KBM ..); the loop
+    // carries that position and steps it without dividing.
+    struct Pos {
+      int h, q0;
+      size_t row0;   // (b * Hq + h) * L + q0
+      size_t dsrow;  // dS block index of (head h, query block q0 / 32, key block 0)
+    };
+    auto make_pos = [&](int h, int q0) -> Pos {
+      const int bh = b * s.Hq + h;
+      return Pos{h, q0, (size_t)bh * s.L + q0, ds_block_index(s, bh, q0 / 32, 0)};
+    };
+    auto next_pos = [&](Pos p) -> Pos {
+      if (p.q0 + KBM >= s.L) return make_pos(p.h + 1, q_first);
+      p.dsrow += p.q0 / 32 + 1;  // query block r holds r + 1 key blocks
+      p.q0 += KBM;
+      p.row0 += KBM;
+      return p;
+    };
+    auto issue = [&](Pos p, bf16* dQ, bf16* dOt, float* dLD) {
+      const size_t row0 = p.row0;
       load_tile<KBM, 4>(q + row0 * BD, BD, dQ, wave, lane);
       load_tile<KBM, 4>(dO + row0 * BD, BD, dOt, wave, lane);
       if (wave == 0) {  // lse of the 32 rows to dLD[0, 32), D to dLD[32, 64)
@@ -149,12 +165,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
       }
     };
 
-    auto body = [&](int it, const bf16* cQ, const bf16* cO, const float* cLD, bf16* nQ, bf16* nO,
-                    float* nLD) {
+    auto body = [&](int it, Pos p, const bf16* cQ, const bf16* cO, const float* cLD, bf16* nQ,
+                    bf16* nO, float* nLD) {
       const FragOffsets fl = opaque(fo);
-      const int q0 = q_first + (it % nq) * KBM;
+      const int q0 = p.q0;
       const bool live = kw < T && q0 + KBM - 1 >= kw;
-      if (!live && it + 1 < total) issue(it + 1, nQ, nO, nLD);
+      if (!live && it + 1 < total) issue(next_pos(p), nQ, nO, nLD);
       if (live) {
         // S, then P (kept in bf16 only), then dP: one accumulator tile live at a time.  The
         // next tile's copy is issued after the S products, so that nothing waited for before
@@ -162,10 +178,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc = mfma32(frag_row(cQ, 0, t, fl), kf[t], acc);
-        if (it + 1 < total) issue(it + 1, nQ, nO, nLD);
+        if (it + 1 < total) issue(next_pos(p), nQ, nO, nLD);
         const bool full = (kw + 31 <= q0) && (kw + 32 <= T);
-        // key > query row q0 + acc_row(i, hi)  <=>  dkey > 8 * (i / 4) + i % 4 (a constant)
-        const int dkey = my_key >= T ? KBM : my_key - q0 - 4 * hi;
+        // key > query row q0 + acc_row(i, hi)  <=>  dkey > 8 * (i / 4) + i % 4 (a constant);
+        // on full tiles dkey is below every such constant, so no element is masked
+        const int dkey = full ? -KBM : (my_key >= T ? KBM : my_key - q0 - 4 * hi);
         bf16x8 pb[2], dsb[2];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
@@ -174,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
             float pv = exp2_fast(__builtin_fmaf(acc[i], c2, -L4[e] * kLog2e));
-            if (!full && dkey > 8 * i4 + e) pv = 0.f;
+            if (dkey > 8 * i4 + e) pv = 0.f;
             pb[i >> 3][i & 7] = (bf16)pv;
           }
         }
@@ -192,8 +209,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
           }
         }
         if (ds_out) {  // hand dS to the dQ kernel (layout: ds_store_offset)
-          const int h = h_begin + it / nq;
-          const size_t blk = ds_block_index(s, b * s.Hq + h, q0 / 32, kw / 32);
+          const size_t blk = p.dsrow + kw / 32;
           void* dst = const_cast<void*>(uniform_ptr(ds_out + blk * 1024));
           unsigned off0 = ds_store_offset(lane, 0), off1 = ds_store_offset(lane, 1);
           asm volatile("" : "+v"(off0), "+v"(off1));
@@ -218,12 +234,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
       __syncthreads();
     };
 
-    if (total > 0) issue(0, sQ0, sO0, sLD0);
+    Pos pos = make_pos(h_begin, q_first);
+    if (total > 0) issue(pos, sQ0, sO0, sLD0);
     wait_vmem();
     __syncthreads();
     for (int it = 0; it < total; it += 2) {
-      body(it, sQ0, sO0, sLD0, sQ1, sO1, sLD1);
-      if (it + 1 < total) body(it + 1, sQ1, sO1, sLD1, sQ0, sO0, sLD0);
+      body(it, pos, sQ0, sO0, sLD0, sQ1, sO1, sLD1);
+      pos = next_pos(pos);
+      if (it + 1 < total) body(it + 1, pos, sQ1, sO1, sLD1, sQ0, sO0, sLD0);
+      pos = next_pos(pos);
     }
 
     // lane owns d = 32u + l32 of key rows kw + acc_row(i, hi).  The lane index goes through

@@ -121,13 +121,14 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
           }
         }
       } else if (!full) {
+        // key > my_q or key >= T  <=>  key > min(my_q, T - 1); with key = k0 + 32 st +
+        // acc_row(i, hi) that is a compile-time constant against one per-lane value
+        const int lim = min(my_q, T - 1) - k0 - 4 * hi;
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + st * 32 + acc_row(i, hi);
-            if (key > my_q || key >= T) sacc[st][i] = kNegInf;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (st * 32 + acc_row(i, 0) > lim) sacc[st][i] = kNegInf;
         }
       }
       float rmax = fmaxf(sacc[0][0], sacc[1][0]);
