@@ -41,6 +41,23 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // Row of the 32x32 accumulator that element i of lane-half h holds.
 __device__ __forceinline__ constexpr int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
+// Element j of a bf16x8 as fp32 (exact): the bf16 is the high half of the fp32 pattern, so
+// each packed pair gives its two values with one shift and one mask.
+__device__ __forceinline__ float bf16x8_elem_f32(const bf16x8& x, int j) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = __builtin_bit_cast(u32x4, x);
+  const unsigned word = w[j >> 1];
+  return __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
+}
+
+// Elements off .. off + 7 of an accumulator, rounded to bf16 in pairs.
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& a, int off) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  const f32x8 x = {a[off], a[off + 1], a[off + 2], a[off + 3],
+                   a[off + 4], a[off + 5], a[off + 6], a[off + 7]};
+  return __builtin_convertvector(x, bf16x8);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));

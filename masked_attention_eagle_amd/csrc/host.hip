@@ -150,12 +150,12 @@ FwdLayout fwd_layout(const Shape& s, bool fused) {
 }
 
 struct BwdLayout {
-  size_t Dd = 0, part = 0, ds = 0, dqacc = 0, total = 0;
+  size_t Dd = 0, lse2 = 0, part = 0, ds = 0, dqacc = 0, total = 0;
   int nsplit = 1;
 };
-// D; split dK/dV partials (bf16, heads of a group over several workgroups); the dS blocks of
-// block 0 when the dQ kernel reads them; for k > 0 the fp32 dQ accumulator that the suffix
-// kernel finalises.
+// D; (bf16) lse * log2(e) for the dK/dV kernel and the split dK/dV partials (heads of a group
+// over several workgroups); the dS blocks of block 0 when the dQ kernel reads them; for k > 0
+// the fp32 dQ accumulator that the suffix kernel finalises.
 BwdLayout bwd_layout(const Shape& s, int dtype, bool with_ds) {
   BwdLayout w;
   const size_t rows_q = (size_t)s.B * s.Hq * s.L;
@@ -163,6 +163,8 @@ BwdLayout bwd_layout(const Shape& s, int dtype, bool with_ds) {
   w.Dd = off;
   off += round_up(rows_q * 4);
   if (dtype == TTT_DTYPE_BF16) {
+    w.lse2 = off;
+    off += round_up(rows_q * 4);
     w.nsplit = dkdv_nsplit(s);
     if (w.nsplit > 1) {
       w.part = off;
@@ -273,8 +275,10 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     float* part = w.nsplit > 1 ? (float*)(ws + w.part) : nullptr;
     bf16* dsb = with_ds ? (bf16*)(ws + w.ds) : nullptr;
     void* dq_causal = final_causal ? dq : (void*)dqacc;
-    if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, st)) != hipSuccess) return TTT_E_HIP;
-    if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
+    float* lse2 = (float*)(ws + w.lse2);
+    if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, lse, lse2, st)) != hipSuccess)
+      return TTT_E_HIP;
+    if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, dob, lse2, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
                                   w.nsplit, dsb, ga, st)) != hipSuccess)
       return TTT_E_HIP;
     if (w.nsplit > 1 &&
@@ -293,7 +297,8 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     const float* kf = (const float*)k;
     const float* vf = (const float*)v;
     const float* dof = (const float*)dout;
-    if ((e = launch_bwd_rowdot<float>(s, (const float*)o, dof, Dd, st)) != hipSuccess) return TTT_E_HIP;
+    if ((e = launch_bwd_rowdot<float>(s, (const float*)o, dof, Dd, nullptr, nullptr, st)) != hipSuccess)
+      return TTT_E_HIP;
     if ((e = launch_bwd_dkdv_valu<float>(s, qf, kf, vf, dof, lse, Dd, seq_T, (float*)dk,
                                          (float*)dv, st)) != hipSuccess)
       return TTT_E_HIP;

@@ -5,12 +5,16 @@ namespace ttt {
 
 // ----------------------------------------------------------------------------------------
 // D_i = sum_d dO_i * O_i, the row term of the softmax Jacobian (dS = P * (dP - D)).
-// 16 lanes per row.
+// 16 lanes per row.  With lse2 set it also writes lse_i * log2(e), the base-2 row offset of
+// P = exp2(S * scale * log2(e) - lse * log2(e)), so that the matrix-core dK/dV kernel, whose
+// lanes each meet 16 rows per tile, subtracts it without a multiply per element.
 // ----------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ o,
                                                      const T* __restrict__ dout,
-                                                     float* __restrict__ Dd, size_t nrows) {
+                                                     float* __restrict__ Dd,
+                                                     const float* __restrict__ lse,
+                                                     float* __restrict__ lse2, size_t nrows) {
   constexpr int E = D / 16;
   const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
@@ -22,23 +26,27 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ o,
 #pragma unroll
   for (int e = 0; e < E; ++e) acc += a[e] * c[e];
   acc = sum16(acc);
-  if (sub == 0) Dd[row] = acc;
+  if (sub == 0) {
+    Dd[row] = acc;
+    if (lse2) lse2[row] = lse[row] * kLog2e;
+  }
 }
 
 template <typename T>
-hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* Dd, hipStream_t st) {
+hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* Dd,
+                             const float* lse, float* lse2, hipStream_t st) {
   const size_t nrows = (size_t)s.B * s.Hq * s.L;
   const dim3 grid((unsigned)((nrows + 15) / 16));
   LaunchTimer timer("bwd_rowdot", st);
   if (s.D == 64)
-    rowdot_kernel<T, 64><<<grid, 256, 0, st>>>(o, dout, Dd, nrows);
+    rowdot_kernel<T, 64><<<grid, 256, 0, st>>>(o, dout, Dd, lse, lse2, nrows);
   else
-    rowdot_kernel<T, 128><<<grid, 256, 0, st>>>(o, dout, Dd, nrows);
+    rowdot_kernel<T, 128><<<grid, 256, 0, st>>>(o, dout, Dd, lse, lse2, nrows);
   return hipGetLastError();
 }
 template hipError_t launch_bwd_rowdot<float>(const Shape&, const float*, const float*, float*,
-                                             hipStream_t);
+                                             const float*, float*, hipStream_t);
 template hipError_t launch_bwd_rowdot<bf16>(const Shape&, const bf16*, const bf16*, float*,
-                                            hipStream_t);
+                                            const float*, float*, hipStream_t);
 
 }  // namespace ttt

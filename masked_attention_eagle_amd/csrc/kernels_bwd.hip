@@ -21,7 +21,7 @@ constexpr int BD = 128;  // head dim of the matrix-core path
 // held in registers and V in LDS; query tiles of 32 rows (of every query head of the group
 // that sees the keys) stream through LDS.  Per wave and tile:
 //   S  = Q K^T,  dP = dO V^T          (M = queries, N = the wave's 32 keys; A = Q / dO rows)
-//   P  = exp2(S * scale*log2e - lse*log2e), dS = P * (dP - D)
+//   P  = exp2(S * scale*log2e - lse*log2e), dS = P * (dP - D)   (lse*log2e precomputed)
 //   dV += P^T dO,  dK += dS^T Q       (A operands straight from the S/dP accumulators,
 //                                      B = dO / Q columns through transposing LDS reads)
 // With nsplit > 1 the query heads of a group are split over nsplit workgroups that write
@@ -83,13 +83,13 @@ __device__ __forceinline__ unsigned ds_read_offset(int lane, int c, int r) {
 // (p, n - 1 - p) of key tiles, which makes every workgroup's work equal.
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
+    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, bf16* __restrict__ dk, bf16* __restrict__ dv,
     float* __restrict__ part, int nsplit, bf16* __restrict__ ds_out, GradAcc ga, Shape s) {
   // Two stages in distinct arrays (the copy into one never stalls reads of the other).
   __shared__ __attribute__((aligned(1024))) bf16 sQ0[KBM * BD];
   __shared__ __attribute__((aligned(1024))) bf16 sO0[KBM * BD];
-  __shared__ __attribute__((aligned(256))) float sLD0[2 * KBM];  // lse (natural log), then D
+  __shared__ __attribute__((aligned(256))) float sLD0[2 * KBM];  // lse * log2(e), then D
   __shared__ __attribute__((aligned(1024))) bf16 sQ1[KBM * BD];
   __shared__ __attribute__((aligned(1024))) bf16 sO1[KBM * BD];
   __shared__ __attribute__((aligned(256))) float sLD1[2 * KBM];
@@ -155,11 +155,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
       const size_t row0 = p.row0;
       load_tile<KBM, 4>(q + row0 * BD, BD, dQ, wave, lane);
       load_tile<KBM, 4>(dO + row0 * BD, BD, dOt, wave, lane);
-      if (wave == 0) {  // lse of the 32 rows to dLD[0, 32), D to dLD[32, 64)
+      if (wave == 0) {  // lse * log2(e) of the 32 rows to dLD[0, 32), D to dLD[32, 64)
         unsigned off = 4u * (lane & (KBM - 1));
         asm volatile("" : "+v"(off));
         if (lane < KBM)
-          g2lds4(reinterpret_cast<const char*>(uniform_ptr(lse + row0)) + off, dLD);
+          g2lds4(reinterpret_cast<const char*>(uniform_ptr(lse2 + row0)) + off, dLD);
         else
           g2lds4(reinterpret_cast<const char*>(uniform_ptr(Dd + row0)) + off, dLD);
       }
@@ -179,35 +179,42 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc = mfma32(frag_row(cQ, 0, t, fl), kf[t], acc);
         if (it + 1 < total) issue(next_pos(p), nQ, nO, nLD);
-        const bool full = (kw + 31 <= q0) && (kw + 32 <= T);
-        // key > query row q0 + acc_row(i, hi)  <=>  dkey > 8 * (i / 4) + i % 4 (a constant);
-        // on full tiles dkey is below every such constant, so no element is masked
-        const int dkey = full ? -KBM : (my_key >= T ? KBM : my_key - q0 - 4 * hi);
-        bf16x8 pb[2], dsb[2];
+        // P in place of S (the row offsets arrive as lse * log2(e)); only tiles that straddle
+        // the diagonal or the T edge (a wave-uniform test) evaluate the mask:
+        // key > query row q0 + acc_row(i, hi)  <=>  dkey > acc_row(i, 0) (a constant)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const f32x4 L4 = *reinterpret_cast<const f32x4*>(&cLD[8 * i4 + 4 * hi]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            float pv = exp2_fast(__builtin_fmaf(acc[i], c2, -L4[e] * kLog2e));
-            if (dkey > 8 * i4 + e) pv = 0.f;
-            pb[i >> 3][i & 7] = (bf16)pv;
-          }
+          for (int e = 0; e < 4; ++e)
+            acc[4 * i4 + e] = exp2_fast(__builtin_fmaf(acc[4 * i4 + e], c2, -L4[e]));
         }
+        const bool full = (kw + 31 <= q0) && (kw + 32 <= T);
+        if (!full) {
+          const int dkey = my_key >= T ? KBM : my_key - q0 - 4 * hi;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (dkey > acc_row(i, 0)) acc[i] = 0.f;
+        }
+        bf16x8 pb[2], dsb[2];
+        pb[0] = to_bf16x8(acc, 0);
+        pb[1] = to_bf16x8(acc, 8);
         acc = f32x16{};
 #pragma unroll
         for (int t = 0; t < 8; ++t)
           acc = mfma32(frag_row(cO, 0, t, fl), vf[t], acc);
+        // dS from the bf16 P that the dV product uses
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const f32x4 D4 = *reinterpret_cast<const f32x4*>(&cLD[KBM + 8 * i4 + 4 * hi]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
-            dsb[i >> 3][i & 7] = (bf16)((float)pb[i >> 3][i & 7] * (acc[i] - D4[e]));
+            acc[i] = bf16x8_elem_f32(pb[i >> 3], i & 7) * (acc[i] - D4[e]);
           }
         }
+        dsb[0] = to_bf16x8(acc, 0);
+        dsb[1] = to_bf16x8(acc, 8);
         if (ds_out) {  // hand dS to the dQ kernel (layout: ds_store_offset)
           const size_t blk = p.dsrow + kw / 32;
           void* dst = const_cast<void*>(uniform_ptr(ds_out + blk * 1024));
@@ -294,12 +301,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
 }
 
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
-                                const bf16* dout, const float* lse, const float* Dd,
+                                const bf16* dout, const float* lse2, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
                                 int nsplit, bf16* ds_out, GradAcc ga, hipStream_t st) {
   const dim3 grid(s.B * s.Hkv * nsplit * ((s.L / KBN + 1) / 2));
   LaunchTimer timer("bwd_dkdv_mfma", st);
-  bwd_dkdv_mfma_kernel<<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dk, dv, part, nsplit,
+  bwd_dkdv_mfma_kernel<<<grid, 256, 0, st>>>(q, k, v, dout, lse2, Dd, seq_T, dk, dv, part, nsplit,
                                              ds_out, ga, s);
   return hipGetLastError();
 }

@@ -43,10 +43,13 @@ struct GradAcc {
 };
 
 // Backward.
+// D = rowsum(dout * o); with lse2 set also lse2 = lse * log2(e).
 template <typename T>
-hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* Dd, hipStream_t st);
+hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* Dd,
+                             const float* lse, float* lse2, hipStream_t st);
+// lse2 = lse * log2(e) (from launch_bwd_rowdot).
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
-                                const bf16* dout, const float* lse, const float* Dd,
+                                const bf16* dout, const float* lse2, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
                                 int nsplit, bf16* ds_out, GradAcc ga, hipStream_t st);
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,

@@ -78,9 +78,10 @@ def test_workspace_sizes():
     assert A.fwd_workspace_size(P(flags=sep, step=0)) == 0
     assert A.fwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, step=0)) == 0
     assert A.fwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, L=4000)) == 2 * 32 * 4000 * (d * 4 + 4)
-    # D rows + fp32 dQ accumulator for step > 0 + fp32 dK/dV partial planes: each workgroup
-    # of the dK/dV kernel owns a pair of 128-key tiles, so 2 x 8 x 16 = 256 workgroups double
-    # to 512 by splitting each KV group's 4 query heads in two.
+    # D and lse * log2(e) rows (fp32 each) + fp32 dQ accumulator for step > 0 + fp32 dK/dV
+    # partial planes: each workgroup of the dK/dV kernel owns a pair of 128-key tiles, so
+    # 2 x 8 x 16 = 256 workgroups double to 512 by splitting each KV group's 4 query heads
+    # in two.
     part = 2 * 2 * B * Hkv * L * d * 4
     dqacc = rows * d * 4
     # bf16 default: dS blocks of block 0 (n(n+1)/2 blocks of 32 x 32 per head, n = L / 32)
@@ -90,20 +91,20 @@ def test_workspace_sizes():
         n = L // 32
         return B * Hq * n * (n + 1) // 2 * 32 * 32 * 2
     sep, rec = A.TTT_FLAG_SEPARATE_SUFFIX, A.TTT_FLAG_RECOMPUTE_DQ
-    assert A.bwd_workspace_size(p) == rows * 4 + part + ds_bytes(B, Hq, L) + dqacc
+    assert A.bwd_workspace_size(p) == rows * 8 + part + ds_bytes(B, Hq, L) + dqacc
     assert A.bwd_workspace_size(P(flags=sep)) == A.bwd_workspace_size(p)
-    assert A.bwd_workspace_size(P(step=0)) == rows * 4 + part + ds_bytes(B, Hq, L)
+    assert A.bwd_workspace_size(P(step=0)) == rows * 8 + part + ds_bytes(B, Hq, L)
     # recomputing dQ kernel: no dS blocks
-    assert A.bwd_workspace_size(P(flags=rec)) == rows * 4 + part + dqacc
-    assert A.bwd_workspace_size(P(flags=rec | sep)) == rows * 4 + part + dqacc
-    assert A.bwd_workspace_size(P(flags=rec, step=0)) == rows * 4 + part
+    assert A.bwd_workspace_size(P(flags=rec)) == rows * 8 + part + dqacc
+    assert A.bwd_workspace_size(P(flags=rec | sep)) == rows * 8 + part + dqacc
+    assert A.bwd_workspace_size(P(flags=rec, step=0)) == rows * 8 + part
     # 1 x 8 x 16 = 128 pair workgroups: heads split in four
     rows4 = 64 * L
-    assert A.bwd_workspace_size(P(B=1, Hq=64, flags=rec)) == rows4 * 4 + rows4 * d * 4 + 4 * 2 * 8 * L * d * 4
+    assert A.bwd_workspace_size(P(B=1, Hq=64, flags=rec)) == rows4 * 8 + rows4 * d * 4 + 4 * 2 * 8 * L * d * 4
     # 8 x 8 x 8 = 512 already: no split, no partials
     rows3 = 8 * 32 * 2048
-    assert A.bwd_workspace_size(P(B=8, L=2048, flags=rec)) == rows3 * 4 + rows3 * d * 4
-    assert A.bwd_workspace_size(P(B=8, L=2048)) == rows3 * 4 + ds_bytes(8, 32, 2048) + rows3 * d * 4
+    assert A.bwd_workspace_size(P(B=8, L=2048, flags=rec)) == rows3 * 8 + rows3 * d * 4
+    assert A.bwd_workspace_size(P(B=8, L=2048)) == rows3 * 8 + ds_bytes(8, 32, 2048) + rows3 * d * 4
     # fp32 (vector-ALU path): flags ignored; D + dQ accumulator
     rowsf = 2 * 32 * 4000
     for f in (0, sep, rec):
