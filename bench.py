@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload number (2: the 8B draft layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra measurement of the step captured in a HIP graph")
     ap.add_argument("--suffix", choices=("fused", "separate", "dense"), default="fused",
                     help="forward: diagonal keys merged inside the causal kernel, the standalone "
                          "suffix kernel, or (measurement variant) masked diagonal matrix-core tiles")
@@ -134,18 +136,18 @@ def sweep_step(args, w, T, blocks, lib, A, dev, t_setup):
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
-    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     fa = (ctypes.byref(p), qa.data_ptr(), kc.data_ptr(), vc.data_ptr(), Td.data_ptr(),
-          oa.data_ptr(), la.data_ptr(), ws.data_ptr(), nb, sp)
+          oa.data_ptr(), la.data_ptr(), ws.data_ptr(), nb)
     ba = (ctypes.byref(p), qa.data_ptr(), kc.data_ptr(), vc.data_ptr(), Td.data_ptr(),
           oa.data_ptr(), la.data_ptr(), da.data_ptr(), dqa.data_ptr(), dkc.data_ptr(),
-          dvc.data_ptr(), ws.data_ptr(), nb, sp)
+          dvc.data_ptr(), ws.data_ptr(), nb)
     keep = (kc, vc, qa, da, Td, oa, la, dqa, dkc, dvc, ws, p)
 
     def one_step():
         _ = keep
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # the caller's stream
         for fn, a in ((lib.ttt_attn_fwd_sweep, fa), (lib.ttt_attn_bwd_sweep, ba)):
-            rc = fn(*a)
+            rc = fn(*a, sp)
             if rc:
                 raise A.TTTError(rc, A.status_string(rc))
     return one_step, setup_s
@@ -213,23 +215,22 @@ def main():
         torch.cuda.synchronize()
         setup_s = time.time() - t_setup
 
-        stream = torch.cuda.current_stream()
-        sp = ctypes.c_void_p(stream.cuda_stream)
         fwd_args = [(ctypes.byref(params[i]), qs[i].data_ptr(), kv[i][0].data_ptr(), kv[i][1].data_ptr(),
-                     Td.data_ptr(), os_[i].data_ptr(), lses[i].data_ptr(), ws.data_ptr(), ws_bytes, sp)
+                     Td.data_ptr(), os_[i].data_ptr(), lses[i].data_ptr(), ws.data_ptr(), ws_bytes)
                     for i in range(K)]
         bwd_args = [(ctypes.byref(params[i]), qs[i].data_ptr(), kv[i][0].data_ptr(), kv[i][1].data_ptr(),
                      Td.data_ptr(), os_[i].data_ptr(), lses[i].data_ptr(), dos[i].data_ptr(),
-                     dqs[i].data_ptr(), dks[i].data_ptr(), dvs[i].data_ptr(), ws.data_ptr(), ws_bytes, sp)
+                     dqs[i].data_ptr(), dks[i].data_ptr(), dvs[i].data_ptr(), ws.data_ptr(), ws_bytes)
                     for i in range(K)]
 
         def one_step():
+            sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # the caller's stream
             for i in range(K):
-                rc = lib.ttt_attn_fwd(*fwd_args[i])
+                rc = lib.ttt_attn_fwd(*fwd_args[i], sp)
                 if rc:
                     raise A.TTTError(rc, A.status_string(rc))
             for i in reversed(range(K)):
-                rc = lib.ttt_attn_bwd(*bwd_args[i])
+                rc = lib.ttt_attn_bwd(*bwd_args[i], sp)
                 if rc:
                     raise A.TTTError(rc, A.status_string(rc))
 
@@ -259,6 +260,29 @@ def main():
         A.timing_enable(False)
         kernels = A.timing_read()
     sec = (t1 - t0) / args.steps
+
+    # the same step captured once in a HIP graph and replayed (launch gaps removed); reported
+    # beside the eager figure, which stays the headline because its kernels are timed
+    graph_sec = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            one_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_sec = (time.perf_counter() - g0) / args.steps
+        del graph
 
     # ---------------------------------------------------------------- accounting
     pairs_step = [sum(total_pairs(w.L, k, int(t)) for t in T) * w.Hq for k in steps]
@@ -341,6 +365,9 @@ def main():
                          "causal_flop": f_causal, "suffix_bytes": b_suffix, "preprocess_bytes": b_pre},
         "step_ms": {"median": round(float(np.median(step_ms)), 4), "min": round(step_ms[0], 4),
                     "max": round(step_ms[-1], 4)},
+        "graph_replay": None if graph_sec is None else {
+            "ms_per_step": round(graph_sec * 1e3, 4), "value": round(flops / graph_sec / 1e12, 2),
+            "tokens_per_s": round(w.B * w.L / graph_sec, 1)},
         "unmasked_flop_per_step": flops,
         "roofline": roofline,
         "kernels": kstats,
