@@ -44,20 +44,30 @@ def kernel_source(name: str) -> str:
     return "kernels_aux.hip" if name == "bwd_rowdot" else "kernels_bwd.hip"
 
 
+def source_digest(files) -> str:
+    """sha256 (16 hex digits) of the code in the given csrc files with comments and white space
+    removed, so that the digest moves with the compiled code and not with its comments."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for fn in files:
+        with open(os.path.join(CSRC, fn)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(config: int, name: str):
     """HBM bytes per launch of kernel `name` from the committed counter summary, or None when
-    there is none for this workload or the kernel's source has changed since."""
-    import hashlib
+    there is none for this workload or the kernel's code has changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             entry = json.load(f)[TRAFFIC_TAG[config]]["kernels"][name]
     except (OSError, KeyError, ValueError):
         return None
-    h = hashlib.sha256()
-    for fn in (kernel_source(name), "common.cuh"):
-        with open(os.path.join(CSRC, fn), "rb") as f:
-            h.update(f.read())
-    if h.hexdigest()[:16] != entry.get("source_sha256_16"):
+    if source_digest((kernel_source(name), "common.cuh")) != entry.get("code_digest"):
         return None
     return int(entry["bytes_per_launch"])
 
@@ -432,12 +442,9 @@ def measured_traffic_loss(name):
             entry = json.load(f)["lmhead"]["kernels"][name]
     except (OSError, KeyError, ValueError):
         return None
-    import hashlib
-    h = hashlib.sha256()
-    for fn in ("kernels_loss.hip", "common.cuh"):
-        with open(os.path.join(CSRC, fn), "rb") as f:
-            h.update(f.read())
-    return int(entry["bytes_per_launch"]) if h.hexdigest()[:16] == entry.get("source_sha256_16") else None
+    if source_digest(("kernels_loss.hip", "common.cuh")) != entry.get("code_digest"):
+        return None
+    return int(entry["bytes_per_launch"])
 
 
 def cpu_baseline_loss(V):

@@ -17,8 +17,8 @@ namespace ttt {
 constexpr int BD = 128;  // head dim of the matrix-core path
 
 // ----------------------------------------------------------------------------------------
-// dK, dV of block 0, bf16 MFMA.  Workgroup = 4 waves x 32 keys = 128 keys; K of its keys is
-// held in registers and V in LDS; query tiles of 32 rows (of every query head of the group
+// dK, dV of block 0, bf16 MFMA.  Workgroup = 4 waves x 32 keys = 128 keys; K and V of each
+// wave's keys are held in registers; query tiles of 32 rows (of every query head of the group
 // that sees the keys) stream through LDS.  Per wave and tile:
 //   S  = Q K^T,  dP = dO V^T          (M = queries, N = the wave's 32 keys; A = Q / dO rows)
 //   P  = exp2(S * scale*log2e - lse*log2e), dS = P * (dP - D)   (lse*log2e precomputed)
