@@ -50,6 +50,12 @@ __device__ __forceinline__ float bf16x8_elem_f32(const bf16x8& x, int j) {
   return __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
 }
 
+// Elements 2j, 2j + 1 of a bf16x8 (one 32-bit register of it).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2 bf16x8_pair(const bf16x8& x, int j) {
+  return bf16x2{x[2 * j], x[2 * j + 1]};
+}
+
 // Elements off .. off + 7 of an accumulator, rounded to bf16 in pairs.
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& a, int off) {
   typedef float f32x8 __attribute__((ext_vector_type(8)));

@@ -220,24 +220,35 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4)
           vv[4 * u + b4] = *reinterpret_cast<const bf16x4*>(vr + off + 32 * u + 8 * b4);
+      // q.k over the lane's 64 elements: packed bf16 pairs, products exact, fp32 sums
       float dot = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot = __builtin_fmaf((float)qf[c][e], (float)kk[c][e], dot);
+        for (int e2 = 0; e2 < 4; ++e2)
+          dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x8_pair(qf[c], e2), bf16x8_pair(kk[c], e2),
+                                                dot, false);
       dot = half_sum(dot);
-      const float m_new = fmaxf(m, dot);
-      const float alpha = exp2_fast((m - m_new) * c2);  // 0 while m = -inf
-      const float p = exp2_fast((dot - m_new) * c2);
-      l = l * alpha + p;
+      // the same lazy rescaling as the tiles below: m moves only when the logit exceeds it by
+      // more than kRescaleLog2 (base 2), always on the first key (m = -inf)
+      const bool grow = dot * c2 > m * c2 + kRescaleLog2;
+      if (__any(grow)) {
+        const float m_new = grow ? dot : m;
+        const float alpha = grow ? exp2_fast((m - m_new) * c2) : 1.f;  // 0 while m = -inf
+        l *= alpha;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] *= alpha;
+        m = m_new;
+      }
+      const float p = exp2_fast((dot - m) * c2);
+      l += p;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            acc[u][4 * b4 + e] = __builtin_fmaf(acc[u][4 * b4 + e], alpha, p * (float)vv[4 * u + b4][e]);
-      m = m_new;
+            acc[u][4 * b4 + e] = __builtin_fmaf(p, (float)vv[4 * u + b4][e], acc[u][4 * b4 + e]);
     }
   }
   wait_vmem();
