@@ -23,8 +23,9 @@ namespace ttt {
 // On partial tiles P is split into bf16 hi + lo parts so that rows with few keys (where one
 // rounding of P would show in O) keep fp32-level accuracy.
 // With FINAL and k > 0 the kernel also merges the suffix keys (one per block 1..k for rows
-// i < T) and writes the final o and lse; without FINAL it writes the fp32 causal state for
-// the standalone suffix kernel.
+// i < T; their K and V rows pass through the same LDS stages before the causal tiles) and
+// writes the final o and lse; without FINAL it writes the fp32 causal state for the
+// standalone suffix kernel.
 //
 // K and V tiles are copied global -> LDS without passing through registers (two stages),
 // which keeps the wave under 256 registers: two workgroups share a CU and the matrix cores
@@ -46,11 +47,14 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
     const int32_t* __restrict__ seq_T, void* __restrict__ o_out, float* __restrict__ lse_out,
     Shape s) {
   // Two stages in distinct arrays: the compiler can then tell the copy into one stage from
-  // the reads of the other and does not wait for the copy before computing.
-  __shared__ __attribute__((aligned(1024))) bf16 sK0[FBN * FD];
-  __shared__ __attribute__((aligned(1024))) bf16 sV0[FBN * FD];
-  __shared__ __attribute__((aligned(1024))) bf16 sK1[FBN * FD];
-  __shared__ __attribute__((aligned(1024))) bf16 sV1[FBN * FD];
+  // the reads of the other and does not wait for the copy before computing.  A stage holds a
+  // K tile and a V tile of 64 rows, or 128 rows of one suffix block (see below).
+  __shared__ __attribute__((aligned(1024))) bf16 sKV0[2 * FBN * FD];
+  __shared__ __attribute__((aligned(1024))) bf16 sKV1[2 * FBN * FD];
+  bf16* const sK0 = sKV0;
+  bf16* const sV0 = sKV0 + FBN * FD;
+  bf16* const sK1 = sKV1;
+  bf16* const sV1 = sKV1 + FBN * FD;
 
   const int n_qt = s.L / FBM;
   int bh, rank;
@@ -201,58 +205,81 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
     __syncthreads();
   };
 
-  if (ntiles > 0) issue(0, sK0, sV0);
-  if (FINAL && !DIAG && s.step > 0 && my_q < T) {
-    // Suffix keys t*Q_LEN + my_q (t = 1..k), merged before the causal tiles (the softmax
-    // state is order-independent) while tile 0 is in flight.  Each lane takes the same half
-    // of the K row as of q (d = 16c + 8*hi ..) and the same half of the V row as of O
-    // (d = 32u + 8*b4 + 4*hi ..); the logit is the sum over the lane pair.  P stays fp32.
-    const bf16* kr = kb + (size_t)my_q * FD + 8 * hi;
-    const bf16* vr = vb + (size_t)my_q * FD + 4 * hi;
-    for (int t = 1; t <= s.step; ++t) {
-      const size_t off = (size_t)t * s.L * FD;
-      bf16x8 kk[8];
-      bf16x4 vv[16];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) kk[c] = *reinterpret_cast<const bf16x8*>(kr + off + 16 * c);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4)
-          vv[4 * u + b4] = *reinterpret_cast<const bf16x4*>(vr + off + 32 * u + 8 * b4);
-      // q.k over the lane's 64 elements: packed bf16 pairs, products exact, fp32 sums
-      float dot = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x8_pair(qf[c], e2), bf16x8_pair(kk[c], e2),
-                                                dot, false);
-      dot = half_sum(dot);
-      // the same lazy rescaling as the tiles below: m moves only when the logit exceeds it by
-      // more than kRescaleLog2 (base 2), always on the first key (m = -inf)
-      const bool grow = dot * c2 > m * c2 + kRescaleLog2;
-      if (__any(grow)) {
-        const float m_new = grow ? dot : m;
-        const float alpha = grow ? exp2_fast((m - m_new) * c2) : 1.f;  // 0 while m = -inf
-        l *= alpha;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] *= alpha;
-        m = m_new;
-      }
-      const float p = exp2_fast((dot - m) * c2);
-      l += p;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[u][4 * b4 + e] = __builtin_fmaf(p, (float)vv[4 * u + b4][e], acc[u][4 * b4 + e]);
-    }
-  }
+  // Suffix keys t*Q_LEN + i (t = 1..k) of the workgroup's rows i in [q0, q0 + 128), merged
+  // before the causal tiles (the softmax state is order-independent).  They are the rows
+  // [t*Q_LEN + q0, t*Q_LEN + q0 + 128) of k and v: per block t, one pipeline slot copies the
+  // 128 K rows into a stage while the lanes take their logits from the other, and one slot
+  // does the same for the V rows.  A lane reads its own row i: the same half of the K row as
+  // of q (d = 16c + 8*hi ..) and the same half of the V row as of O (d = 32u + 8*b4 + 4*hi ..);
+  // the logit is the sum over the lane pair.  P stays fp32.  Rows i >= T see no suffix key.
+  const int nsuf = (FINAL && !DIAG && q0 < T) ? s.step : 0;
+  auto issue_rows = [&](const bf16* base, int t, bf16* dst) {  // rows t*Q_LEN + q0 .. + 127
+    load_tile<2 * FBN, 4>(base + ((size_t)t * s.L + q0) * FD, FD, dst, wave, lane);
+  };
+  if (nsuf > 0)
+    issue_rows(kb, 1, sKV0);
+  else if (ntiles > 0)
+    issue(0, sK0, sV0);
   wait_vmem();
   __syncthreads();
+  if (nsuf > 0) {
+    const int row = wave * 32 + l32;                      // this lane's row in the slot
+    const int swz = 4 * (row & 3) + ((row >> 2) & 3);     // chunk swizzle of that row
+    const bool live = my_q < T;
+    float p = 0.f;
+    for (int t = 1; t <= nsuf; ++t) {
+      issue_rows(vb, t, sKV1);
+      if (live) {
+        bf16x8 kk[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          kk[c] = *reinterpret_cast<const bf16x8*>(sKV0 + row * FD + 8 * ((2 * c + hi) ^ swz));
+        // q.k over the lane's 64 elements: packed bf16 pairs, products exact, fp32 sums
+        float dot = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2)
+            dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x8_pair(qf[c], e2), bf16x8_pair(kk[c], e2),
+                                                  dot, false);
+        dot = half_sum(dot);
+        // the same lazy rescaling as the tiles below: m moves only when the logit exceeds it
+        // by more than kRescaleLog2 (base 2), always on the first key (m = -inf)
+        const bool grow = dot * c2 > m * c2 + kRescaleLog2;
+        if (__any(grow)) {
+          const float m_new = grow ? dot : m;
+          const float alpha = grow ? exp2_fast((m - m_new) * c2) : 1.f;  // 0 while m = -inf
+          l *= alpha;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] *= alpha;
+          m = m_new;
+        }
+        p = exp2_fast((dot - m) * c2);
+        l += p;
+      }
+      wait_vmem();
+      __syncthreads();
+      if (t < nsuf)
+        issue_rows(kb, t + 1, sKV0);
+      else if (ntiles > 0)
+        issue(0, sK0, sV0);
+      if (live) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const bf16x4 vv = *reinterpret_cast<const bf16x4*>(
+                sKV1 + row * FD + 8 * ((4 * u + b4) ^ swz) + 4 * hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[u][4 * b4 + e] = __builtin_fmaf(p, (float)vv[e], acc[u][4 * b4 + e]);
+          }
+        }
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+  }
   for (int j = 0; j < ntiles; j += 2) {
     body(j, sK0, sV0, sK1, sV1);
     if (j + 1 < ntiles) body(j + 1, sK1, sV1, sK0, sV0);
