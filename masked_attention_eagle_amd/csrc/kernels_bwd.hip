@@ -155,13 +155,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
       const size_t row0 = p.row0;
       load_tile<KBM, 4>(q + row0 * BD, BD, dQ, wave, lane);
       load_tile<KBM, 4>(dO + row0 * BD, BD, dOt, wave, lane);
-      if (wave == 0) {  // lse * log2(e) of the 32 rows to dLD[0, 32), D to dLD[32, 64)
-        unsigned off = 4u * (lane & (KBM - 1));
+      if (wave < 2 && lane < KBM) {  // wave 0: lse * log2(e) of the 32 rows to dLD[0, 32); wave 1: D to dLD[32, 64)
+        unsigned off = 4u * lane;
         asm volatile("" : "+v"(off));
-        if (lane < KBM)
-          g2lds4(reinterpret_cast<const char*>(uniform_ptr(lse2 + row0)) + off, dLD);
-        else
-          g2lds4(reinterpret_cast<const char*>(uniform_ptr(Dd + row0)) + off, dLD);
+        g2lds4(reinterpret_cast<const char*>(uniform_ptr((wave == 0 ? lse2 : Dd) + row0)) + off,
+               dLD + KBM * wave);
       }
     };
 
