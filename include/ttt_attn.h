@@ -61,12 +61,15 @@ enum ttt_attn_dtype {
  *   that the standalone bandwidth-bound suffix kernel merges (the fp32 path always does so).
  * TTT_FLAG_RECOMPUTE_DQ: no stored dS (a much smaller backward workspace); the dQ kernel
  *   recomputes S and dP, three products per tile.  dk/dv are bitwise the same either way.
- * TTT_FLAG_DENSE_DIAGONAL (a measurement variant of the forward, not for production): the
- *   diagonal keys go through the matrix cores as masked 64-key tiles (two per block t per
- *   128-query tile), the way a block-sparse mask (FlexAttention's BlockMask) would evaluate
- *   them, instead of the per-row gather.  Cannot be combined with TTT_FLAG_SEPARATE_SUFFIX;
- *   the backward ignores it.
- * In the backward the suffix kernel always adds the diagonal keys' terms for k > 0.  The
+ * TTT_FLAG_DENSE_DIAGONAL (a measurement variant, not for production): the diagonal keys go
+ *   through the matrix cores as masked tiles, the way a block-sparse mask (FlexAttention's
+ *   BlockMask) would evaluate them.  Forward: two masked 64-key tiles per block t per 128-query
+ *   tile instead of the per-row merge.  Backward (k > 0): extra workgroups of the dK/dV kernel,
+ *   one per 128-key tile of each block t, take the 128 queries of that tile as masked tiles,
+ *   and the dQ kernel recomputes S and dP over the causal tiles and two masked tiles per
+ *   block t, writing the final dq (no suffix kernel, no stored dS).  Cannot be combined with
+ *   TTT_FLAG_SEPARATE_SUFFIX; the whole-TTT backward ignores it.
+ * Otherwise, in the backward the suffix kernel adds the diagonal keys' terms for k > 0.  The
  * workspace sizes below depend on the flags.
  */
 enum ttt_attn_flags {

@@ -95,9 +95,14 @@ int validate(const ttt_attn_params* p) {
   return TTT_OK;
 }
 
-// bf16 backward: the dQ kernel reads dS stored by the dK/dV kernel unless asked to recompute.
+// bf16 backward with the diagonal keys as masked matrix-core tiles (measurement variant).
+bool dense_bwd(const ttt_attn_params* p) {
+  return p->dtype == TTT_DTYPE_BF16 && (p->flags & TTT_FLAG_DENSE_DIAGONAL) && p->ttt_step > 0;
+}
+// bf16 backward: the dQ kernel reads dS stored by the dK/dV kernel unless asked to recompute
+// (the dense-diagonal backward always recomputes: its dQ kernel also takes the diagonal tiles).
 bool stored_ds(const ttt_attn_params* p) {
-  return p->dtype == TTT_DTYPE_BF16 && !(p->flags & TTT_FLAG_RECOMPUTE_DQ);
+  return p->dtype == TTT_DTYPE_BF16 && !(p->flags & TTT_FLAG_RECOMPUTE_DQ) && !dense_bwd(p);
 }
 // The forward merges the suffix inside the causal kernel unless asked for the separate
 // suffix kernel; the fp32 path always runs it.
@@ -156,7 +161,7 @@ struct BwdLayout {
 // D; (bf16) lse * log2(e) for the dK/dV kernel and the split dK/dV partials (heads of a group
 // over several workgroups); the dS blocks of block 0 when the dQ kernel reads them; for k > 0
 // the fp32 dQ accumulator that the suffix kernel finalises.
-BwdLayout bwd_layout(const Shape& s, int dtype, bool with_ds) {
+BwdLayout bwd_layout(const Shape& s, int dtype, bool with_ds, bool dense = false) {
   BwdLayout w;
   const size_t rows_q = (size_t)s.B * s.Hq * s.L;
   size_t off = 0;
@@ -176,7 +181,7 @@ BwdLayout bwd_layout(const Shape& s, int dtype, bool with_ds) {
     w.ds = off;
     off += round_up((size_t)s.B * s.Hq * (n * (n + 1) / 2) * 32 * 32 * 2);
   }
-  if (s.step > 0) {
+  if (s.step > 0 && !dense) {
     w.dqacc = off;
     off += round_up(rows_q * s.D * 4);
   }
@@ -215,7 +220,7 @@ size_t ttt_attn_fwd_workspace_size(const ttt_attn_params* p) {
 
 size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p) {
   if (validate(p) != TTT_OK) return 0;
-  return bwd_layout(make_shape(p), p->dtype, stored_ds(p)).total;
+  return bwd_layout(make_shape(p), p->dtype, stored_ds(p), dense_bwd(p)).total;
 }
 
 }  // extern "C"
@@ -262,9 +267,10 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
             const void* dout, void* dq, void* dk, void* dv, char* ws, GradAcc ga,
             hipStream_t st) {
   const bool with_ds = stored_ds(p);
-  const BwdLayout w = bwd_layout(s, p->dtype, with_ds);
+  const bool dense = dense_bwd(p) && !ga.dk;  // (the whole-TTT calls ignore the variant)
+  const BwdLayout w = bwd_layout(s, p->dtype, with_ds, dense);
   float* Dd = (float*)(ws + w.Dd);
-  const bool final_causal = s.step == 0;
+  const bool final_causal = s.step == 0 || dense;
   float* dqacc = final_causal ? nullptr : (float*)(ws + w.dqacc);
   hipError_t e;
   if (p->dtype == TTT_DTYPE_BF16) {
@@ -279,7 +285,7 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, lse, lse2, st)) != hipSuccess)
       return TTT_E_HIP;
     if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, dob, lse2, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
-                                  w.nsplit, dsb, ga, st)) != hipSuccess)
+                                  w.nsplit, dsb, ga, dense, st)) != hipSuccess)
       return TTT_E_HIP;
     if (w.nsplit > 1 &&
         (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, ga, st)) != hipSuccess)
@@ -287,7 +293,8 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     if (with_ds)
       e = launch_bwd_dq_ds(s, kb, dsb, seq_T, dq_causal, final_causal, st);
     else
-      e = launch_bwd_dq_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T, dq_causal, final_causal, st);
+      e = launch_bwd_dq_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T, dq_causal, final_causal, dense,
+                             st);
     if (e != hipSuccess) return TTT_E_HIP;
     if (!final_causal)
       e = launch_bwd_suffix<bf16>(s, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq, (bf16*)dk,
@@ -323,6 +330,13 @@ size_t sweep_fwd_ws(const ttt_attn_params* p) {
   size_t m = 0;
   for (int k = 0; k <= p->ttt_step; ++k) m = std::max(m, fwd_layout(sweep_shape(p, k), fused_fwd(p)).total);
   return m;
+}
+// The whole-TTT backward ignores TTT_FLAG_DENSE_DIAGONAL (its dK/dV sums go through the
+// suffix kernel): its paths and workspace follow the flags without that bit.
+ttt_attn_params sweep_bwd_params(const ttt_attn_params* p) {
+  ttt_attn_params q = *p;
+  q.flags &= ~TTT_FLAG_DENSE_DIAGONAL;
+  return q;
 }
 size_t sweep_bwd_step_ws(const ttt_attn_params* p) {
   size_t m = 0;
@@ -363,7 +377,7 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
   if (rc != TTT_OK) return rc;
   if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
   const Shape s = make_shape(p);
-  const BwdLayout w = bwd_layout(s, p->dtype, stored_ds(p));
+  const BwdLayout w = bwd_layout(s, p->dtype, stored_ds(p), dense_bwd(p));
   if (w.total > 0 && !workspace) return TTT_E_NULL;
   if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
@@ -381,7 +395,8 @@ size_t ttt_attn_fwd_sweep_workspace_size(const ttt_attn_params* p) {
 
 size_t ttt_attn_bwd_sweep_workspace_size(const ttt_attn_params* p) {
   if (validate(p) != TTT_OK || p->dtype != TTT_DTYPE_BF16) return 0;
-  return round_up(sweep_bwd_step_ws(p)) + 2 * round_up(sweep_grad_elems(p) * 4);
+  const ttt_attn_params pb = sweep_bwd_params(p);
+  return round_up(sweep_bwd_step_ws(&pb)) + 2 * round_up(sweep_grad_elems(p) * 4);
 }
 
 int ttt_attn_fwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
@@ -416,7 +431,8 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
   if (p->dtype != TTT_DTYPE_BF16) return TTT_E_UNSUPPORTED;
   if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
   if (!workspace) return TTT_E_NULL;
-  const size_t step_ws = round_up(sweep_bwd_step_ws(p));
+  const ttt_attn_params pb = sweep_bwd_params(p);
+  const size_t step_ws = round_up(sweep_bwd_step_ws(&pb));
   const size_t gbytes = round_up(sweep_grad_elems(p) * 4);
   if (workspace_bytes < step_ws + 2 * gbytes) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
@@ -433,7 +449,7 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
   // Last step first: it covers every row of the cache and so initialises the fp32 sums.
   for (int kk = p->ttt_step; kk >= 0; --kk) {
     ga.add = kk < p->ttt_step;
-    rc = run_bwd(p, sweep_shape(p, kk), (const bf16*)q + kk * qel, k, v, seq_T,
+    rc = run_bwd(&pb, sweep_shape(p, kk), (const bf16*)q + kk * qel, k, v, seq_T,
                  (const bf16*)o + kk * qel, lse + kk * rows, (const bf16*)dout + kk * qel,
                  (bf16*)dq + kk * qel, dk, dv, ws, ga, st);
     if (rc != TTT_OK) return rc;

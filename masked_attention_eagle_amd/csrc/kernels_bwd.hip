@@ -81,6 +81,13 @@ __device__ __forceinline__ unsigned ds_read_offset(int lane, int c, int r) {
 // Key tile kt is seen by every query row >= 128 * kt (padded rows see every key < T), so the
 // work of tile kt falls linearly with kt.  A workgroup takes the complementary pair
 // (p, n - 1 - p) of key tiles, which makes every workgroup's work equal.
+// DIAG (measurement variant of the backward, the way a BlockMask-driven kernel handles the
+// suffix): after the workgroups of block 0, one workgroup per (b, KV group, block t = 1..k,
+// 128-key tile) takes the key rows [t*Q_LEN + k0, t*Q_LEN + k0 + 128) and the query rows
+// [k0, k0 + 128) of every head of the group as masked tiles whose mask keeps key row
+// t*Q_LEN + i for query i < T; each 32-query tile meets the keys of one wave, the other three
+// skip it.  These workgroups write their dK/dV rows directly (no split, no dS hand-over).
+template <bool DIAG>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dd,
@@ -95,29 +102,40 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
   __shared__ __attribute__((aligned(256))) float sLD1[2 * KBM];
 
   const int nkt = s.L / KBN;
-  int unit, pair;
-  map_block(blockIdx.x, s.B * s.Hkv * nsplit, nsplit, unit, pair);
-  const int split = unit % nsplit, bg = unit / nsplit;
+  const int n_pair_wgs = s.B * s.Hkv * nsplit * ((nkt + 1) / 2);
+  const bool dwg = DIAG && (int)blockIdx.x >= n_pair_wgs;  // a diagonal tile of a block t >= 1
+  int unit, pair, tblk = 0, nsp = nsplit;
+  if (dwg) {
+    const int d = (int)blockIdx.x - n_pair_wgs;
+    unit = d % (s.B * s.Hkv);
+    pair = (d / (s.B * s.Hkv)) % nkt;  // the key tile
+    tblk = 1 + d / (s.B * s.Hkv * nkt);
+    nsp = 1;
+  } else {
+    map_block(blockIdx.x, s.B * s.Hkv * nsplit, nsplit, unit, pair);
+  }
+  const int split = unit % nsp, bg = unit / nsp;
   const int b = bg / s.Hkv;
   const int T = clamp_T(seq_T, b, s.L);
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int hpg = s.G / nsplit;
+  const int hpg = s.G / nsp;
   const int h_begin = (bg % s.Hkv) * s.G + split * hpg;
+  const size_t krow0 = (size_t)tblk * s.L;  // first K/V row of the block
   const float c2 = s.scale_log2;
   const FragOffsets fo = make_frag_offsets(lane);
 
 #pragma nounroll
   for (int pass = 0; pass < 2; ++pass) {
-    const int kt = pass == 0 ? pair : nkt - 1 - pair;
-    if (pass == 1 && kt == pair) break;  // odd tile count: the middle tile has no partner
+    const int kt = (pass == 0 || dwg) ? pair : nkt - 1 - pair;
+    if (pass == 1 && kt == pair) break;  // odd tile count (or a diagonal tile): no partner
     const int k0 = kt * KBN;
     const int kw = k0 + wave * 32;
     const int my_key = kw + l32;
 
     bf16x8 kf[8], vf[8];
     {
-      const bf16* kr = k + ((size_t)bg * s.KV + my_key) * BD + 8 * hi;
-      const bf16* vr = v + ((size_t)bg * s.KV + my_key) * BD + 8 * hi;
+      const bf16* kr = k + ((size_t)bg * s.KV + krow0 + my_key) * BD + 8 * hi;
+      const bf16* vr = v + ((size_t)bg * s.KV + krow0 + my_key) * BD + 8 * hi;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         kf[t] = *reinterpret_cast<const bf16x8*>(kr + 16 * t);
@@ -128,9 +146,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) dKacc[u] = dVacc[u] = f32x16{};
 
-    // Queries that see keys [k0, k0 + 128): rows >= k0 (rows >= T see every key < T).
+    // Queries that see keys [k0, k0 + 128): rows >= k0 (rows >= T see every key < T); for a
+    // diagonal tile, rows [k0, k0 + 128) only.
     const int q_first = (k0 < T) ? k0 : s.L;
-    const int nq = (s.L - q_first) / KBM;
+    const int q_end = dwg ? k0 + KBN : s.L;
+    const int nq = max(q_end - q_first, 0) / KBM;
     const int total = nq * hpg;
 
     // Tile `it` is (head h_begin + it / nq, query rows q_first + (it % nq) * KBM ..); the loop
@@ -145,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
       return Pos{h, q0, (size_t)bh * s.L + q0, ds_block_index(s, bh, q0 / 32, 0)};
     };
     auto next_pos = [&](Pos p) -> Pos {
-      if (p.q0 + KBM >= s.L) return make_pos(p.h + 1, q_first);
+      if (p.q0 + KBM >= q_end) return make_pos(p.h + 1, q_first);
       p.dsrow += p.q0 / 32 + 1;  // query block r holds r + 1 key blocks
       p.q0 += KBM;
       p.row0 += KBM;
@@ -167,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
                     bf16* nO, float* nLD) {
       const FragOffsets fl = opaque(fo);
       const int q0 = p.q0;
-      const bool live = kw < T && q0 + KBM - 1 >= kw;
+      const bool live = kw < T && (dwg ? q0 == kw : q0 + KBM - 1 >= kw);
       if (!live && it + 1 < total) issue(next_pos(p), nQ, nO, nLD);
       if (live) {
         // S, then P (kept in bf16 only), then dP: one accumulator tile live at a time.  The
@@ -187,8 +207,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
           for (int e = 0; e < 4; ++e)
             acc[4 * i4 + e] = exp2_fast(__builtin_fmaf(acc[4 * i4 + e], c2, -L4[e]));
         }
-        const bool full = (kw + 31 <= q0) && (kw + 32 <= T);
-        if (!full) {
+        const bool full = !dwg && (kw + 31 <= q0) && (kw + 32 <= T);
+        if (dwg) {  // key row t*Q_LEN + my_key serves query my_key only (q0 == kw), if < T
+          const int dkey = my_key >= T ? KBM : my_key - q0 - 4 * hi;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (dkey != acc_row(i, 0)) acc[i] = 0.f;
+        } else if (!full) {
           const int dkey = my_key >= T ? KBM : my_key - q0 - 4 * hi;
 #pragma unroll
           for (int i = 0; i < 16; ++i)
@@ -213,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
         }
         dsb[0] = to_bf16x8(acc, 0);
         dsb[1] = to_bf16x8(acc, 8);
-        if (ds_out) {  // hand dS to the dQ kernel (layout: ds_store_offset)
+        if (ds_out && !dwg) {  // hand dS to the dQ kernel (layout: ds_store_offset)
           const size_t blk = p.dsrow + kw / 32;
           void* dst = const_cast<void*>(uniform_ptr(ds_out + blk * 1024));
           unsigned off0 = ds_store_offset(lane, 0), off1 = ds_store_offset(lane, 1);
@@ -256,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     int lo = lane;
     asm volatile("" : "+v"(lo));
     const int ohi = lo >> 5, ol32 = lo & 31;
-    if (nsplit == 1 && ga.dk) {  // sweep: fp32 sums over the TTT steps
+    if (nsp == 1 && ga.dk) {  // sweep: fp32 sums over the TTT steps
       float* akp = ga.dk + ((size_t)bg * s.KV + kw) * BD;
       float* avp = ga.dv + ((size_t)bg * s.KV + kw) * BD;
 #pragma unroll
@@ -269,9 +294,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
           avp[o] = ga.add ? avp[o] + xv : xv;
         }
       }
-    } else if (nsplit == 1) {
-      bf16* dkp = dk + ((size_t)bg * s.KV + kw) * BD;
-      bf16* dvp = dv + ((size_t)bg * s.KV + kw) * BD;
+    } else if (nsp == 1) {
+      bf16* dkp = dk + ((size_t)bg * s.KV + krow0 + kw) * BD;
+      bf16* dvp = dv + ((size_t)bg * s.KV + krow0 + kw) * BD;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -301,11 +326,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse2, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
-                                int nsplit, bf16* ds_out, GradAcc ga, hipStream_t st) {
-  const dim3 grid(s.B * s.Hkv * nsplit * ((s.L / KBN + 1) / 2));
+                                int nsplit, bf16* ds_out, GradAcc ga, bool dense_diagonal,
+                                hipStream_t st) {
+  const int pairs = s.B * s.Hkv * nsplit * ((s.L / KBN + 1) / 2);
   LaunchTimer timer("bwd_dkdv_mfma", st);
-  bwd_dkdv_mfma_kernel<<<grid, 256, 0, st>>>(q, k, v, dout, lse2, Dd, seq_T, dk, dv, part, nsplit,
-                                             ds_out, ga, s);
+  if (dense_diagonal && s.step > 0) {
+    const dim3 grid(pairs + s.B * s.Hkv * (s.L / KBN) * s.step);
+    bwd_dkdv_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, v, dout, lse2, Dd, seq_T, dk, dv, part,
+                                                     nsplit, nullptr, ga, s);
+    return hipGetLastError();
+  }
+  bwd_dkdv_mfma_kernel<false><<<dim3(pairs), 256, 0, st>>>(q, k, v, dout, lse2, Dd, seq_T, dk, dv,
+                                                           part, nsplit, ds_out, ga, s);
   return hipGetLastError();
 }
 
@@ -378,7 +410,11 @@ hipError_t launch_grad_convert(const float* ak, const float* av, bf16* dk, bf16*
 constexpr int QBM = 128;
 constexpr int QBN = 64;
 
-template <bool FINAL>
+// DIAG (measurement variant, with FINAL): the diagonal keys of blocks 1..k go through the
+// matrix cores as masked tiles, the way a BlockMask-driven kernel handles them: block t's key
+// rows [t*Q_LEN + q0, t*Q_LEN + q0 + 128) form two extra 64-key tiles after the causal ones,
+// whose mask keeps key row t*Q_LEN + i for query i < T; dQ then covers every key and is final.
+template <bool FINAL, bool DIAG>
 __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
@@ -416,22 +452,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
   const bf16* kb = k + (size_t)bg * s.KV * BD;
   const bf16* vb = v + (size_t)bg * s.KV * BD;
   const int kv_end = min(q0 + QBM, T);
-  const int ntiles = (kv_end + QBN - 1) / QBN;
+  const int ncausal = (kv_end + QBN - 1) / QBN;
+  // DIAG: two diagonal tiles per block t = 1..k, unless no row of this workgroup is live
+  const int ntiles = ncausal + ((DIAG && q0 < T) ? 2 * s.step : 0);
+  auto tile_row = [&](int j) -> size_t {  // first key row of tile j in k/v
+    if (!DIAG || j < ncausal) return (size_t)j * QBN;
+    const int d = j - ncausal;
+    return (size_t)(1 + d / 2) * s.L + q0 + QBN * (d & 1);
+  };
 
   f32x16 acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
 
   auto issue = [&](int j, bf16* dK, bf16* dV) {
-    load_tile<QBN, 4>(kb + (size_t)j * QBN * BD, BD, dK, wave, lane);
-    load_tile<QBN, 4>(vb + (size_t)j * QBN * BD, BD, dV, wave, lane);
+    load_tile<QBN, 4>(kb + tile_row(j) * BD, BD, dK, wave, lane);
+    load_tile<QBN, 4>(vb + tile_row(j) * BD, BD, dV, wave, lane);
   };
 
   auto body = [&](int j, const bf16* cK, const bf16* cV, bf16* nK, bf16* nV) {
     const FragOffsets fl = opaque(fo);
     if (j + 1 < ntiles) issue(j + 1, nK, nV);
-    const int k0 = j * QBN;
-    if (k0 <= qw + 31) {
+    const bool diag = DIAG && j >= ncausal;  // a diagonal tile of block t >= 1
+    // block-local index of the tile's first key
+    const int k0 = diag ? q0 + QBN * ((j - ncausal) & 1) : j * QBN;
+    if (diag ? (k0 <= qw + 31 && qw <= k0 + QBN - 1) : (k0 <= qw + 31)) {
       f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -441,14 +486,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
           pacc[st] = mfma32(frag_row(cV, st * 32, t, fl), df[t], pacc[st]);
         }
       }
-      const bool full = (k0 + QBN - 1 <= qw) && (k0 + QBN <= T);
+      const bool full = !diag && (k0 + QBN - 1 <= qw) && (k0 + QBN <= T);
       bf16x8 dsb[4];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float pv = exp2_fast(__builtin_fmaf(sacc[st][i], c2, -lse2));
-          if (!full) {
+          if (diag) {  // key row t*Q_LEN + key serves query key only, and only for rows < T
+            const int key = k0 + st * 32 + acc_row(i, hi);
+            if (key != my_q || my_q >= T) pv = 0.f;
+          } else if (!full) {
             const int key = k0 + st * 32 + acc_row(i, hi);
             if (key > my_q || key >= T) pv = 0.f;
           }
@@ -504,13 +552,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
 
 hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                               const bf16* dout, const float* lse, const float* Dd,
-                              const int32_t* seq_T, void* dq, bool final_out, hipStream_t st) {
+                              const int32_t* seq_T, void* dq, bool final_out,
+                              bool dense_diagonal, hipStream_t st) {
   const dim3 grid(s.B * s.Hq * (s.L / QBM));
   LaunchTimer timer("bwd_dq_mfma", st);
-  if (final_out)
-    bwd_dq_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
+  if (dense_diagonal)  // every key of the row: the final dq
+    bwd_dq_mfma_kernel<true, true><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
+  else if (final_out)
+    bwd_dq_mfma_kernel<true, false><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
   else
-    bwd_dq_mfma_kernel<false><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
+    bwd_dq_mfma_kernel<false, false><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq, s);
   return hipGetLastError();
 }
 

@@ -51,7 +51,8 @@ hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* D
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse2, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
-                                int nsplit, bf16* ds_out, GradAcc ga, hipStream_t st);
+                                int nsplit, bf16* ds_out, GradAcc ga, bool dense_diagonal,
+                                hipStream_t st);
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
                                   bf16* dv, GradAcc ga, hipStream_t st);
 // dk, dv (bf16) = the fp32 sums of a sweep (n elements each).
@@ -59,7 +60,8 @@ hipError_t launch_grad_convert(const float* ak, const float* av, bf16* dk, bf16*
                                hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                               const bf16* dout, const float* lse, const float* Dd,
-                              const int32_t* seq_T, void* dq, bool final_out, hipStream_t st);
+                              const int32_t* seq_T, void* dq, bool final_out,
+                              bool dense_diagonal, hipStream_t st);
 hipError_t launch_bwd_dq_ds(const Shape& s, const bf16* k, const bf16* ds, const int32_t* seq_T,
                             void* dq, bool final_out, hipStream_t st);
 template <typename T>

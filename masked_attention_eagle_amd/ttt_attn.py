@@ -210,16 +210,18 @@ def ttt_attn_fwd(q, k, v, seq_T, scale: Optional[float] = None, out=None, lse=No
 
 
 def ttt_attn_bwd(q, k, v, seq_T, o, lse, dout, scale: Optional[float] = None, dq=None, dk=None,
-                 dv=None, workspace=None, dq_mode: str = "stored"):
+                 dv=None, workspace=None, dq_mode: str = "stored", suffix: str = "fused"):
     """dq, dk, dv: gradients of sum(dout * o) for the o/lse of ttt_attn_fwd.
 
     dq_mode "stored": the dK/dV kernel hands dS of block 0 to the dQ kernel through the
     workspace (one matrix product per tile there); "recompute": a small workspace, and the dQ
-    kernel recomputes S and dP.
+    kernel recomputes S and dP.  suffix "dense" (measurement variant) takes the diagonal keys of
+    blocks 1..k through the matrix-core kernels as masked tiles (dQ recomputed) instead of the
+    suffix kernel; "fused" and "separate" give the same backward.
     """
     import torch
     lib = load()
-    p = _params_from(q, k, scale, path_flags("fused", dq_mode))
+    p = _params_from(q, k, scale, path_flags(suffix, dq_mode))
     _require(q, "q")
     _require(k, "k", q.dtype)
     _require(v, "v", q.dtype, k.shape)

@@ -36,7 +36,8 @@ def gpu_fwd_bwd(lib, q, k, v, do, T, scale, dtype_name, with_bwd=True, dq_mode="
     o, lse = lib.ttt_attn_fwd(qd, kd, vd, Td, scale, suffix=suffix)
     out = {"o": to_np(o), "lse": to_np(lse)}
     if with_bwd:
-        dq, dk, dv = lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, scale, dq_mode=dq_mode)
+        dq, dk, dv = lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, scale, dq_mode=dq_mode,
+                                      suffix=suffix)
         out.update(dq=to_np(dq), dk=to_np(dk), dv=to_np(dv))
     torch.cuda.synchronize()
     return out

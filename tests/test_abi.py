@@ -94,6 +94,12 @@ def test_workspace_sizes():
     assert A.bwd_workspace_size(p) == rows * 8 + part + ds_bytes(B, Hq, L) + dqacc
     assert A.bwd_workspace_size(P(flags=sep)) == A.bwd_workspace_size(p)
     assert A.bwd_workspace_size(P(step=0)) == rows * 8 + part + ds_bytes(B, Hq, L)
+    # dense-diagonal backward (measurement variant): dQ recomputed over the causal and the
+    # diagonal tiles in one kernel, written final: no dS blocks and no fp32 dQ accumulator
+    dense = A.TTT_FLAG_DENSE_DIAGONAL
+    assert A.bwd_workspace_size(P(flags=dense)) == rows * 8 + part
+    assert A.bwd_workspace_size(P(flags=dense | rec)) == rows * 8 + part
+    assert A.bwd_workspace_size(P(flags=dense, step=0)) == A.bwd_workspace_size(P(step=0))
     # recomputing dQ kernel: no dS blocks
     assert A.bwd_workspace_size(P(flags=rec)) == rows * 8 + part + dqacc
     assert A.bwd_workspace_size(P(flags=rec | sep)) == rows * 8 + part + dqacc
@@ -179,6 +185,9 @@ def test_sweep_workspace_and_errors():
     assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(p)) == 0  # fused forward
     sep = P(step=K - 1, flags=A.TTT_FLAG_SEPARATE_SUFFIX)
     assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(sep)) == A.fwd_workspace_size(sep)
+    # the whole-TTT backward ignores the dense-diagonal variant (same paths, same workspace)
+    dense = P(step=K - 1, flags=A.TTT_FLAG_DENSE_DIAGONAL)
+    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(dense)) == per_step + sums
     pf = P(step=2, dtype=A.TTT_DTYPE_F32)
     assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(pf)) == 0
     assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(pf)) == 0

@@ -71,15 +71,38 @@ def test_bf16_gqa_groups(gpu_lib, Hq, Hkv, dq_mode, suffix):
 
 @pytest.mark.parametrize("step", [1, 3])
 @pytest.mark.parametrize("T", [(256, 256), (0, 256), (1, 255), (65, 127), (200, 17)])
-def test_bf16_dense_diagonal_forward(gpu_lib, step, T):
-    """The measurement variant that runs the diagonal keys through masked matrix-core tiles
-    (forward only; the backward ignores the flag)."""
+def test_bf16_dense_diagonal(gpu_lib, step, T):
+    """The measurement variant that runs the diagonal keys through masked matrix-core tiles,
+    forward and backward (dQ over the causal and diagonal tiles in one kernel, dK/dV of blocks
+    1..k from extra workgroups of the dK/dV kernel)."""
     run_case(gpu_lib, 70 + step, 2, 4, 2, 128, 256, step, T, "bf16", suffix="dense")
+
+
+def test_bf16_dense_diagonal_backward_block0_bitwise(gpu_lib):
+    """The dense-diagonal backward computes block 0's dK/dV with the same code as the default
+    path: bitwise equal there; blocks 1..k agree with the suffix kernel within the gradient
+    tolerance (both are checked against the oracle above)."""
+    import torch
+    from tests.helpers import to_dev
+    L = 384
+    q, k, v, do, T = inputs.make_case(57, 2, 8, 2, 128, L, 3, (384, 301), "bf16")
+    qd, kd, vd, dod = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+    Td = torch.as_tensor(T, device="cuda")
+    o, lse = gpu_lib.ttt_attn_fwd(qd, kd, vd, Td)
+    a = gpu_lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, suffix="dense")
+    b = gpu_lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod)
+    for x, y in ((a[1], b[1]), (a[2], b[2])):
+        assert torch.equal(x[:, :, :L].view(torch.int16), y[:, :, :L].view(torch.int16))
+        den = float(y.float().abs().max())
+        assert float((x.float() - y.float()).abs().max()) <= 2e-2 * den
+    den = float(b[0].float().abs().max())
+    assert float((a[0].float() - b[0].float()).abs().max()) <= 2e-2 * den
 
 
 @pytest.mark.parametrize("step", [5, 12])
 def test_bf16_long_ttt(gpu_lib, step):
-    """Many suffix blocks (the long-TTT workload runs to k = 12): fused and separate paths."""
+    """Many suffix blocks (the long-TTT workload runs to k = 12): fused, separate and dense
+    (masked diagonal matrix-core tiles) paths."""
     for suffix in ("fused", "separate", "dense"):
         run_case(gpu_lib, 60 + step, 1, 4, 1, 128, 256, step, 201, "bf16", suffix=suffix)
 
