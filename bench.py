@@ -95,8 +95,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra measurement of the step captured in a HIP graph")
     ap.add_argument("--suffix", choices=("fused", "separate", "dense"), default="fused",
-                    help="forward: diagonal keys merged inside the causal kernel, the standalone "
-                         "suffix kernel, or (measurement variant) masked diagonal matrix-core tiles")
+                    help="diagonal keys of blocks 1..k: merged inside the causal forward kernel, "
+                         "the forward's standalone suffix kernel, or (measurement variant, forward "
+                         "and backward) masked diagonal matrix-core tiles")
     ap.add_argument("--sweep", action="store_true",
                     help="time the whole-TTT calls (one forward and one backward call over one KV "
                          "cache, dK/dV summed over the steps) instead of the per-step calls")
