@@ -20,8 +20,9 @@ namespace ttt {
 //                                          reads, B = P^T straight from S^T)
 // Tiles past min(q0 + 128, T) are never loaded (the BlockMask "skip" class); only tiles that
 // straddle the diagonal or the T edge evaluate the mask ("partial"); the rest are "full".
-// On partial tiles P is split into bf16 hi + lo parts so that rows with few keys (where one
-// rounding of P would show in O) keep fp32-level accuracy.
+// On partial tiles of waves whose rows see fewer than 64 keys, P is split into bf16 hi + lo
+// parts so that rows with few keys (where one rounding of P would show in O) keep fp32-level
+// accuracy.
 // With FINAL and k > 0 the kernel also merges the suffix keys (one per block 1..k for rows
 // i < T; their K and V rows pass through the same LDS stages before the causal tiles) and
 // writes the final o and lse; without FINAL it writes the fp32 causal state for the
@@ -115,6 +116,9 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
           sacc[st] = mfma32(frag_row(cK, st * 32, t, fl), qf[t], sacc[st]);
       }
       const bool full = !diag && (k0 + FBN - 1 <= qw) && (k0 + FBN <= T);
+      // every row of the wave sees at least 64 keys of block 0 (rows i < T see min(i + 1, T),
+      // rows i >= T see T): one bf16 rounding of P then costs O no more than on full tiles
+      const bool wide = !diag && qw >= FBN - 1 && T >= FBN;
       if (diag) {  // key row t*Q_LEN + key serves query key only, and only for rows < T
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
       const float mc = (m == kNegInf) ? 0.f : m * c2;
       float lsum = 0.f;
       bf16x8 pf[4];
-      if (full) {
+      if (full || wide) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
 #pragma unroll
