@@ -115,6 +115,14 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
         for (int st = 0; st < 2; ++st)
           sacc[st] = mfma32(frag_row(cK, st * 32, t, fl), qf[t], sacc[st]);
       }
+      // K fragment reads kept two products ahead of the products
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int t = 0; t < 5; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
       const bool full = !diag && (k0 + FBN - 1 <= qw) && (k0 + FBN <= T);
       // every row of the wave sees at least 64 keys of block 0 (rows i < T see min(i + 1, T),
       // rows i >= T see T): one bf16 rounding of P then costs O no more than on full tiles
