@@ -446,15 +446,18 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
   const size_t qel = (size_t)p->batch * p->heads_q * p->q_len * p->head_dim;
   const size_t rows = (size_t)p->batch * p->heads_q * p->q_len;
   hipStream_t st = (hipStream_t)stream;
-  // Last step first: it covers every row of the cache and so initialises the fp32 sums.
+  // Last step first: it covers every row of the cache and so initialises the fp32 sums.  Step
+  // kk is the last contribution to block kk (steps k >= t reach block t; block 0 sees all),
+  // whose rows therefore go to dk/dv as bf16 in that step.
   for (int kk = p->ttt_step; kk >= 0; --kk) {
     ga.add = kk < p->ttt_step;
+    ga.final_block = kk;
     rc = run_bwd(&pb, sweep_shape(p, kk), (const bf16*)q + kk * qel, k, v, seq_T,
                  (const bf16*)o + kk * qel, lse + kk * rows, (const bf16*)dout + kk * qel,
                  (bf16*)dq + kk * qel, dk, dv, ws, ga, st);
     if (rc != TTT_OK) return rc;
   }
-  return hip_status(launch_grad_convert(ga.dk, ga.dv, (bf16*)dk, (bf16*)dv, sweep_grad_elems(p), st));
+  return TTT_OK;
 }
 
 int ttt_loss_grad_inplace(const ttt_loss_params* p, void* z, const void* target, const float* g,

@@ -30,9 +30,10 @@ constexpr int BD = 128;  // head dim of the matrix-core path
 constexpr int KBN = 128;  // keys per tile
 constexpr int KBM = 32;   // queries per tile
 
-// One dK or dV row slice of a suffix key: bf16 output, or (TTT sweep) the fp32 sum.
+// One dK or dV row slice of a suffix key: bf16 output, or (TTT sweep) the fp32 sum, whose
+// final value (fin: the row's last contribution) goes to the output instead.
 template <typename T, int E>
-__device__ __forceinline__ void put_grad_row(T* out, float* acc, int add, size_t idx,
+__device__ __forceinline__ void put_grad_row(T* out, float* acc, int add, bool fin, size_t idx,
                                              const float* x) {
   if (acc) {
     float a[E];
@@ -44,7 +45,10 @@ __device__ __forceinline__ void put_grad_row(T* out, float* acc, int add, size_t
 #pragma unroll
       for (int e = 0; e < E; ++e) a[e] = x[e];
     }
-    store_vec<float, E>(acc + idx, a);
+    if (fin)
+      store_vec<T, E>(out + idx, a);
+    else
+      store_vec<float, E>(acc + idx, a);
   } else {
     store_vec<T, E>(out + idx, x);
   }
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     int lo = lane;
     asm volatile("" : "+v"(lo));
     const int ohi = lo >> 5, ol32 = lo & 31;
-    if (nsp == 1 && ga.dk) {  // sweep: fp32 sums over the TTT steps
+    if (nsp == 1 && ga.dk && ga.final_block != 0) {  // sweep: fp32 sums over the TTT steps
       float* akp = ga.dk + ((size_t)bg * s.KV + kw) * BD;
       float* avp = ga.dv + ((size_t)bg * s.KV + kw) * BD;
 #pragma unroll
@@ -297,13 +301,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     } else if (nsp == 1) {
       bf16* dkp = dk + ((size_t)bg * s.KV + krow0 + kw) * BD;
       bf16* dvp = dv + ((size_t)bg * s.KV + krow0 + kw) * BD;
+      // a sweep's last step for block 0 adds the fp32 sums of the other steps
+      const float* akp = (ga.dk && ga.add) ? ga.dk + ((size_t)bg * s.KV + kw) * BD : nullptr;
+      const float* avp = (ga.dk && ga.add) ? ga.dv + ((size_t)bg * s.KV + kw) * BD : nullptr;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int o = acc_row(i, ohi) * BD + 32 * u + ol32;
-          dkp[o] = (bf16)(dKacc[u][i] * s.scale);
-          dvp[o] = (bf16)dVacc[u][i];
+          float xk = dKacc[u][i] * s.scale, xv = dVacc[u][i];
+          if (akp) {
+            xk += akp[o];
+            xv += avp[o];
+          }
+          dkp[o] = (bf16)xk;
+          dvp[o] = (bf16)xv;
         }
       }
     } else {
@@ -355,10 +367,13 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
   for (int sp = 1; sp < nsplit; ++sp)
     acc += *reinterpret_cast<const f32x4*>(part + (size_t)sp * 2 * plane + (is_v ? plane : 0) + e);
   const size_t bg = e / ((size_t)s.L * BD), rem = e % ((size_t)s.L * BD);
-  if (ga.dk) {  // sweep: fp32 sums over the TTT steps
+  if (ga.dk) {  // sweep: fp32 sums over the TTT steps; block 0's last step writes the outputs
     f32x4* a = reinterpret_cast<f32x4*>((is_v ? ga.dv : ga.dk) + bg * s.KV * BD + rem);
-    *a = ga.add ? *a + acc : acc;
-    return;
+    if (ga.add) acc += *a;
+    if (ga.final_block != 0) {
+      *a = acc;
+      return;
+    }
   }
   bf16x4 w;
 #pragma unroll
@@ -372,30 +387,6 @@ hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit,
   const dim3 grid((unsigned)((n4 + 255) / 256));
   LaunchTimer timer("bwd_dkdv_reduce", st);
   dkdv_reduce_kernel<<<grid, 256, 0, st>>>(part, nsplit, dk, dv, ga, s);
-  return hipGetLastError();
-}
-
-// dk, dv = bf16 of the fp32 sums of a TTT sweep.
-__global__ __launch_bounds__(256) void grad_convert_kernel(const float* __restrict__ ak,
-                                                           const float* __restrict__ av,
-                                                           bf16* __restrict__ dk,
-                                                           bf16* __restrict__ dv, size_t n) {
-  const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e >= 2 * n) return;
-  const bool is_v = e >= n;
-  const size_t i = is_v ? e - n : e;
-  const f32x4 x = *reinterpret_cast<const f32x4*>((is_v ? av : ak) + i);
-  bf16x4 w;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = (bf16)x[j];
-  *reinterpret_cast<bf16x4*>((is_v ? dv : dk) + i) = w;
-}
-
-hipError_t launch_grad_convert(const float* ak, const float* av, bf16* dk, bf16* dv, size_t n,
-                               hipStream_t st) {
-  const dim3 grid((unsigned)((2 * n / 4 + 255) / 256));
-  LaunchTimer timer("grad_convert", st);
-  grad_convert_kernel<<<grid, 256, 0, st>>>(ak, av, dk, dv, n);
   return hipGetLastError();
 }
 
@@ -907,12 +898,14 @@ template hipError_t launch_bwd_dq_valu<float>(const Shape&, const float*, const 
 // Two passes (dQ head by head, then dK/dV key row by key row) keep the register footprint
 // independent of the group size; the second pass re-reads q/dO from cache.
 // ----------------------------------------------------------------------------------------
-template <typename T, int D>
+// ACC: the TTT sweep's fp32 dK/dV sums (ga) are in use; without it ga is ignored.
+template <typename T, int D, bool ACC>
 __global__ __launch_bounds__(256) void bwd_suffix_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, const float* __restrict__ dq_acc, T* __restrict__ dq,
-    T* __restrict__ dk, T* __restrict__ dv, GradAcc ga, Shape s) {
+    T* __restrict__ dk, T* __restrict__ dv, GradAcc ga_arg, Shape s) {
+  const GradAcc ga = ACC ? ga_arg : GradAcc{};
   constexpr int E = D / 16;
   const int sub = threadIdx.x & 15;
   const int blocks_per_bg = (s.L + 15) / 16;
@@ -988,9 +981,10 @@ __global__ __launch_bounds__(256) void bwd_suffix_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[e] *= s.scale;
     }
-    if (live || !ga.add) {  // dead rows: zero, or nothing to add
-      put_grad_row<T, E>(dk, ga.dk, ga.add, kv_base + (size_t)t * s.L * D, aK);
-      put_grad_row<T, E>(dv, ga.dv, ga.add, kv_base + (size_t)t * s.L * D, aV);
+    const bool fin = ga.final_block == t;
+    if (live || !ga.add || fin) {  // dead rows: zero, or nothing to add
+      put_grad_row<T, E>(dk, ga.dk, ga.add, fin, kv_base + (size_t)t * s.L * D, aK);
+      put_grad_row<T, E>(dv, ga.dv, ga.add, fin, kv_base + (size_t)t * s.L * D, aV);
     }
   }
 }
@@ -998,12 +992,13 @@ __global__ __launch_bounds__(256) void bwd_suffix_kernel(
 // Single pass with the step loop outside and every head of the group in registers: each
 // diagonal K/V row is read once per (row, group) and its dK/dV row is written right away;
 // dQ of all heads accumulates in registers and is written at the end.
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool ACC>
 __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, const float* __restrict__ dq_acc, T* __restrict__ dq,
-    T* __restrict__ dk, T* __restrict__ dv, GradAcc ga, Shape s) {
+    T* __restrict__ dk, T* __restrict__ dv, GradAcc ga_arg, Shape s) {
+  const GradAcc ga = ACC ? ga_arg : GradAcc{};
   constexpr int E = D / 16;
   const int sub = threadIdx.x & 15;
   const int blocks_per_bg = (s.L + 15) / 16;
@@ -1065,8 +1060,9 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[e] *= s.scale;
-      put_grad_row<T, E>(dk, ga.dk, ga.add, kv_base + (size_t)t * s.L * D, aK);
-      put_grad_row<T, E>(dv, ga.dv, ga.add, kv_base + (size_t)t * s.L * D, aV);
+      const bool fin = ga.final_block == t;
+      put_grad_row<T, E>(dk, ga.dk, ga.add, fin, kv_base + (size_t)t * s.L * D, aK);
+      put_grad_row<T, E>(dv, ga.dv, ga.add, fin, kv_base + (size_t)t * s.L * D, aV);
       if (t < s.step) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -1075,13 +1071,17 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
         }
       }
     }
-  } else if (!ga.add) {  // rows no query sees: zero (nothing to add in a sweep's later steps)
+  } else if (!ga.add || ga.final_block >= 1) {
+    // rows no query sees: zero (in a sweep's later steps nothing to add, except the rows of
+    // the block that is final in this step, which go to the outputs)
     float z[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) z[e] = 0.f;
     for (int t = 1; t <= s.step; ++t) {
-      put_grad_row<T, E>(dk, ga.dk, 0, kv_base + (size_t)t * s.L * D, z);
-      put_grad_row<T, E>(dv, ga.dv, 0, kv_base + (size_t)t * s.L * D, z);
+      const bool fin = ga.final_block == t;
+      if (ga.add && !fin) continue;
+      put_grad_row<T, E>(dk, ga.dk, 0, fin, kv_base + (size_t)t * s.L * D, z);
+      put_grad_row<T, E>(dv, ga.dv, 0, fin, kv_base + (size_t)t * s.L * D, z);
     }
   }
 #pragma unroll
@@ -1095,18 +1095,28 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
   }
 }
 
+template <typename T, int D, bool ACC>
+static void bwd_suffix_launch(const Shape& s, dim3 grid, hipStream_t st, const T* q,
+                              const T* k, const T* v, const T* dout, const float* lse,
+                              const float* Dd, const int32_t* seq_T, const float* dq_acc,
+                              T* dq, T* dk, T* dv, GradAcc ga) {
+  switch (s.G) {
+    case 1: bwd_suffix_g_kernel<T, D, 1, ACC><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
+    case 2: bwd_suffix_g_kernel<T, D, 2, ACC><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
+    case 4: bwd_suffix_g_kernel<T, D, 4, ACC><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
+    case 8: bwd_suffix_g_kernel<T, D, 8, ACC><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
+    default: bwd_suffix_kernel<T, D, ACC><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
+  }
+}
 template <typename T, int D>
 static hipError_t bwd_suffix_dispatch(const Shape& s, dim3 grid, hipStream_t st, const T* q,
                                       const T* k, const T* v, const T* dout, const float* lse,
                                       const float* Dd, const int32_t* seq_T, const float* dq_acc,
                                       T* dq, T* dk, T* dv, GradAcc ga) {
-  switch (s.G) {
-    case 1: bwd_suffix_g_kernel<T, D, 1><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
-    case 2: bwd_suffix_g_kernel<T, D, 2><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
-    case 4: bwd_suffix_g_kernel<T, D, 4><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
-    case 8: bwd_suffix_g_kernel<T, D, 8><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
-    default: bwd_suffix_kernel<T, D><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
-  }
+  if (ga.dk)
+    bwd_suffix_launch<T, D, true>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga);
+  else
+    bwd_suffix_launch<T, D, false>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga);
   return hipGetLastError();
 }
 

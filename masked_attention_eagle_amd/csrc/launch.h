@@ -35,11 +35,14 @@ hipError_t launch_fwd_suffix(const Shape& s, const T* q, const T* k, const T* v,
 
 // fp32 accumulation of dK/dV over the steps of a TTT sweep: with dk non-null the backward
 // kernels store (add == 0) or add (add != 0) their dK/dV rows there instead of writing the
-// bf16 outputs.  Rows a step does not own are left alone.
+// bf16 outputs.  Rows a step does not own are left alone.  The rows of block final_block get
+// their last contribution in this step: they go to the bf16 outputs (sum + contribution,
+// rounded once) instead.
 struct GradAcc {
   float* dk = nullptr;
   float* dv = nullptr;
   int add = 0;
+  int final_block = -1;
 };
 
 // Backward.
@@ -55,9 +58,6 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, co
                                 hipStream_t st);
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
                                   bf16* dv, GradAcc ga, hipStream_t st);
-// dk, dv (bf16) = the fp32 sums of a sweep (n elements each).
-hipError_t launch_grad_convert(const float* ak, const float* av, bf16* dk, bf16* dv, size_t n,
-                               hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                               const bf16* dout, const float* lse, const float* Dd,
                               const int32_t* seq_T, void* dq, bool final_out,
