@@ -21,6 +21,9 @@ struct Shape {
   int B, Hq, Hkv, L, D, step, G, KV;  // KV = (step + 1) * L
   float scale;                        // multiplies q.k
   float scale_log2;                   // scale * log2(e): logits in base-2 units
+  // TTT steps whose queries one launch covers: 1, or (whole-TTT backward: row-dot, dK/dV of
+  // block 0 and its reduction) all of them, stacked step after step (B*Hq*L rows per step)
+  int nst;
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

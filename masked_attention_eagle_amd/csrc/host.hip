@@ -122,18 +122,20 @@ Shape make_shape(const ttt_attn_params* p) {
   s.KV = (p->ttt_step + 1) * p->q_len;
   s.scale = p->scale;
   s.scale_log2 = p->scale * kLog2e;
+  s.nst = 1;
   return s;
 }
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Number of workgroups that share the query heads of one KV group in the dK/dV kernel
-// (each workgroup owns a pair of 128-key tiles): doubled while the grid is below two
-// workgroups per CU and the group still splits evenly.
+// Number of workgroups that share the (step, query head) pairs of one KV group in the dK/dV
+// kernel (each workgroup owns a pair of 128-key tiles): doubled while the grid is below two
+// workgroups per CU and the pairs still split evenly.
 int dkdv_nsplit(const Shape& s) {
   const int64_t base = (int64_t)s.B * s.Hkv * ((s.L / 128 + 1) / 2);
+  const int pairs = s.G * s.nst;
   int n = 1;
-  while (base * n < 512 && n < s.G && s.G % (2 * n) == 0) n *= 2;
+  while (base * n < 512 && n < pairs && pairs % (2 * n) == 0) n *= 2;
   return n;
 }
 
@@ -160,10 +162,16 @@ struct BwdLayout {
 };
 // D; (bf16) lse * log2(e) for the dK/dV kernel and the split dK/dV partials (heads of a group
 // over several workgroups); the dS blocks of block 0 when the dQ kernel reads them; for k > 0
-// the fp32 dQ accumulator that the suffix kernel finalises.
+// the fp32 dQ accumulator that the suffix kernel finalises.  D, lse * log2(e) and dS are held
+// for each of the s.nst steps; the dQ accumulator serves one step at a time.
+size_t ds_step_elems(const Shape& s) {
+  const size_t n = s.L / 32;
+  return (size_t)s.B * s.Hq * (n * (n + 1) / 2) * 32 * 32;
+}
 BwdLayout bwd_layout(const Shape& s, int dtype, bool with_ds, bool dense = false) {
   BwdLayout w;
-  const size_t rows_q = (size_t)s.B * s.Hq * s.L;
+  const size_t rows_1 = (size_t)s.B * s.Hq * s.L;
+  const size_t rows_q = rows_1 * s.nst;
   size_t off = 0;
   w.Dd = off;
   off += round_up(rows_q * 4);
@@ -177,13 +185,12 @@ BwdLayout bwd_layout(const Shape& s, int dtype, bool with_ds, bool dense = false
     }
   }
   if (with_ds) {
-    const size_t n = s.L / 32;
     w.ds = off;
-    off += round_up((size_t)s.B * s.Hq * (n * (n + 1) / 2) * 32 * 32 * 2);
+    off += round_up(ds_step_elems(s) * s.nst * 2);
   }
   if (s.step > 0 && !dense) {
     w.dqacc = off;
-    off += round_up(rows_q * s.D * 4);
+    off += round_up(rows_1 * s.D * 4);
   }
   w.total = off;
   return w;
@@ -260,14 +267,12 @@ int run_fwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
   return hip_status(e);
 }
 
-// One backward step on validated arguments.  With ga.dk set (bf16 only) the dK/dV rows of
-// this step go to the fp32 sums instead of dk/dv.
+// One backward step on validated arguments.
 int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void* k,
             const void* v, const int32_t* seq_T, const void* o, const float* lse,
-            const void* dout, void* dq, void* dk, void* dv, char* ws, GradAcc ga,
-            hipStream_t st) {
+            const void* dout, void* dq, void* dk, void* dv, char* ws, hipStream_t st) {
   const bool with_ds = stored_ds(p);
-  const bool dense = dense_bwd(p) && !ga.dk;  // (the whole-TTT calls ignore the variant)
+  const bool dense = dense_bwd(p);
   const BwdLayout w = bwd_layout(s, p->dtype, with_ds, dense);
   float* Dd = (float*)(ws + w.Dd);
   const bool final_causal = s.step == 0 || dense;
@@ -285,10 +290,10 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, lse, lse2, st)) != hipSuccess)
       return TTT_E_HIP;
     if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, dob, lse2, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
-                                  w.nsplit, dsb, ga, dense, st)) != hipSuccess)
+                                  w.nsplit, dsb, dense, st)) != hipSuccess)
       return TTT_E_HIP;
     if (w.nsplit > 1 &&
-        (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, ga, st)) != hipSuccess)
+        (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
       return TTT_E_HIP;
     if (with_ds)
       e = launch_bwd_dq_ds(s, kb, dsb, seq_T, dq_causal, final_causal, st);
@@ -298,7 +303,7 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     if (e != hipSuccess) return TTT_E_HIP;
     if (!final_causal)
       e = launch_bwd_suffix<bf16>(s, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq, (bf16*)dk,
-                                  (bf16*)dv, ga, st);
+                                  (bf16*)dv, GradAcc{}, st);
   } else {
     const float* qf = (const float*)q;
     const float* kf = (const float*)k;
@@ -338,11 +343,12 @@ ttt_attn_params sweep_bwd_params(const ttt_attn_params* p) {
   q.flags &= ~TTT_FLAG_DENSE_DIAGONAL;
   return q;
 }
-size_t sweep_bwd_step_ws(const ttt_attn_params* p) {
-  size_t m = 0;
-  for (int k = 0; k <= p->ttt_step; ++k)
-    m = std::max(m, bwd_layout(sweep_shape(p, k), p->dtype, stored_ds(p)).total);
-  return m;
+// The whole-TTT backward's shape for the launches that cover every step at once (row-dot,
+// dK/dV of block 0, its reduction).
+Shape sweep_all_shape(const ttt_attn_params* p) {
+  Shape s = make_shape(p);
+  s.nst = p->ttt_step + 1;
+  return s;
 }
 size_t sweep_grad_elems(const ttt_attn_params* p) {  // elements of dk (or dv)
   return (size_t)p->batch * p->heads_kv * (size_t)(p->ttt_step + 1) * p->q_len * p->head_dim;
@@ -384,7 +390,7 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || !aligned16(workspace))
     return TTT_E_ALIGN;
-  return run_bwd(p, s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, (char*)workspace, GradAcc{},
+  return run_bwd(p, s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, (char*)workspace,
                  (hipStream_t)stream);
 }
 
@@ -396,7 +402,8 @@ size_t ttt_attn_fwd_sweep_workspace_size(const ttt_attn_params* p) {
 size_t ttt_attn_bwd_sweep_workspace_size(const ttt_attn_params* p) {
   if (validate(p) != TTT_OK || p->dtype != TTT_DTYPE_BF16) return 0;
   const ttt_attn_params pb = sweep_bwd_params(p);
-  return round_up(sweep_bwd_step_ws(&pb)) + 2 * round_up(sweep_grad_elems(p) * 4);
+  return bwd_layout(sweep_all_shape(p), p->dtype, stored_ds(&pb)).total +
+         2 * round_up(sweep_grad_elems(p) * 4);
 }
 
 int ttt_attn_fwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
@@ -432,30 +439,62 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
   if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
   if (!workspace) return TTT_E_NULL;
   const ttt_attn_params pb = sweep_bwd_params(p);
-  const size_t step_ws = round_up(sweep_bwd_step_ws(&pb));
+  const bool with_ds = stored_ds(&pb);
+  const Shape sa = sweep_all_shape(p);
+  const BwdLayout w = bwd_layout(sa, p->dtype, with_ds);
   const size_t gbytes = round_up(sweep_grad_elems(p) * 4);
-  if (workspace_bytes < step_ws + 2 * gbytes) return TTT_E_WORKSPACE;
+  if (workspace_bytes < w.total + 2 * gbytes) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || !aligned16(workspace))
     return TTT_E_ALIGN;
   char* ws = (char*)workspace;
-  GradAcc ga;
-  ga.dk = (float*)(ws + step_ws);
-  ga.dv = (float*)(ws + step_ws + gbytes);
   const size_t qel = (size_t)p->batch * p->heads_q * p->q_len * p->head_dim;
   const size_t rows = (size_t)p->batch * p->heads_q * p->q_len;
   hipStream_t st = (hipStream_t)stream;
-  // Last step first: it covers every row of the cache and so initialises the fp32 sums.  Step
-  // kk is the last contribution to block kk (steps k >= t reach block t; block 0 sees all),
-  // whose rows therefore go to dk/dv as bf16 in that step.
+  const bf16* qb = (const bf16*)q;
+  const bf16* kb = (const bf16*)k;
+  const bf16* vb = (const bf16*)v;
+  const bf16* dob = (const bf16*)dout;
+  float* Dd = (float*)(ws + w.Dd);
+  float* lse2 = (float*)(ws + w.lse2);
+  float* part = w.nsplit > 1 ? (float*)(ws + w.part) : nullptr;
+  bf16* dsb = with_ds ? (bf16*)(ws + w.ds) : nullptr;
+  float* dqacc = (float*)(ws + w.dqacc);
+  hipError_t e;
+  // Block 0: one row-dot launch, one dK/dV launch and one reduction over the queries of all
+  // steps (the keys of block 0 are seen by every step), which writes its dk/dv rows.
+  if ((e = launch_bwd_rowdot<bf16>(sa, (const bf16*)o, dob, Dd, lse, lse2, st)) != hipSuccess)
+    return TTT_E_HIP;
+  if ((e = launch_bwd_dkdv_mfma(sa, qb, kb, vb, dob, lse2, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
+                                w.nsplit, dsb, false, st)) != hipSuccess)
+    return TTT_E_HIP;
+  if (w.nsplit > 1 &&
+      (e = launch_bwd_dkdv_reduce(sa, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
+    return TTT_E_HIP;
+  // Per step, dQ and the suffix.  Blocks t >= 1 get their dK/dV from the suffix kernels of the
+  // steps k >= t: the last step first initialises the fp32 sums of every block, and step t
+  // makes the last contribution to block t, whose rows it writes to dk/dv in bf16.
+  GradAcc ga;
+  ga.dk = (float*)(ws + w.total);
+  ga.dv = (float*)(ws + w.total + gbytes);
   for (int kk = p->ttt_step; kk >= 0; --kk) {
-    ga.add = kk < p->ttt_step;
-    ga.final_block = kk;
-    rc = run_bwd(&pb, sweep_shape(p, kk), (const bf16*)q + kk * qel, k, v, seq_T,
-                 (const bf16*)o + kk * qel, lse + kk * rows, (const bf16*)dout + kk * qel,
-                 (bf16*)dq + kk * qel, dk, dv, ws, ga, st);
-    if (rc != TTT_OK) return rc;
+    const Shape s = sweep_shape(p, kk);
+    bf16* dqk = (bf16*)dq + kk * qel;
+    void* dq_causal = kk == 0 ? (void*)dqk : (void*)dqacc;
+    if (with_ds)
+      e = launch_bwd_dq_ds(s, kb, dsb + kk * ds_step_elems(s), seq_T, dq_causal, kk == 0, st);
+    else
+      e = launch_bwd_dq_mfma(s, qb + kk * qel, kb, vb, dob + kk * qel, lse + kk * rows,
+                             Dd + kk * rows, seq_T, dq_causal, kk == 0, false, st);
+    if (e != hipSuccess) return TTT_E_HIP;
+    if (kk > 0) {
+      ga.add = kk < p->ttt_step;
+      ga.final_block = kk;
+      e = launch_bwd_suffix<bf16>(s, qb + kk * qel, kb, vb, dob + kk * qel, lse + kk * rows,
+                                  Dd + kk * rows, seq_T, dqacc, dqk, (bf16*)dk, (bf16*)dv, ga, st);
+      if (e != hipSuccess) return TTT_E_HIP;
+    }
   }
   return TTT_OK;
 }

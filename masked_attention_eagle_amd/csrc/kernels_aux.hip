@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ o,
 template <typename T>
 hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* Dd,
                              const float* lse, float* lse2, hipStream_t st) {
-  const size_t nrows = (size_t)s.B * s.Hq * s.L;
+  const size_t nrows = (size_t)s.B * s.Hq * s.L * s.nst;
   const dim3 grid((unsigned)((nrows + 15) / 16));
   LaunchTimer timer("bwd_rowdot", st);
   if (s.D == 64)

@@ -24,8 +24,9 @@ constexpr int BD = 128;  // head dim of the matrix-core path
 //   P  = exp2(S * scale*log2e - lse*log2e), dS = P * (dP - D)   (lse*log2e precomputed)
 //   dV += P^T dO,  dK += dS^T Q       (A operands straight from the S/dP accumulators,
 //                                      B = dO / Q columns through transposing LDS reads)
-// With nsplit > 1 the query heads of a group are split over nsplit workgroups that write
-// fp32 partial sums, reduced afterwards in split order.
+// With s.nst > 1 (whole TTT) the query tiles of every step pass through the same workgroup:
+// the (step, head) pairs of the group act as G * nst heads.  With nsplit > 1 those pairs are
+// split over nsplit workgroups that write fp32 partial sums, reduced afterwards in split order.
 // ----------------------------------------------------------------------------------------
 constexpr int KBN = 128;  // keys per tile
 constexpr int KBM = 32;   // queries per tile
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, bf16* __restrict__ dk, bf16* __restrict__ dv,
-    float* __restrict__ part, int nsplit, bf16* __restrict__ ds_out, GradAcc ga, Shape s) {
+    float* __restrict__ part, int nsplit, bf16* __restrict__ ds_out, Shape s) {
   // Two stages in distinct arrays (the copy into one never stalls reads of the other).
   __shared__ __attribute__((aligned(1024))) bf16 sQ0[KBM * BD];
   __shared__ __attribute__((aligned(1024))) bf16 sO0[KBM * BD];
@@ -122,8 +123,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
   const int b = bg / s.Hkv;
   const int T = clamp_T(seq_T, b, s.L);
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int hpg = s.G / nsp;
-  const int h_begin = (bg % s.Hkv) * s.G + split * hpg;
+  const int hpg = s.G * s.nst / nsp;      // (step, head) pairs of this workgroup
+  const int hg0 = (bg % s.Hkv) * s.G;     // the group's first query head
+  const int vh_begin = split * hpg;
   const size_t krow0 = (size_t)tblk * s.L;  // first K/V row of the block
   const float c2 = s.scale_log2;
   const FragOffsets fo = make_frag_offsets(lane);
@@ -157,19 +159,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const int nq = max(q_end - q_first, 0) / KBM;
     const int total = nq * hpg;
 
-    // Tile `it` is (head h_begin + it / nq, query rows q_first + (it % nq) * KBM ..); the loop
-    // carries that position and steps it without dividing.
+    // Tile `it` is (pair vh = vh_begin + it / nq, query rows q_first + (it % nq) * KBM ..),
+    // where pair vh is step j = vh / G and head hg0 + hh, hh = vh % G; the loop carries that
+    // position and steps it without dividing.
     struct Pos {
-      int h, q0;
-      size_t row0;   // (b * Hq + h) * L + q0
-      size_t dsrow;  // dS block index of (head h, query block q0 / 32, key block 0)
+      int j, hh, q0;
+      size_t row0;   // ((j * B + b) * Hq + hg0 + hh) * L + q0
+      size_t dsrow;  // dS block index of (step j, that head, query block q0 / 32, key block 0)
     };
-    auto make_pos = [&](int h, int q0) -> Pos {
-      const int bh = b * s.Hq + h;
-      return Pos{h, q0, (size_t)bh * s.L + q0, ds_block_index(s, bh, q0 / 32, 0)};
+    auto make_pos = [&](int j, int hh, int q0) -> Pos {
+      const int sbh = (j * s.B + b) * s.Hq + hg0 + hh;
+      return Pos{j, hh, q0, (size_t)sbh * s.L + q0, ds_block_index(s, sbh, q0 / 32, 0)};
     };
     auto next_pos = [&](Pos p) -> Pos {
-      if (p.q0 + KBM >= q_end) return make_pos(p.h + 1, q_first);
+      if (p.q0 + KBM >= q_end)
+        return p.hh + 1 < s.G ? make_pos(p.j, p.hh + 1, q_first) : make_pos(p.j + 1, 0, q_first);
       p.dsrow += p.q0 / 32 + 1;  // query block r holds r + 1 key blocks
       p.q0 += KBM;
       p.row0 += KBM;
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
       __syncthreads();
     };
 
-    Pos pos = make_pos(h_begin, q_first);
+    Pos pos = make_pos(vh_begin / s.G, vh_begin % s.G, q_first);
     if (total > 0) issue(pos, sQ0, sO0, sLD0);
     wait_vmem();
     __syncthreads();
@@ -285,37 +289,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     int lo = lane;
     asm volatile("" : "+v"(lo));
     const int ohi = lo >> 5, ol32 = lo & 31;
-    if (nsp == 1 && ga.dk && ga.final_block != 0) {  // sweep: fp32 sums over the TTT steps
-      float* akp = ga.dk + ((size_t)bg * s.KV + kw) * BD;
-      float* avp = ga.dv + ((size_t)bg * s.KV + kw) * BD;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int o = acc_row(i, ohi) * BD + 32 * u + ol32;
-          const float xk = dKacc[u][i] * s.scale, xv = dVacc[u][i];
-          akp[o] = ga.add ? akp[o] + xk : xk;
-          avp[o] = ga.add ? avp[o] + xv : xv;
-        }
-      }
-    } else if (nsp == 1) {
+    if (nsp == 1) {
       bf16* dkp = dk + ((size_t)bg * s.KV + krow0 + kw) * BD;
       bf16* dvp = dv + ((size_t)bg * s.KV + krow0 + kw) * BD;
-      // a sweep's last step for block 0 adds the fp32 sums of the other steps
-      const float* akp = (ga.dk && ga.add) ? ga.dk + ((size_t)bg * s.KV + kw) * BD : nullptr;
-      const float* avp = (ga.dk && ga.add) ? ga.dv + ((size_t)bg * s.KV + kw) * BD : nullptr;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int o = acc_row(i, ohi) * BD + 32 * u + ol32;
-          float xk = dKacc[u][i] * s.scale, xv = dVacc[u][i];
-          if (akp) {
-            xk += akp[o];
-            xv += avp[o];
-          }
-          dkp[o] = (bf16)xk;
-          dvp[o] = (bf16)xv;
+          dkp[o] = (bf16)(dKacc[u][i] * s.scale);
+          dvp[o] = (bf16)dVacc[u][i];
         }
       }
     } else {
@@ -338,26 +321,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse2, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
-                                int nsplit, bf16* ds_out, GradAcc ga, bool dense_diagonal,
-                                hipStream_t st) {
+                                int nsplit, bf16* ds_out, bool dense_diagonal, hipStream_t st) {
   const int pairs = s.B * s.Hkv * nsplit * ((s.L / KBN + 1) / 2);
   LaunchTimer timer("bwd_dkdv_mfma", st);
   if (dense_diagonal && s.step > 0) {
     const dim3 grid(pairs + s.B * s.Hkv * (s.L / KBN) * s.step);
     bwd_dkdv_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, v, dout, lse2, Dd, seq_T, dk, dv, part,
-                                                     nsplit, nullptr, ga, s);
+                                                     nsplit, nullptr, s);
     return hipGetLastError();
   }
   bwd_dkdv_mfma_kernel<false><<<dim3(pairs), 256, 0, st>>>(q, k, v, dout, lse2, Dd, seq_T, dk, dv,
-                                                           part, nsplit, ds_out, ga, s);
+                                                           part, nsplit, ds_out, s);
   return hipGetLastError();
 }
 
 // Sum of the nsplit partial dK/dV planes, in split order, into block 0 of dk/dv.
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
                                                           int nsplit, bf16* __restrict__ dk,
-                                                          bf16* __restrict__ dv, GradAcc ga,
-                                                          Shape s) {
+                                                          bf16* __restrict__ dv, Shape s) {
   const size_t plane = (size_t)s.B * s.Hkv * s.L * BD;
   const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e0 >= 2 * plane) return;
@@ -367,14 +348,6 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
   for (int sp = 1; sp < nsplit; ++sp)
     acc += *reinterpret_cast<const f32x4*>(part + (size_t)sp * 2 * plane + (is_v ? plane : 0) + e);
   const size_t bg = e / ((size_t)s.L * BD), rem = e % ((size_t)s.L * BD);
-  if (ga.dk) {  // sweep: fp32 sums over the TTT steps; block 0's last step writes the outputs
-    f32x4* a = reinterpret_cast<f32x4*>((is_v ? ga.dv : ga.dk) + bg * s.KV * BD + rem);
-    if (ga.add) acc += *a;
-    if (ga.final_block != 0) {
-      *a = acc;
-      return;
-    }
-  }
   bf16x4 w;
 #pragma unroll
   for (int j = 0; j < 4; ++j) w[j] = (bf16)acc[j];
@@ -382,11 +355,11 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
 }
 
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
-                                  bf16* dv, GradAcc ga, hipStream_t st) {
+                                  bf16* dv, hipStream_t st) {
   const size_t n4 = (size_t)s.B * s.Hkv * s.L * BD * 2 / 4;
   const dim3 grid((unsigned)((n4 + 255) / 256));
   LaunchTimer timer("bwd_dkdv_reduce", st);
-  dkdv_reduce_kernel<<<grid, 256, 0, st>>>(part, nsplit, dk, dv, ga, s);
+  dkdv_reduce_kernel<<<grid, 256, 0, st>>>(part, nsplit, dk, dv, s);
   return hipGetLastError();
 }
 

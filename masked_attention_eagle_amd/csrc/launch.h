@@ -33,11 +33,11 @@ hipError_t launch_fwd_suffix(const Shape& s, const T* q, const T* k, const T* v,
                              const int32_t* seq_T, const float* oc, const float* lsec, T* o,
                              float* lse, hipStream_t st);
 
-// fp32 accumulation of dK/dV over the steps of a TTT sweep: with dk non-null the backward
-// kernels store (add == 0) or add (add != 0) their dK/dV rows there instead of writing the
-// bf16 outputs.  Rows a step does not own are left alone.  The rows of block final_block get
-// their last contribution in this step: they go to the bf16 outputs (sum + contribution,
-// rounded once) instead.
+// fp32 accumulation over the steps of a TTT sweep of the dK/dV rows of blocks 1..k (the
+// suffix kernel's rows): with dk non-null the suffix kernel stores (add == 0) or adds
+// (add != 0) its dK/dV rows there instead of writing the bf16 outputs.  The rows of block
+// final_block get their last contribution in this step: they go to the bf16 outputs (sum +
+// contribution, rounded once) instead.
 struct GradAcc {
   float* dk = nullptr;
   float* dv = nullptr;
@@ -54,10 +54,9 @@ hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* D
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse2, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
-                                int nsplit, bf16* ds_out, GradAcc ga, bool dense_diagonal,
-                                hipStream_t st);
+                                int nsplit, bf16* ds_out, bool dense_diagonal, hipStream_t st);
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
-                                  bf16* dv, GradAcc ga, hipStream_t st);
+                                  bf16* dv, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                               const bf16* dout, const float* lse, const float* Dd,
                               const int32_t* seq_T, void* dq, bool final_out,
