@@ -149,9 +149,10 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
  * blocks 1..k diagonal).  The forward writes o and lse of every step.  The backward writes dq
  * of every step and the total gradient of the cache, dk/dv = sum over the steps k of step
  * k's dK/dV (block t receives the diagonal gradients of every step k >= t, block 0 the causal
- * gradient of all of them); every sum is kept in fp32 (block 0's inside one dK/dV launch over
- * the queries of all steps, blocks 1..k in the workspace) and rounded to bf16 once.  The
- * backward's workspace holds D, lse * log2(e) and (stored-dS path) the dS blocks of every step.
+ * gradient of all of them); every sum is kept in fp32 inside the kernels (block 0's in one
+ * dK/dV launch over the queries of all steps, blocks 1..k in one suffix launch over all steps)
+ * and rounded to bf16 once.  The backward's workspace holds D, lse * log2(e), the fp32 block-0
+ * dQ of steps 1..k and (stored-dS path) the dS blocks of every step.
  * Launches run in order on `stream`; flags select the paths as for the per-step calls.
  * Same error codes; fp32 data returns TTT_E_UNSUPPORTED.
  */

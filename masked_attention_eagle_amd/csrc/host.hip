@@ -163,7 +163,7 @@ struct BwdLayout {
 // D; (bf16) lse * log2(e) for the dK/dV kernel and the split dK/dV partials (heads of a group
 // over several workgroups); the dS blocks of block 0 when the dQ kernel reads them; for k > 0
 // the fp32 dQ accumulator that the suffix kernel finalises.  D, lse * log2(e) and dS are held
-// for each of the s.nst steps; the dQ accumulator serves one step at a time.
+// for each of the s.nst steps, and (whole TTT) the dQ accumulators of steps 1..nst-1.
 size_t ds_step_elems(const Shape& s) {
   const size_t n = s.L / 32;
   return (size_t)s.B * s.Hq * (n * (n + 1) / 2) * 32 * 32;
@@ -190,7 +190,7 @@ BwdLayout bwd_layout(const Shape& s, int dtype, bool with_ds, bool dense = false
   }
   if (s.step > 0 && !dense) {
     w.dqacc = off;
-    off += round_up(rows_1 * s.D * 4);
+    off += round_up(rows_1 * s.D * 4 * (s.nst > 1 ? s.nst - 1 : 1));
   }
   w.total = off;
   return w;
@@ -303,7 +303,7 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     if (e != hipSuccess) return TTT_E_HIP;
     if (!final_causal)
       e = launch_bwd_suffix<bf16>(s, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq, (bf16*)dk,
-                                  (bf16*)dv, GradAcc{}, st);
+                                  (bf16*)dv, st);
   } else {
     const float* qf = (const float*)q;
     const float* kf = (const float*)k;
@@ -319,7 +319,7 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
       return TTT_E_HIP;
     if (!final_causal)
       e = launch_bwd_suffix<float>(s, qf, kf, vf, dof, lse, Dd, seq_T, dqacc, (float*)dq,
-                                   (float*)dk, (float*)dv, GradAcc{}, st);
+                                   (float*)dk, (float*)dv, st);
   }
   return hip_status(e);
 }
@@ -349,9 +349,6 @@ Shape sweep_all_shape(const ttt_attn_params* p) {
   Shape s = make_shape(p);
   s.nst = p->ttt_step + 1;
   return s;
-}
-size_t sweep_grad_elems(const ttt_attn_params* p) {  // elements of dk (or dv)
-  return (size_t)p->batch * p->heads_kv * (size_t)(p->ttt_step + 1) * p->q_len * p->head_dim;
 }
 
 }  // namespace
@@ -402,8 +399,7 @@ size_t ttt_attn_fwd_sweep_workspace_size(const ttt_attn_params* p) {
 size_t ttt_attn_bwd_sweep_workspace_size(const ttt_attn_params* p) {
   if (validate(p) != TTT_OK || p->dtype != TTT_DTYPE_BF16) return 0;
   const ttt_attn_params pb = sweep_bwd_params(p);
-  return bwd_layout(sweep_all_shape(p), p->dtype, stored_ds(&pb)).total +
-         2 * round_up(sweep_grad_elems(p) * 4);
+  return bwd_layout(sweep_all_shape(p), p->dtype, stored_ds(&pb)).total;
 }
 
 int ttt_attn_fwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
@@ -442,8 +438,7 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
   const bool with_ds = stored_ds(&pb);
   const Shape sa = sweep_all_shape(p);
   const BwdLayout w = bwd_layout(sa, p->dtype, with_ds);
-  const size_t gbytes = round_up(sweep_grad_elems(p) * 4);
-  if (workspace_bytes < w.total + 2 * gbytes) return TTT_E_WORKSPACE;
+  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || !aligned16(workspace))
@@ -472,30 +467,22 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
   if (w.nsplit > 1 &&
       (e = launch_bwd_dkdv_reduce(sa, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
     return TTT_E_HIP;
-  // Per step, dQ and the suffix.  Blocks t >= 1 get their dK/dV from the suffix kernels of the
-  // steps k >= t: the last step first initialises the fp32 sums of every block, and step t
-  // makes the last contribution to block t, whose rows it writes to dk/dv in bf16.
-  GradAcc ga;
-  ga.dk = (float*)(ws + w.total);
-  ga.dv = (float*)(ws + w.total + gbytes);
-  for (int kk = p->ttt_step; kk >= 0; --kk) {
+  // Per step, the block-0 dQ: final for step 0, into its fp32 accumulator for the others.
+  for (int kk = 0; kk <= p->ttt_step; ++kk) {
     const Shape s = sweep_shape(p, kk);
-    bf16* dqk = (bf16*)dq + kk * qel;
-    void* dq_causal = kk == 0 ? (void*)dqk : (void*)dqacc;
+    void* dq_causal = kk == 0 ? (void*)((bf16*)dq) : (void*)(dqacc + (kk - 1) * qel);
     if (with_ds)
       e = launch_bwd_dq_ds(s, kb, dsb + kk * ds_step_elems(s), seq_T, dq_causal, kk == 0, st);
     else
       e = launch_bwd_dq_mfma(s, qb + kk * qel, kb, vb, dob + kk * qel, lse + kk * rows,
                              Dd + kk * rows, seq_T, dq_causal, kk == 0, false, st);
     if (e != hipSuccess) return TTT_E_HIP;
-    if (kk > 0) {
-      ga.add = kk < p->ttt_step;
-      ga.final_block = kk;
-      e = launch_bwd_suffix<bf16>(s, qb + kk * qel, kb, vb, dob + kk * qel, lse + kk * rows,
-                                  Dd + kk * rows, seq_T, dqacc, dqk, (bf16*)dk, (bf16*)dv, ga, st);
-      if (e != hipSuccess) return TTT_E_HIP;
-    }
   }
+  // Blocks 1..K-1 and the diagonal part of dQ: one launch over every step.
+  if (p->ttt_step > 0 &&
+      (e = launch_bwd_suffix_sweep(sa, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq,
+                                   (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
+    return TTT_E_HIP;
   return TTT_OK;
 }
 

@@ -31,30 +31,6 @@ constexpr int BD = 128;  // head dim of the matrix-core path
 constexpr int KBN = 128;  // keys per tile
 constexpr int KBM = 32;   // queries per tile
 
-// One dK or dV row slice of a suffix key: bf16 output, or (TTT sweep) the fp32 sum, whose
-// final value (fin: the row's last contribution) goes to the output instead.
-template <typename T, int E>
-__device__ __forceinline__ void put_grad_row(T* out, float* acc, int add, bool fin, size_t idx,
-                                             const float* x) {
-  if (acc) {
-    float a[E];
-    if (add) {
-      load_vec<float, E>(acc + idx, a);
-#pragma unroll
-      for (int e = 0; e < E; ++e) a[e] += x[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) a[e] = x[e];
-    }
-    if (fin)
-      store_vec<T, E>(out + idx, a);
-    else
-      store_vec<float, E>(acc + idx, a);
-  } else {
-    store_vec<T, E>(out + idx, x);
-  }
-}
-
 // dS hand-over between the dK/dV kernel and the dQ kernel.  dS of one head is kept in
 // 32 x 32 blocks (32 query rows x 32 keys of block 0); only blocks on or below the diagonal
 // exist, packed row after row (query block r holds key blocks 0..r).
@@ -871,14 +847,12 @@ template hipError_t launch_bwd_dq_valu<float>(const Shape&, const float*, const 
 // Two passes (dQ head by head, then dK/dV key row by key row) keep the register footprint
 // independent of the group size; the second pass re-reads q/dO from cache.
 // ----------------------------------------------------------------------------------------
-// ACC: the TTT sweep's fp32 dK/dV sums (ga) are in use; without it ga is ignored.
-template <typename T, int D, bool ACC>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_suffix_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, const float* __restrict__ dq_acc, T* __restrict__ dq,
-    T* __restrict__ dk, T* __restrict__ dv, GradAcc ga_arg, Shape s) {
-  const GradAcc ga = ACC ? ga_arg : GradAcc{};
+    T* __restrict__ dk, T* __restrict__ dv, Shape s) {
   constexpr int E = D / 16;
   const int sub = threadIdx.x & 15;
   const int blocks_per_bg = (s.L + 15) / 16;
@@ -954,24 +928,20 @@ __global__ __launch_bounds__(256) void bwd_suffix_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[e] *= s.scale;
     }
-    const bool fin = ga.final_block == t;
-    if (live || !ga.add || fin) {  // dead rows: zero, or nothing to add
-      put_grad_row<T, E>(dk, ga.dk, ga.add, fin, kv_base + (size_t)t * s.L * D, aK);
-      put_grad_row<T, E>(dv, ga.dv, ga.add, fin, kv_base + (size_t)t * s.L * D, aV);
-    }
+    store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, aK);
+    store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, aV);
   }
 }
 
 // Single pass with the step loop outside and every head of the group in registers: each
 // diagonal K/V row is read once per (row, group) and its dK/dV row is written right away;
 // dQ of all heads accumulates in registers and is written at the end.
-template <typename T, int D, int G, bool ACC>
+template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, const float* __restrict__ dq_acc, T* __restrict__ dq,
-    T* __restrict__ dk, T* __restrict__ dv, GradAcc ga_arg, Shape s) {
-  const GradAcc ga = ACC ? ga_arg : GradAcc{};
+    T* __restrict__ dk, T* __restrict__ dv, Shape s) {
   constexpr int E = D / 16;
   const int sub = threadIdx.x & 15;
   const int blocks_per_bg = (s.L + 15) / 16;
@@ -1033,9 +1003,8 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[e] *= s.scale;
-      const bool fin = ga.final_block == t;
-      put_grad_row<T, E>(dk, ga.dk, ga.add, fin, kv_base + (size_t)t * s.L * D, aK);
-      put_grad_row<T, E>(dv, ga.dv, ga.add, fin, kv_base + (size_t)t * s.L * D, aV);
+      store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, aK);
+      store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, aV);
       if (t < s.step) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -1044,17 +1013,13 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
         }
       }
     }
-  } else if (!ga.add || ga.final_block >= 1) {
-    // rows no query sees: zero (in a sweep's later steps nothing to add, except the rows of
-    // the block that is final in this step, which go to the outputs)
+  } else {  // rows no query sees: zero
     float z[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) z[e] = 0.f;
     for (int t = 1; t <= s.step; ++t) {
-      const bool fin = ga.final_block == t;
-      if (ga.add && !fin) continue;
-      put_grad_row<T, E>(dk, ga.dk, 0, fin, kv_base + (size_t)t * s.L * D, z);
-      put_grad_row<T, E>(dv, ga.dv, 0, fin, kv_base + (size_t)t * s.L * D, z);
+      store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, z);
+      store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, z);
     }
   }
 #pragma unroll
@@ -1068,49 +1033,149 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
   }
 }
 
-template <typename T, int D, bool ACC>
-static void bwd_suffix_launch(const Shape& s, dim3 grid, hipStream_t st, const T* q,
-                              const T* k, const T* v, const T* dout, const float* lse,
-                              const float* Dd, const int32_t* seq_T, const float* dq_acc,
-                              T* dq, T* dk, T* dv, GradAcc ga) {
-  switch (s.G) {
-    case 1: bwd_suffix_g_kernel<T, D, 1, ACC><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
-    case 2: bwd_suffix_g_kernel<T, D, 2, ACC><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
-    case 4: bwd_suffix_g_kernel<T, D, 4, ACC><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
-    case 8: bwd_suffix_g_kernel<T, D, 8, ACC><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
-    default: bwd_suffix_kernel<T, D, ACC><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga, s); break;
-  }
-}
 template <typename T, int D>
 static hipError_t bwd_suffix_dispatch(const Shape& s, dim3 grid, hipStream_t st, const T* q,
                                       const T* k, const T* v, const T* dout, const float* lse,
                                       const float* Dd, const int32_t* seq_T, const float* dq_acc,
-                                      T* dq, T* dk, T* dv, GradAcc ga) {
-  if (ga.dk)
-    bwd_suffix_launch<T, D, true>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga);
-  else
-    bwd_suffix_launch<T, D, false>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga);
+                                      T* dq, T* dk, T* dv) {
+  switch (s.G) {
+    case 1: bwd_suffix_g_kernel<T, D, 1><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 2: bwd_suffix_g_kernel<T, D, 2><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 4: bwd_suffix_g_kernel<T, D, 4><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 8: bwd_suffix_g_kernel<T, D, 8><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    default: bwd_suffix_kernel<T, D><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+  }
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_bwd_suffix(const Shape& s, const T* q, const T* k, const T* v, const T* dout,
                              const float* lse, const float* Dd, const int32_t* seq_T,
-                             const float* dq_acc, T* dq, T* dk, T* dv, GradAcc ga,
-                             hipStream_t st) {
+                             const float* dq_acc, T* dq, T* dk, T* dv, hipStream_t st) {
   const dim3 grid(s.B * s.Hkv * ((s.L + 15) / 16));
   LaunchTimer timer("bwd_suffix", st);
   if (s.D == 64)
-    return bwd_suffix_dispatch<T, 64>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga);
-  return bwd_suffix_dispatch<T, 128>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, ga);
+    return bwd_suffix_dispatch<T, 64>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv);
+  return bwd_suffix_dispatch<T, 128>(s, grid, st, q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv);
 }
 template hipError_t launch_bwd_suffix<float>(const Shape&, const float*, const float*,
                                              const float*, const float*, const float*,
                                              const float*, const int32_t*, const float*, float*,
-                                             float*, float*, GradAcc, hipStream_t);
+                                             float*, float*, hipStream_t);
 template hipError_t launch_bwd_suffix<bf16>(const Shape&, const bf16*, const bf16*, const bf16*,
                                             const bf16*, const float*, const float*,
                                             const int32_t*, const float*, bf16*, bf16*, bf16*,
-                                            GradAcc, hipStream_t);
+                                            hipStream_t);
+
+// ----------------------------------------------------------------------------------------
+// Whole-TTT suffix backward (bf16, d = 128): one group of 16 lanes per (b, KV group, row i)
+// takes the diagonal keys r = t*Q_LEN + i of every block t = 1..K-1 for the queries of every
+// step k >= t (same per-key terms as the per-step kernels above).  Blocks go in chunks of
+// NB whose dK/dV rows accumulate in registers over the steps and heads and are written once;
+// steps run in the outer loop, so a step's dQ row (its fp32 block-0 part from dq_acc plus the
+// diagonal terms) is complete in the chunk that holds its last block k, and goes back to
+// dq_acc in fp32 from the chunks before that one.
+// Layouts: q, dO, dq [K, B, Hq, Q_LEN, d]; lse, Dd [K, B, Hq, Q_LEN]; dq_acc of steps
+// 1..K-1 [K-1, B, Hq, Q_LEN, d] fp32; k, v, dk, dv the cache [B, Hkv, K*Q_LEN, d]; s.step =
+// K-1, s.KV = K*Q_LEN.  dQ of step 0 has no diagonal term and is not touched.
+// ----------------------------------------------------------------------------------------
+template <int NB>
+__global__ __launch_bounds__(256) void bwd_suffix_sweep_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
+    const int32_t* __restrict__ seq_T, float* __restrict__ dq_acc, bf16* __restrict__ dq,
+    bf16* __restrict__ dk, bf16* __restrict__ dv, Shape s) {
+  constexpr int E = BD / 16;
+  const int sub = threadIdx.x & 15;
+  const int blocks_per_bg = (s.L + 15) / 16;
+  const int bg = blockIdx.x / blocks_per_bg;
+  const int i = (blockIdx.x % blocks_per_bg) * 16 + (threadIdx.x >> 4);
+  if (i >= s.L) return;
+  const int b = bg / s.Hkv, g = bg % s.Hkv;
+  const bool live = i < clamp_T(seq_T, b, s.L);
+  const size_t kv_base = ((size_t)bg * s.KV + i) * BD + sub * E;
+  const size_t step_rows = (size_t)s.B * s.Hq * s.L;
+  const size_t row_g = (size_t)(b * s.Hq + g * s.G) * s.L + i;  // head g*G, step 0
+  const int nblk = s.step;
+
+  for (int t0 = 1; t0 <= nblk; t0 += NB) {
+    const int nb = min(NB, nblk - t0 + 1);  // blocks t0 .. t0 + nb - 1
+    float aK[NB][E], aV[NB][E];
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+#pragma unroll
+      for (int e = 0; e < E; ++e) aK[c][e] = aV[c][e] = 0.f;
+    for (int kk = t0; kk <= nblk; ++kk) {  // steps k >= t0 reach blocks t0 .. min(k, t0 + nb - 1)
+      const int reach = min(kk - t0 + 1, nb);
+      const bool last = kk < t0 + nb;  // no later chunk holds a block <= kk
+      for (int h = 0; h < s.G; ++h) {
+        const size_t hrow = row_g + (size_t)h * s.L;
+        const size_t row = (size_t)kk * step_rows + hrow;
+        float* accp = dq_acc + ((size_t)(kk - 1) * step_rows + hrow) * BD + sub * E;
+        float dqa[E];  // sum over the chunk's blocks of ds * k (the per-step kernels' order)
+#pragma unroll
+        for (int e = 0; e < E; ++e) dqa[e] = 0.f;
+        if (live) {
+          float qv[E], ov[E];
+          load_vec<bf16, E>(q + row * BD + sub * E, qv);
+          load_vec<bf16, E>(dO + row * BD + sub * E, ov);
+          const float l2 = lse[row] * kLog2e, Di = Dd[row];
+#pragma unroll
+          for (int c = 0; c < NB; ++c) {
+            if (c < reach) {
+              float kc[E], vc[E];
+              load_vec<bf16, E>(k + kv_base + (size_t)(t0 + c) * s.L * BD, kc);
+              load_vec<bf16, E>(v + kv_base + (size_t)(t0 + c) * s.L * BD, vc);
+              float sd = 0.f, pd = 0.f;
+#pragma unroll
+              for (int e = 0; e < E; ++e) {
+                sd += qv[e] * kc[e];
+                pd += ov[e] * vc[e];
+              }
+              sd = sum16(sd);
+              pd = sum16(pd);
+              const float p = exp2_fast(sd * s.scale_log2 - l2);
+              const float ds = p * (pd - Di);
+#pragma unroll
+              for (int e = 0; e < E; ++e) {
+                aV[c][e] += p * ov[e];
+                aK[c][e] += ds * qv[e];
+                dqa[e] += ds * kc[e];
+              }
+            }
+          }
+        }
+        float a[E];
+        load_vec<float, E>(accp, a);
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[e] += s.scale * dqa[e];
+        if (last)
+          store_vec<bf16, E>(dq + row * BD + sub * E, a);
+        else
+          store_vec<float, E>(accp, a);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      if (c < nb) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) aK[c][e] *= s.scale;
+        store_vec<bf16, E>(dk + kv_base + (size_t)(t0 + c) * s.L * BD, aK[c]);
+        store_vec<bf16, E>(dv + kv_base + (size_t)(t0 + c) * s.L * BD, aV[c]);
+      }
+    }
+  }
+}
+
+hipError_t launch_bwd_suffix_sweep(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
+                                   const bf16* dout, const float* lse, const float* Dd,
+                                   const int32_t* seq_T, float* dq_acc, bf16* dq, bf16* dk,
+                                   bf16* dv, hipStream_t st) {
+  const dim3 grid(s.B * s.Hkv * ((s.L + 15) / 16));
+  LaunchTimer timer("bwd_suffix_sweep", st);
+  bwd_suffix_sweep_kernel<6><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk,
+                                                   dv, s);
+  return hipGetLastError();
+}
 
 }  // namespace ttt

@@ -33,17 +33,6 @@ hipError_t launch_fwd_suffix(const Shape& s, const T* q, const T* k, const T* v,
                              const int32_t* seq_T, const float* oc, const float* lsec, T* o,
                              float* lse, hipStream_t st);
 
-// fp32 accumulation over the steps of a TTT sweep of the dK/dV rows of blocks 1..k (the
-// suffix kernel's rows): with dk non-null the suffix kernel stores (add == 0) or adds
-// (add != 0) its dK/dV rows there instead of writing the bf16 outputs.  The rows of block
-// final_block get their last contribution in this step: they go to the bf16 outputs (sum +
-// contribution, rounded once) instead.
-struct GradAcc {
-  float* dk = nullptr;
-  float* dv = nullptr;
-  int add = 0;
-  int final_block = -1;
-};
 
 // Backward.
 // D = rowsum(dout * o); with lse2 set also lse2 = lse * log2(e).
@@ -74,8 +63,14 @@ hipError_t launch_bwd_dq_valu(const Shape& s, const T* q, const T* k, const T* v
 template <typename T>
 hipError_t launch_bwd_suffix(const Shape& s, const T* q, const T* k, const T* v, const T* dout,
                              const float* lse, const float* Dd, const int32_t* seq_T,
-                             const float* dq_acc, T* dq, T* dk, T* dv, GradAcc ga,
-                             hipStream_t st);
+                             const float* dq_acc, T* dq, T* dk, T* dv, hipStream_t st);
+// Whole TTT (s.step = K - 1, s.KV = K * L): the diagonal keys of blocks 1..K-1 for the queries
+// of steps 1..K-1 (stacked step after step); dq_acc holds the fp32 block-0 dQ of steps
+// 1..K-1 and is overwritten; writes dq of steps 1..K-1 and dk/dv of blocks 1..K-1.
+hipError_t launch_bwd_suffix_sweep(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
+                                   const bf16* dout, const float* lse, const float* Dd,
+                                   const int32_t* seq_T, float* dq_acc, bf16* dq, bf16* dk,
+                                   bf16* dv, hipStream_t st);
 
 // In-place masked softmax-loss gradient.
 template <typename T>

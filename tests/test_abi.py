@@ -175,9 +175,9 @@ def test_oracle_is_not_imported_by_the_product():
 
 def test_sweep_workspace_and_errors():
     """The sweep's backward workspace: D and lse * log2(e) rows and the dS blocks of every step
-    (one dK/dV launch covers all steps), the split dK/dV partials, one step's fp32 dQ
-    accumulator and the two fp32 gradient sums of the cache; fp32 data is not supported;
-    errors come before any launch."""
+    (one dK/dV launch covers all steps), the split dK/dV partials and the fp32 dQ accumulators
+    of steps 1..K-1 (one suffix launch covers all steps); fp32 data is not supported; errors
+    come before any launch."""
     lib = A.load()
     B, Hq, Hkv, L, d, K = 2, 32, 8, 4096, 128, 7
     p = P(step=K - 1)
@@ -186,20 +186,18 @@ def test_sweep_workspace_and_errors():
     ds_step = B * Hq * n * (n + 1) // 2 * 32 * 32 * 2
     # 2 x 8 x 16 = 256 pair workgroups: the 4 x 7 (step, head) pairs of a KV group split in two
     part = 2 * 2 * B * Hkv * L * d * 4
-    sums = 2 * B * Hkv * K * L * d * 4
-    whole = K * rows * 8 + part + K * ds_step + rows * d * 4
-    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(p)) == whole + sums
+    whole = K * rows * 8 + part + K * ds_step + (K - 1) * rows * d * 4
+    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(p)) == whole
     rec = P(step=K - 1, flags=A.TTT_FLAG_RECOMPUTE_DQ)
-    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(rec)) == whole - K * ds_step + sums
-    one = P(step=0)  # a single step: no dQ accumulator, no suffix sums beyond block 0
-    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(one)) == (
-        rows * 8 + part + ds_step + 2 * B * Hkv * L * d * 4)
+    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(rec)) == whole - K * ds_step
+    one = P(step=0)  # a single step: no dQ accumulator
+    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(one)) == rows * 8 + part + ds_step
     assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(p)) == 0  # fused forward
     sep = P(step=K - 1, flags=A.TTT_FLAG_SEPARATE_SUFFIX)
     assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(sep)) == A.fwd_workspace_size(sep)
     # the whole-TTT backward ignores the dense-diagonal variant (same paths, same workspace)
     dense = P(step=K - 1, flags=A.TTT_FLAG_DENSE_DIAGONAL)
-    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(dense)) == whole + sums
+    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(dense)) == whole
     pf = P(step=2, dtype=A.TTT_DTYPE_F32)
     assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(pf)) == 0
     assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(pf)) == 0
