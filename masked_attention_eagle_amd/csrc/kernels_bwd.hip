@@ -1105,10 +1105,39 @@ __global__ __launch_bounds__(256) void bwd_suffix_sweep_kernel(
     for (int c = 0; c < NB; ++c)
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[c][e] = aV[c][e] = 0.f;
-    for (int kk = t0; kk <= nblk; ++kk) {  // steps k >= t0 reach blocks t0 .. min(k, t0 + nb - 1)
+    // (step, head) pairs (kk, h), kk = t0..K-1: steps k >= t0 reach blocks t0 .. min(k, t0 +
+    // nb - 1).  The rows of the next pair are loaded while the current one computes.
+    struct RowIn {
+      bf16x8 qr, orw;
+      float l2, Di;
+      f32x4 a0, a1;
+    };
+    auto load_in = [&](int kk, int h, RowIn& r) {
+      const size_t hrow = row_g + (size_t)h * s.L;
+      const size_t row = (size_t)kk * step_rows + hrow;
+      const float* accp = dq_acc + ((size_t)(kk - 1) * step_rows + hrow) * BD + sub * E;
+      r.a0 = *reinterpret_cast<const f32x4*>(accp);
+      r.a1 = *reinterpret_cast<const f32x4*>(accp + 4);
+      if (live) {
+        r.qr = *reinterpret_cast<const bf16x8*>(q + row * BD + sub * E);
+        r.orw = *reinterpret_cast<const bf16x8*>(dO + row * BD + sub * E);
+        r.l2 = lse[row] * kLog2e;
+        r.Di = Dd[row];
+      }
+    };
+    RowIn cur, nxt;
+    load_in(t0, 0, cur);
+    for (int kk = t0, h = 0;;) {
+      int kn = kk, hn = h + 1;
+      if (hn == s.G) {
+        hn = 0;
+        ++kn;
+      }
+      const bool more = kn <= nblk;
+      if (more) load_in(kn, hn, nxt);
       const int reach = min(kk - t0 + 1, nb);
       const bool last = kk < t0 + nb;  // no later chunk holds a block <= kk
-      for (int h = 0; h < s.G; ++h) {
+      {
         const size_t hrow = row_g + (size_t)h * s.L;
         const size_t row = (size_t)kk * step_rows + hrow;
         float* accp = dq_acc + ((size_t)(kk - 1) * step_rows + hrow) * BD + sub * E;
@@ -1117,9 +1146,12 @@ __global__ __launch_bounds__(256) void bwd_suffix_sweep_kernel(
         for (int e = 0; e < E; ++e) dqa[e] = 0.f;
         if (live) {
           float qv[E], ov[E];
-          load_vec<bf16, E>(q + row * BD + sub * E, qv);
-          load_vec<bf16, E>(dO + row * BD + sub * E, ov);
-          const float l2 = lse[row] * kLog2e, Di = Dd[row];
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            qv[e] = (float)cur.qr[e];
+            ov[e] = (float)cur.orw[e];
+          }
+          const float l2 = cur.l2, Di = cur.Di;
 #pragma unroll
           for (int c = 0; c < NB; ++c) {
             if (c < reach) {
@@ -1145,8 +1177,8 @@ __global__ __launch_bounds__(256) void bwd_suffix_sweep_kernel(
             }
           }
         }
-        float a[E];
-        load_vec<float, E>(accp, a);
+        float a[E] = {cur.a0[0], cur.a0[1], cur.a0[2], cur.a0[3],
+                      cur.a1[0], cur.a1[1], cur.a1[2], cur.a1[3]};
 #pragma unroll
         for (int e = 0; e < E; ++e) a[e] += s.scale * dqa[e];
         if (last)
@@ -1154,6 +1186,10 @@ __global__ __launch_bounds__(256) void bwd_suffix_sweep_kernel(
         else
           store_vec<float, E>(accp, a);
       }
+      if (!more) break;
+      cur = nxt;
+      kk = kn;
+      h = hn;
     }
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
