@@ -33,7 +33,10 @@ def _norm_err(got, ref):
 
 @pytest.mark.parametrize("dq_mode", ["stored", "recompute"])
 @pytest.mark.parametrize("B,Hq,Hkv,L,K,T", [(2, 4, 2, 256, 4, (256, 140)), (1, 8, 2, 128, 3, 77),
-                                             (2, 2, 1, 256, 2, (0, 255))])
+                                             (2, 2, 1, 256, 2, (0, 255)),
+                                             # more diagonal blocks than the suffix kernel keeps
+                                             # in registers at once (6): two and three chunks
+                                             (1, 4, 1, 128, 9, 100), (2, 2, 1, 128, 14, (128, 37))])
 def test_sweep_against_oracle(gpu_lib, B, Hq, Hkv, L, K, T, dq_mode):
     import torch
     d = 128
