@@ -67,3 +67,45 @@ def test_step_replays_in_a_graph(gpu_lib, suffix, dq_mode):
         torch.cuda.synchronize()
         for name, got, ref in zip(("o", "lse", "dq", "dk", "dv"), outs, refs):
             assert torch.equal(got, ref), f"replay {rep}: {name} differs from the eager call"
+
+
+def test_sweep_replays_in_a_graph(gpu_lib):
+    """The whole-TTT calls (forward and backward over every step, one KV cache) captured once
+    and replayed: each replay matches the eager calls bitwise.  Outputs and workspaces come from
+    the capture's memory pool, so they stay in place across replays."""
+    import torch
+    from tests.test_parity_sweep import _sweep_case
+    A = gpu_lib
+    B, Hq, Hkv, d, L, K = 2, 4, 2, 128, 256, 3
+    q, kc, vc, do, T = _sweep_case(77, B, Hq, Hkv, d, L, K, (256, 140))
+    print(f"graph sweep case B={B} Hq={Hq} Hkv={Hkv} L={L} K={K} T={list(T)}", flush=True)
+    bf = torch.bfloat16
+    qd, kd, vd, dod = (to_dev(x, bf) for x in (q, kc, vc, do))
+    Td = torch.as_tensor(T, device="cuda")
+    scale = 1.0 / np.sqrt(d)
+    o_e, lse_e = A.ttt_attn_fwd_sweep(qd, kd, vd, Td, scale)
+    refs = (o_e, lse_e) + tuple(A.ttt_attn_bwd_sweep(qd, kd, vd, Td, o_e, lse_e, dod, scale))
+    torch.cuda.synchronize()
+
+    def step_fn():
+        o, lse = A.ttt_attn_fwd_sweep(qd, kd, vd, Td, scale)
+        return (o, lse) + tuple(A.ttt_attn_bwd_sweep(qd, kd, vd, Td, o, lse, dod, scale))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_fn()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step_fn()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, ref in zip(("o", "lse", "dq", "dk", "dv"), outs, refs):
+            assert torch.equal(got, ref), f"replay {rep}: {name} differs from the eager call"

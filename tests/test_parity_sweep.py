@@ -36,7 +36,9 @@ def _norm_err(got, ref):
                                              (2, 2, 1, 256, 2, (0, 255)),
                                              # more diagonal blocks than the suffix kernel keeps
                                              # in registers at once (6): two and three chunks
-                                             (1, 4, 1, 128, 9, 100), (2, 2, 1, 128, 14, (128, 37))])
+                                             (1, 4, 1, 128, 9, 100), (2, 2, 1, 128, 14, (128, 37)),
+                                             # a single step: block 0 only, no suffix launch
+                                             (1, 4, 2, 128, 1, 100)])
 def test_sweep_against_oracle(gpu_lib, B, Hq, Hkv, L, K, T, dq_mode):
     import torch
     d = 128
