@@ -205,7 +205,7 @@ using namespace ttt;
 
 extern "C" {
 
-int ttt_attn_version(void) { return 101; }
+int ttt_attn_version(void) { return 102; }
 
 const char* ttt_attn_status_string(int status) {
   switch (status) {
