@@ -128,14 +128,13 @@ Shape make_shape(const ttt_attn_params* p) {
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Number of workgroups that share the (step, query head) pairs of one KV group in the dK/dV
-// kernel (each workgroup owns a pair of 128-key tiles): doubled while the grid is below two
-// workgroups per CU and the pairs still split evenly.
+// Number of workgroups that share the query heads of one KV group in the dK/dV kernel (each
+// workgroup owns a pair of 128-key tiles): doubled while the grid is below two workgroups per
+// CU and the group still splits evenly.
 int dkdv_nsplit(const Shape& s) {
   const int64_t base = (int64_t)s.B * s.Hkv * ((s.L / 128 + 1) / 2);
-  const int pairs = s.G * s.nst;
   int n = 1;
-  while (base * n < 512 && n < pairs && pairs % (2 * n) == 0) n *= 2;
+  while (base * n < 512 && n < s.G && s.G % (2 * n) == 0) n *= 2;
   return n;
 }
 

@@ -24,9 +24,10 @@ constexpr int BD = 128;  // head dim of the matrix-core path
 //   P  = exp2(S * scale*log2e - lse*log2e), dS = P * (dP - D)   (lse*log2e precomputed)
 //   dV += P^T dO,  dK += dS^T Q       (A operands straight from the S/dP accumulators,
 //                                      B = dO / Q columns through transposing LDS reads)
-// With s.nst > 1 (whole TTT) the query tiles of every step pass through the same workgroup:
-// the (step, head) pairs of the group act as G * nst heads.  With nsplit > 1 those pairs are
-// split over nsplit workgroups that write fp32 partial sums, reduced afterwards in split order.
+// With s.nst > 1 (whole TTT) the query tiles of every step pass through the same workgroup,
+// step after step.  With nsplit > 1 the query heads of the group are split over nsplit
+// workgroups (each takes its heads at every step, so all workgroups work on the same step at
+// about the same time) that write fp32 partial sums, reduced afterwards in split order.
 // ----------------------------------------------------------------------------------------
 constexpr int KBN = 128;  // keys per tile
 constexpr int KBM = 32;   // queries per tile
@@ -99,9 +100,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
   const int b = bg / s.Hkv;
   const int T = clamp_T(seq_T, b, s.L);
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int hpg = s.G * s.nst / nsp;      // (step, head) pairs of this workgroup
+  const int hps = s.G / nsp;              // query heads of this workgroup, at every step
   const int hg0 = (bg % s.Hkv) * s.G;     // the group's first query head
-  const int vh_begin = split * hpg;
+  const int hh_begin = split * hps;
   const size_t krow0 = (size_t)tblk * s.L;  // first K/V row of the block
   const float c2 = s.scale_log2;
   const FragOffsets fo = make_frag_offsets(lane);
@@ -133,11 +134,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const int q_first = (k0 < T) ? k0 : s.L;
     const int q_end = dwg ? k0 + KBN : s.L;
     const int nq = max(q_end - q_first, 0) / KBM;
-    const int total = nq * hpg;
+    const int total = nq * hps * s.nst;
 
-    // Tile `it` is (pair vh = vh_begin + it / nq, query rows q_first + (it % nq) * KBM ..),
-    // where pair vh is step j = vh / G and head hg0 + hh, hh = vh % G; the loop carries that
-    // position and steps it without dividing.
+    // Tile `it` is (pair p = it / nq, query rows q_first + (it % nq) * KBM ..), where pair p is
+    // step j = p / hps and head hg0 + hh_begin + p % hps; the loop carries that position and
+    // steps it without dividing.
     struct Pos {
       int j, hh, q0;
       size_t row0;   // ((j * B + b) * Hq + hg0 + hh) * L + q0
@@ -149,7 +150,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     };
     auto next_pos = [&](Pos p) -> Pos {
       if (p.q0 + KBM >= q_end)
-        return p.hh + 1 < s.G ? make_pos(p.j, p.hh + 1, q_first) : make_pos(p.j + 1, 0, q_first);
+        return p.hh + 1 < hh_begin + hps ? make_pos(p.j, p.hh + 1, q_first)
+                                         : make_pos(p.j + 1, hh_begin, q_first);
       p.dsrow += p.q0 / 32 + 1;  // query block r holds r + 1 key blocks
       p.q0 += KBM;
       p.row0 += KBM;
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
       __syncthreads();
     };
 
-    Pos pos = make_pos(vh_begin / s.G, vh_begin % s.G, q_first);
+    Pos pos = make_pos(0, hh_begin, q_first);
     if (total > 0) issue(pos, sQ0, sO0, sLD0);
     wait_vmem();
     __syncthreads();

@@ -184,7 +184,7 @@ def test_sweep_workspace_and_errors():
     rows = B * Hq * L
     n = L // 32
     ds_step = B * Hq * n * (n + 1) // 2 * 32 * 32 * 2
-    # 2 x 8 x 16 = 256 pair workgroups: the 4 x 7 (step, head) pairs of a KV group split in two
+    # 2 x 8 x 16 = 256 pair workgroups: the 4 query heads of a KV group split in two
     part = 2 * 2 * B * Hkv * L * d * 4
     whole = K * rows * 8 + part + K * ds_step + (K - 1) * rows * d * 4
     assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(p)) == whole
