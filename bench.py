@@ -314,22 +314,27 @@ def main():
 
     kstats = {name: {"launches": n, "avg_ms": ms / n, "total_ms_per_step": ms / args.steps}
               for name, (n, ms) in kernels.items()}
-    # algorithmic matrix-core flops per launch of each causal kernel: dK/dV kernel does the
-    # S, dP, dV and dK products (8d per pair), dQ kernel the dQ product (2d), forward 4d.
+    # algorithmic matrix-core flops of each causal kernel per TTT step: dK/dV kernel does the
+    # S, dP, dV and dK products (8d per pair), dQ kernel the dQ product (2d), forward 4d.  The
+    # rate is the kernel's flops per sweep over its time per sweep: per launch for the
+    # per-step calls (one launch per step), and the same for the whole-TTT dK/dV launch, which
+    # covers every step.
     alg = {"bwd_dkdv_mfma": 8 * w.d * causal, "bwd_dq_mfma": 2 * w.d * causal,
            "bwd_dq_ds": 2 * w.d * causal, "fwd_causal_mfma": 4 * w.d * causal}
+    nsteps = len(steps)
     roofline = None
     if kstats:
         mfma = {n: s for n, s in kstats.items() if n in alg}
         dom = max(mfma, key=lambda n: mfma[n]["total_ms_per_step"])
-        achieved = alg[dom] / (mfma[dom]["avg_ms"] / 1e3) / 1e12
+        achieved = nsteps * alg[dom] / (mfma[dom]["total_ms_per_step"] / 1e3) / 1e12
+        # the counters were taken on the per-step calls' launches
+        traffic = measured_traffic(args.config, dom) if not args.sweep else None
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": measured_traffic(args.config, dom)}
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
         for n in alg:
             if n in kstats:
-                a = alg[n] / (kstats[n]["avg_ms"] / 1e3) / 1e12
+                a = nsteps * alg[n] / (kstats[n]["total_ms_per_step"] / 1e3) / 1e12
                 kstats[n]["alg_tflops"] = round(a, 1)
                 kstats[n]["frac_mfma_peak"] = round(a / PEAK_BF16_TFLOPS, 4)
         # suffix kernels: algorithmic HBM bytes per launch averaged over the steps with k >= 1
@@ -359,6 +364,14 @@ def main():
                          live_kv * k * 2 * w.d * 2 + w.B * w.Hkv * k * w.L * 2 * w.d * 2 for k in kk])
             gbs = b / (kstats["bwd_suffix"]["avg_ms"] / 1e3) / 1e9
             kstats["bwd_suffix"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+        if kk and "bwd_suffix_sweep" in kstats:
+            # whole TTT, one launch: the same rows for every step k >= 1 (q, dO, lse, D, the fp32
+            # dQ accumulator read, dq written), the diagonal K/V rows of every block t = 1..K-1
+            # read once and its dK/dV rows written once
+            b = (len(kk) * (2 * live_q * w.d * 2 + 2 * live_q * 4 + rows_q * w.d * 4 + rows_q * w.d * 2) +
+                 max(kk) * (live_kv * 2 * w.d * 2 + w.B * w.Hkv * w.L * 2 * w.d * 2))
+            gbs = b / (kstats["bwd_suffix_sweep"]["avg_ms"] / 1e3) / 1e9
+            kstats["bwd_suffix_sweep"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
 
     # % roofline of the whole sweep: the time the causal flops would take at the matrix-core
     # peak, plus the suffix's marginal bytes (diagonal K/V rows read by the forward, read and
