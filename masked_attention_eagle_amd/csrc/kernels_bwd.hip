@@ -937,35 +937,41 @@ __global__ __launch_bounds__(256) void bwd_suffix_kernel(
 
 // Single pass with the step loop outside and every head of the group in registers: each
 // diagonal K/V row is read once per (row, group) and its dK/dV row is written right away;
-// dQ of all heads accumulates in registers and is written at the end.
-template <typename T, int D, int G>
+// dQ of all heads accumulates in registers and is written at the end.  With H = 2 a row takes
+// 32 lanes: each half of them holds G/2 of the heads, the halves' dK/dV sums meet through one
+// lane exchange, and one half writes the dK row, the other the dV row.
+template <typename T, int D, int G, int H>
 __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, const float* __restrict__ dq_acc, T* __restrict__ dq,
     T* __restrict__ dk, T* __restrict__ dv, Shape s) {
   constexpr int E = D / 16;
+  constexpr int GH = G / H;          // heads per half
+  constexpr int RPB = 16 / H;        // rows per workgroup
   const int sub = threadIdx.x & 15;
-  const int blocks_per_bg = (s.L + 15) / 16;
+  const int half = H == 1 ? 0 : (threadIdx.x >> 4) & (H - 1);
+  const int blocks_per_bg = (s.L + RPB - 1) / RPB;
   const int bg = blockIdx.x / blocks_per_bg;
-  const int i = (blockIdx.x % blocks_per_bg) * 16 + (threadIdx.x >> 4);
+  const int i = (blockIdx.x % blocks_per_bg) * RPB + (threadIdx.x >> 4) / H;
   if (i >= s.L) return;
   const int b = bg / s.Hkv, g = bg % s.Hkv;
   const int Tlen = clamp_T(seq_T, b, s.L);
   const size_t kv_base = (size_t)bg * s.KV * D + (size_t)i * D + sub * E;
-  const size_t row0 = (size_t)(b * s.Hq + g * G) * s.L + i;
+  const size_t row0 = (size_t)(b * s.Hq + g * G + half * GH) * s.L + i;
   const bool live = i < Tlen;
+  T* const dkv = half == 0 ? dk : dv;  // (H = 2) the row this half writes
 
-  float dqa[G][E];
+  float dqa[GH][E];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < GH; ++h)
 #pragma unroll
     for (int e = 0; e < E; ++e) dqa[h][e] = 0.f;
 
   if (live) {
-    float qv[G][E], ov[G][E], l2[G], Dh[G];
+    float qv[GH][E], ov[GH][E], l2[GH], Dh[GH];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < GH; ++h) {
       const size_t row = row0 + (size_t)h * s.L;
       load_vec<T, E>(q + row * D + sub * E, qv[h]);
       load_vec<T, E>(dO + row * D + sub * E, ov[h]);
@@ -985,7 +991,7 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[e] = aV[e] = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int h = 0; h < GH; ++h) {
         float sd = 0.f, pd = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -1005,8 +1011,19 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[e] *= s.scale;
-      store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, aK);
-      store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, aV);
+      if constexpr (H == 1) {
+        store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, aK);
+        store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, aV);
+      } else {
+        // half 0 writes dK, half 1 dV: each sends the other the sum it lacks
+        float w[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float mine = half == 0 ? aK[e] : aV[e];
+          w[e] = mine + __shfl_xor(half == 0 ? aV[e] : aK[e], 16);
+        }
+        store_vec<T, E>(dkv + kv_base + (size_t)t * s.L * D, w);
+      }
       if (t < s.step) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -1020,12 +1037,16 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
 #pragma unroll
     for (int e = 0; e < E; ++e) z[e] = 0.f;
     for (int t = 1; t <= s.step; ++t) {
-      store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, z);
-      store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, z);
+      if constexpr (H == 1) {
+        store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, z);
+        store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, z);
+      } else {
+        store_vec<T, E>(dkv + kv_base + (size_t)t * s.L * D, z);
+      }
     }
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < GH; ++h) {
     const size_t row = row0 + (size_t)h * s.L;
     float a[E];
     load_vec<float, E>(dq_acc + row * D + sub * E, a);
@@ -1040,11 +1061,12 @@ static hipError_t bwd_suffix_dispatch(const Shape& s, dim3 grid, hipStream_t st,
                                       const T* k, const T* v, const T* dout, const float* lse,
                                       const float* Dd, const int32_t* seq_T, const float* dq_acc,
                                       T* dq, T* dk, T* dv) {
+  const dim3 grid2(s.B * s.Hkv * ((s.L + 7) / 8));  // 8 rows of 32 lanes per workgroup
   switch (s.G) {
-    case 1: bwd_suffix_g_kernel<T, D, 1><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
-    case 2: bwd_suffix_g_kernel<T, D, 2><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
-    case 4: bwd_suffix_g_kernel<T, D, 4><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
-    case 8: bwd_suffix_g_kernel<T, D, 8><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 1: bwd_suffix_g_kernel<T, D, 1, 1><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 2: bwd_suffix_g_kernel<T, D, 2, 1><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 4: bwd_suffix_g_kernel<T, D, 4, 1><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
+    case 8: bwd_suffix_g_kernel<T, D, 8, 2><<<grid2, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
     default: bwd_suffix_kernel<T, D><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dd, seq_T, dq_acc, dq, dk, dv, s); break;
   }
   return hipGetLastError();

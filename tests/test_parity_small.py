@@ -47,6 +47,12 @@ def test_fp32_edge_cases(gpu_lib, step, T, d, L):
     run_case(gpu_lib, 100 + step, 2, 4, 2, d, L, step, T, "f32")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_group_of_eight(gpu_lib, d):
+    """G = 8: the suffix kernel splits a row's heads over two 16-lane halves."""
+    run_case(gpu_lib, 110 + d, 2, 8, 1, d, 96, 3, (90, 33), "f32")
+
+
 # ------------------------------------------------------------------ bf16 matrix-core path
 # Paths of the bf16 library: dq_mode "stored" (the dK/dV kernel hands dS to the dQ kernel
 # through the workspace) or "recompute" (the dQ kernel recomputes S and dP); suffix "fused"
