@@ -12,7 +12,7 @@ per unmasked (query, key) pair) / step time.  tokens/s = B * Q_LEN / step time.
 pct_roofline = t_roof / step time, t_roof = causal flops at the bf16 matrix-core peak plus the
 suffix's marginal K/V bytes and the backward preprocessing bytes at the HBM peak.
 
-Prints one JSON line.  ``--gpus`` above 1 is refused: this build measures one GPU.
+Prints one JSON line.  ``--gpus`` above 1 is refused: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -172,8 +172,9 @@ def inputs_mod():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the TTT attention path needs no collective and this "
-              "build runs no multi-GPU configuration (see DESIGN.md for how it would shard).",
+        print("bench.py measures one GPU only: the TTT attention path needs no collective (every "
+              "(sequence, KV group) is independent under data parallelism), so each GPU runs its "
+              "share at these shapes; multi-GPU runs are not supported here.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -14,7 +14,7 @@ kernel the review's "§3 -> Memory-efficient gradient computation" describes):
 * s = sum_i p_i g_i with g the upstream gradient;
 * the gradient written over the logits, z <- -(p g - pi s).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   - z, p are [N, V] (one row per token, V draft-vocabulary columns) and the
     upstream gradient is one weight per row, g [N], broadcast along the row
     (a per-token loss has one scalar gradient per token; the loss mask and the

@@ -22,7 +22,7 @@ What it computes is the plain definition, written out densely:
   (dS = P * (dP - rowsum(P * dP))), the same identity the review uses for the
   loss gradient in "§4 Core formulas -> In-place backward".
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   - queries index the current TTT step's Q_LEN rows; keys of step t sit in rows
     [t*Q_LEN, (t+1)*Q_LEN) of the stacked K/V, block 0 is the prefix;
   - padded query rows (i >= T) follow the formula literally: they see keys
