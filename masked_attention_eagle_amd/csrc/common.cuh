@@ -184,6 +184,14 @@ __device__ __forceinline__ bf16x8 load16_global(const void* base, unsigned off) 
   return *(gvec*)((gchar*)base + off);
 }
 
+// The same load with the non-temporal hint, for data read once (it then displaces less of what
+// the caches hold for other reads).
+__device__ __forceinline__ bf16x8 load16_global_nt(const void* base, unsigned off) {
+  typedef const __attribute__((address_space(1))) char gchar;
+  typedef const __attribute__((address_space(1))) bf16x8 gvec;
+  return __builtin_nontemporal_load((gvec*)((gchar*)base + off));
+}
+
 // 16-byte streaming store to global memory at base + off (base wave-uniform, off per lane).
 // The explicit global address space keeps it a global_store: a flat store could alias LDS,
 // and the compiler would first wait for every copy into LDS still in flight.  The

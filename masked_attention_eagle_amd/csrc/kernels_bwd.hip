@@ -558,14 +558,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const bf16* __restric
   auto issue_k = [&](int j, bf16* dst) {
     load_tile<QBN, 4>(kb + (size_t)min(j, ntiles - 1) * QBN * BD, BD, dst, wave, lane);
   };
-  // 4 KB of this wave's dS for tile j: blocks 2j and 2j + 1, 1 KB per load.
+  // 4 KB of this wave's dS for tile j: blocks 2j and 2j + 1, 1 KB per load (read once:
+  // non-temporal, so the stream leaves the K tiles in the caches).
   auto load_ds = [&](int j, bf16x8 (&r)[4]) {
     unsigned off = 16u * lane;
     asm volatile("" : "+v"(off));
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int blk = max(min(2 * j + (x >> 1), nkb - 1), 0);
-      r[x] = load16_global(uniform_ptr(srow + (size_t)blk * 2048 + (x & 1) * 1024), off);
+      r[x] = load16_global_nt(uniform_ptr(srow + (size_t)blk * 2048 + (x & 1) * 1024), off);
     }
   };
 
