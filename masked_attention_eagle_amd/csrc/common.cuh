@@ -108,11 +108,13 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
-// Load N consecutive elements (N * sizeof(T) bytes, naturally aligned) as fp32.
-template <typename T, int N>
+// Load N consecutive elements (N * sizeof(T) bytes, naturally aligned) as fp32; NT: with the
+// non-temporal hint (data read once), for the 16-byte forms.
+template <typename T, int N, bool NT = false>
 __device__ __forceinline__ void load_vec(const T* p, float* out) {
   if constexpr (sizeof(T) == 2 && N == 8) {
-    bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+    bf16x8 v = NT ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p))
+                  : *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
     for (int j = 0; j < 8; ++j) out[j] = (float)v[j];
   } else if constexpr (sizeof(T) == 2 && N == 4) {
@@ -122,7 +124,8 @@ __device__ __forceinline__ void load_vec(const T* p, float* out) {
   } else if constexpr (sizeof(T) == 4 && N % 4 == 0) {
 #pragma unroll
     for (int j = 0; j < N; j += 4) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(p + j);
+      f32x4 v = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + j))
+                   : *reinterpret_cast<const f32x4*>(p + j);
       out[j] = v[0]; out[j + 1] = v[1]; out[j + 2] = v[2]; out[j + 3] = v[3];
     }
   } else {

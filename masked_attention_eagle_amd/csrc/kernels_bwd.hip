@@ -937,7 +937,8 @@ __global__ __launch_bounds__(256) void bwd_suffix_kernel(
 }
 
 // Single pass with the step loop outside and every head of the group in registers: each
-// diagonal K/V row is read once per (row, group) and its dK/dV row is written right away;
+// diagonal K/V row is read once per (row, group) and its dK/dV row is written right away
+// (every input is read once, with the non-temporal hint);
 // dQ of all heads accumulates in registers and is written at the end.  With H = 2 a row takes
 // 32 lanes: each half of them holds G/2 of the heads, the halves' dK/dV sums meet through one
 // lane exchange, and one half writes the dK row, the other the dV row.
@@ -974,19 +975,19 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
       const size_t row = row0 + (size_t)h * s.L;
-      load_vec<T, E>(q + row * D + sub * E, qv[h]);
-      load_vec<T, E>(dO + row * D + sub * E, ov[h]);
+      load_vec<T, E, true>(q + row * D + sub * E, qv[h]);
+      load_vec<T, E, true>(dO + row * D + sub * E, ov[h]);
       l2[h] = lse[row] * kLog2e;
       Dh[h] = Dd[row];
     }
     float kc[E], vc[E];
-    load_vec<T, E>(k + kv_base + (size_t)s.L * D, kc);
-    load_vec<T, E>(v + kv_base + (size_t)s.L * D, vc);
+    load_vec<T, E, true>(k + kv_base + (size_t)s.L * D, kc);
+    load_vec<T, E, true>(v + kv_base + (size_t)s.L * D, vc);
     for (int t = 1; t <= s.step; ++t) {
       float kn[E], vn[E];
       if (t < s.step) {
-        load_vec<T, E>(k + kv_base + (size_t)(t + 1) * s.L * D, kn);
-        load_vec<T, E>(v + kv_base + (size_t)(t + 1) * s.L * D, vn);
+        load_vec<T, E, true>(k + kv_base + (size_t)(t + 1) * s.L * D, kn);
+        load_vec<T, E, true>(v + kv_base + (size_t)(t + 1) * s.L * D, vn);
       }
       float aK[E], aV[E];
 #pragma unroll
@@ -1050,7 +1051,7 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
   for (int h = 0; h < GH; ++h) {
     const size_t row = row0 + (size_t)h * s.L;
     float a[E];
-    load_vec<float, E>(dq_acc + row * D + sub * E, a);
+    load_vec<float, E, true>(dq_acc + row * D + sub * E, a);
 #pragma unroll
     for (int e = 0; e < E; ++e) a[e] += s.scale * dqa[h][e];
     store_vec<T, E>(dq + row * D + sub * E, a);
@@ -1131,7 +1132,8 @@ __global__ __launch_bounds__(256) void bwd_suffix_sweep_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[c][e] = aV[c][e] = 0.f;
     // (step, head) pairs (kk, h), kk = t0..K-1: steps k >= t0 reach blocks t0 .. min(k, t0 +
-    // nb - 1).  The rows of the next pair are loaded while the current one computes.
+    // nb - 1).  The rows of the next pair are loaded while the current one computes (read
+    // once: non-temporal; the diagonal K/V rows, read for every pair, stay cached).
     struct RowIn {
       bf16x8 qr, orw;
       float l2, Di;
@@ -1141,11 +1143,11 @@ __global__ __launch_bounds__(256) void bwd_suffix_sweep_kernel(
       const size_t hrow = row_g + (size_t)h * s.L;
       const size_t row = (size_t)kk * step_rows + hrow;
       const float* accp = dq_acc + ((size_t)(kk - 1) * step_rows + hrow) * BD + sub * E;
-      r.a0 = *reinterpret_cast<const f32x4*>(accp);
-      r.a1 = *reinterpret_cast<const f32x4*>(accp + 4);
+      r.a0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(accp));
+      r.a1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(accp + 4));
       if (live) {
-        r.qr = *reinterpret_cast<const bf16x8*>(q + row * BD + sub * E);
-        r.orw = *reinterpret_cast<const bf16x8*>(dO + row * BD + sub * E);
+        r.qr = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(q + row * BD + sub * E));
+        r.orw = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(dO + row * BD + sub * E));
         r.l2 = lse[row] * kLog2e;
         r.Di = Dd[row];
       }
