@@ -20,18 +20,21 @@ namespace ttt {
 constexpr int LT = 512;  // threads per row
 constexpr int NW = LT / 64;  // waves per row
 
-// 8 consecutive elements of a row, kept in their storage type (bf16: 4 registers).
+// 8 consecutive elements of a row, kept in their storage type (bf16: 4 registers), loaded with
+// the non-temporal hint (each row is read once, or twice in a row by one workgroup).
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> {
   bf16x8 v;
-  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void load(const bf16* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+  }
   __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
 };
 template <> struct Vec8<float> {
   f32x4 a, b;
   __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const f32x4*>(p);
-    b = *reinterpret_cast<const f32x4*>(p + 4);
+    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
   }
   __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };
