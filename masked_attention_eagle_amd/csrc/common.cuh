@@ -134,13 +134,18 @@ __device__ __forceinline__ void load_vec(const T* p, float* out) {
   }
 }
 
-template <typename T, int N>
+// Store N fp32 values as N consecutive elements; NT: with the non-temporal hint (data not read
+// again soon), for the 16-byte bf16 form.
+template <typename T, int N, bool NT = false>
 __device__ __forceinline__ void store_vec(T* p, const float* in) {
   if constexpr (sizeof(T) == 2 && N == 8) {
     bf16x8 v;
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = (bf16)in[j];
-    *reinterpret_cast<bf16x8*>(p) = v;
+    if (NT)
+      __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p));
+    else
+      *reinterpret_cast<bf16x8*>(p) = v;
   } else if constexpr (sizeof(T) == 2 && N == 4) {
     bf16x4 v;
 #pragma unroll

@@ -938,7 +938,7 @@ __global__ __launch_bounds__(256) void bwd_suffix_kernel(
 
 // Single pass with the step loop outside and every head of the group in registers: each
 // diagonal K/V row is read once per (row, group) and its dK/dV row is written right away
-// (every input is read once, with the non-temporal hint);
+// (every input is read once and every output written once, with the non-temporal hint);
 // dQ of all heads accumulates in registers and is written at the end.  With H = 2 a row takes
 // 32 lanes: each half of them holds G/2 of the heads, the halves' dK/dV sums meet through one
 // lane exchange, and one half writes the dK row, the other the dV row.
@@ -1014,8 +1014,8 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) aK[e] *= s.scale;
       if constexpr (H == 1) {
-        store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, aK);
-        store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, aV);
+        store_vec<T, E, true>(dk + kv_base + (size_t)t * s.L * D, aK);
+        store_vec<T, E, true>(dv + kv_base + (size_t)t * s.L * D, aV);
       } else {
         // half 0 writes dK, half 1 dV: each sends the other the sum it lacks
         float w[E];
@@ -1024,7 +1024,7 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
           const float mine = half == 0 ? aK[e] : aV[e];
           w[e] = mine + __shfl_xor(half == 0 ? aV[e] : aK[e], 16);
         }
-        store_vec<T, E>(dkv + kv_base + (size_t)t * s.L * D, w);
+        store_vec<T, E, true>(dkv + kv_base + (size_t)t * s.L * D, w);
       }
       if (t < s.step) {
 #pragma unroll
@@ -1040,10 +1040,10 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
     for (int e = 0; e < E; ++e) z[e] = 0.f;
     for (int t = 1; t <= s.step; ++t) {
       if constexpr (H == 1) {
-        store_vec<T, E>(dk + kv_base + (size_t)t * s.L * D, z);
-        store_vec<T, E>(dv + kv_base + (size_t)t * s.L * D, z);
+        store_vec<T, E, true>(dk + kv_base + (size_t)t * s.L * D, z);
+        store_vec<T, E, true>(dv + kv_base + (size_t)t * s.L * D, z);
       } else {
-        store_vec<T, E>(dkv + kv_base + (size_t)t * s.L * D, z);
+        store_vec<T, E, true>(dkv + kv_base + (size_t)t * s.L * D, z);
       }
     }
   }
@@ -1054,7 +1054,7 @@ __global__ __launch_bounds__(256) void bwd_suffix_g_kernel(
     load_vec<float, E, true>(dq_acc + row * D + sub * E, a);
 #pragma unroll
     for (int e = 0; e < E; ++e) a[e] += s.scale * dqa[h][e];
-    store_vec<T, E>(dq + row * D + sub * E, a);
+    store_vec<T, E, true>(dq + row * D + sub * E, a);
   }
 }
 
@@ -1209,7 +1209,7 @@ __global__ __launch_bounds__(256) void bwd_suffix_sweep_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) a[e] += s.scale * dqa[e];
         if (last)
-          store_vec<bf16, E>(dq + row * BD + sub * E, a);
+          store_vec<bf16, E, true>(dq + row * BD + sub * E, a);
         else
           store_vec<float, E>(accp, a);
       }
@@ -1223,8 +1223,8 @@ __global__ __launch_bounds__(256) void bwd_suffix_sweep_kernel(
       if (c < nb) {
 #pragma unroll
         for (int e = 0; e < E; ++e) aK[c][e] *= s.scale;
-        store_vec<bf16, E>(dk + kv_base + (size_t)(t0 + c) * s.L * BD, aK[c]);
-        store_vec<bf16, E>(dv + kv_base + (size_t)(t0 + c) * s.L * BD, aV[c]);
+        store_vec<bf16, E, true>(dk + kv_base + (size_t)(t0 + c) * s.L * BD, aK[c]);
+        store_vec<bf16, E, true>(dv + kv_base + (size_t)(t0 + c) * s.L * BD, aV[c]);
       }
     }
   }
