@@ -5,14 +5,14 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 product path (the HIP library and its Python binding) never touches it, and it
 imports nothing from the product.
 
-What it computes, in the order and notation of the SpecForge paper review,
-"§4 Core formulas -> Masked softmax loss" and "-> In-place backward" (the
-kernel the review's "§3 -> Memory-efficient gradient computation" describes):
+What it computes (the kernel the review's "§3 -> Memory-efficient gradient
+computation" describes; formulas in "§4 Core formulas -> Masked softmax loss"
+and "-> In-place backward"):
 
-* pi = softmax(z) over each row of the logits z;
-* the loss of a row, L = -sum_i p_i log pi_i, with p the target distribution;
-* s = sum_i p_i g_i with g the upstream gradient;
-* the gradient written over the logits, z <- -(p g - pi s).
+* the loss of a row, L = -sum_i p_i log softmax(z)_i, with p the target
+  distribution;
+* the gradient of sum_n g_n L_n with respect to the logits, which the kernel
+  writes over z.
 
 Readings where the pages are silent:
   - z, p are [N, V] (one row per token, V draft-vocabulary columns) and the
@@ -51,15 +51,14 @@ def loss_rows(z: np.ndarray, p: np.ndarray) -> np.ndarray:
 
 
 def grad_inplace(z: np.ndarray, p: np.ndarray, g: np.ndarray) -> np.ndarray:
-    """The value the kernel leaves in z (review §4 "In-place backward"):
-    pi = softmax(z), s = sum(p * g), z <- -(p * g - pi * s), with g [N] broadcast over
-    each row."""
+    """The value the kernel leaves in z: the gradient of sum_n g_n L_n with respect to the
+    logits of row n, g_n (softmax(z_n) sum_i p_ni - p_n), which is the review's §4
+    "In-place backward" expression with its s = sum_i p_i g_i (g [N] broadcast over each row).
+    """
     z = np.asarray(z, dtype=np.float64)
     p = np.asarray(p, dtype=np.float64)
-    gb = np.asarray(g, dtype=np.float64)[..., None]
-    pi = softmax_rows(z)
-    s = (p * gb).sum(axis=-1, keepdims=True)
-    return -(p * gb - pi * s)
+    g_row = np.asarray(g, dtype=np.float64)[..., None]
+    return g_row * (softmax_rows(z) * p.sum(axis=-1, keepdims=True) - p)
 
 
 def loss_and_grad(z, p, g):

@@ -46,23 +46,19 @@ ROW_CHUNK = 1024  # rows per block of the dense computation (memory bound only)
 def mask_rows(q_len: int, ttt_step: int, valid_len: int, r0: int, r1: int) -> np.ndarray:
     """Rows [r0, r1) of the boolean mask M of shape [Q_LEN, (ttt_step + 1) * Q_LEN].
 
-    Written term by term from the BlockMask construction formulas
-    (review §3 "BlockMask construction algorithm", §4 "BlockMask construction").
+    The formula of the BlockMask construction (review §3 "BlockMask construction algorithm",
+    restated in §4 "BlockMask construction"), evaluated on the global query index i (r0..r1-1)
+    and key index j (0..KV-1):  M = causal | suffix, with
+        causal = (i >= j) & (j < T)
+        suffix = (j >= Q_LEN) & (j mod Q_LEN < T) & ((j - i) mod Q_LEN == 0).
     ``%`` on numpy integers is the non-negative (floored) modulus.
     """
-    L = int(q_len)
-    kv_len = (int(ttt_step) + 1) * L
-    T = int(valid_len)
-    q_i = np.arange(r0, r1, dtype=np.int64)[:, None]
-    kv_i = np.arange(kv_len, dtype=np.int64)[None, :]
-    m_causal = q_i >= kv_i
-    m_pad_causal = kv_i < T
-    M_causal = m_causal & m_pad_causal
-    m_suffix = kv_i >= L
-    m_pad_suffix = (kv_i % L) < T
-    m_diag = ((kv_i - q_i) % L) == 0
-    M_suffix = m_suffix & m_pad_suffix & m_diag
-    return M_causal | M_suffix
+    L, T = int(q_len), int(valid_len)
+    i = np.arange(r0, r1, dtype=np.int64)[:, None]
+    j = np.arange((int(ttt_step) + 1) * L, dtype=np.int64)[None, :]
+    causal = (i >= j) & (j < T)
+    suffix = (j >= L) & (j % L < T) & ((j - i) % L == 0)
+    return causal | suffix
 
 
 def mask(q_len: int, ttt_step: int, valid_len: int) -> np.ndarray:

@@ -332,3 +332,60 @@ def test_padding_heavy_lengths_are_seeded_and_in_range():
     T = inputs.seq_lengths(w)
     assert T.shape == (8,) and T.min() >= 256 and T.max() <= 2048
     np.testing.assert_array_equal(T, inputs.seq_lengths(w))
+
+
+# ----------------------------------------------------------------------------- row chunks
+@pytest.mark.parametrize("L,step,T", [(13, 2, 9), (13, 3, 13), (11, 1, 4), (12, 2, 0)])
+@pytest.mark.parametrize("r0,r1", [(0, 3), (3, 8), (5, 11), (7, 11)])
+def test_mask_rows_equals_rows_of_rule_in_words(L, step, T, r0, r1):
+    """Any row range of the mask (the oracle evaluates it range by range) equals the same rows
+    of the brute-force rule; the query index is global, not local to the range."""
+    np.testing.assert_array_equal(O.mask_rows(L, step, T, r0, r1), brute_mask(L, step, T)[r0:r1])
+
+
+@pytest.mark.parametrize("chunk", [3, 5])
+def test_row_chunked_forward_and_backward(monkeypatch, chunk):
+    """With ROW_CHUNK smaller than Q_LEN (13, a multiple of neither 3 nor 5) the oracle walks
+    several row ranges per (b, h), as it does for every Q_LEN >= 1024.  Pinned to the same
+    library routines as the one-range path: SDPA with the brute-force mask and logsumexp for
+    the forward, torch autograd through that SDPA for the backward, and the K = 0 closed form;
+    padded rows (T < Q_LEN), TTT step >= 2 and GQA are all present."""
+    monkeypatch.setattr(O, "ROW_CHUNK", chunk)
+    rng = np.random.default_rng(40 + chunk)
+    B, Hq, Hkv, L, d, step = 2, 4, 2, 13, 6, 2
+    Ts = (9, 13)
+    scale = 0.45
+    q = rand((B, Hq, L, d), rng)
+    k, v = rand((B, Hkv, (step + 1) * L, d), rng), rand((B, Hkv, (step + 1) * L, d), rng)
+    do = rand((B, Hq, L, d), rng)
+    o, lse = O.forward(q, k, v, Ts, scale)
+    dq, dk, dv = O.backward(q, k, v, Ts, scale, do)
+    G = Hq // Hkv
+    for b in range(B):
+        M = brute_mask(L, step, Ts[b])
+        np.testing.assert_allclose(o[b], _sdpa(q[b:b + 1], k[b:b + 1], v[b:b + 1], M, scale)[0],
+                                   rtol=0, atol=1e-12)
+        for h in range(Hq):
+            s = scale * q[b, h] @ k[b, h // G].T
+            np.testing.assert_allclose(lse[b, h], scipy.special.logsumexp(np.where(M, s, -np.inf), axis=1),
+                                       rtol=0, atol=1e-12)
+        Mt = torch.from_numpy(M)
+        qt = torch.from_numpy(q[b:b + 1]).requires_grad_()
+        kt = torch.from_numpy(k[b:b + 1]).requires_grad_()
+        vt = torch.from_numpy(v[b:b + 1]).requires_grad_()
+        out = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1), attn_mask=Mt, scale=scale)
+        out.backward(torch.from_numpy(do[b:b + 1]))
+        np.testing.assert_allclose(dq[b], qt.grad[0].numpy(), atol=1e-11)
+        np.testing.assert_allclose(dk[b], kt.grad[0].numpy(), atol=1e-11)
+        np.testing.assert_allclose(dv[b], vt.grad[0].numpy(), atol=1e-11)
+    # K = 0: lse_i = ln|M_i| and O_i = mean of the visible V rows, row range by row range
+    z = np.zeros_like(k)
+    oz, lz = O.forward(q, z, v, Ts, scale)
+    for b in range(B):
+        M = brute_mask(L, step, Ts[b])
+        for i in range(L):
+            idx = np.nonzero(M[i])[0]
+            np.testing.assert_allclose(lz[b, :, i], np.log(len(idx)), atol=1e-14)
+            for h in range(Hq):
+                np.testing.assert_allclose(oz[b, h, i], v[b, h // G, idx].mean(axis=0), atol=1e-13)
