@@ -107,6 +107,14 @@ def parse():
     ap.add_argument("--loss", action="store_true",
                     help="measure the in-place masked softmax-loss gradient on the draft LM head "
                          "of one TTT step (N = 8192 tokens, V = 32000, bf16) instead")
+    ap.add_argument("--no-also", action="store_true",
+                    help="with the default workload, skip the sub-record of the other headline "
+                         "workload (the Llama-3.3-70B-shaped layer)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured matrix-core and stream-copy peaks")
+    ap.add_argument("--cold-steps", type=int, default=2,
+                    help="steps timed again with the caches flushed before every launch "
+                         "(per-kernel cold-cache averages; 0 to skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run one plain device-to-device copy of MIB MiB (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -189,10 +197,67 @@ def main():
     if args.loss:
         bench_loss(args)
         return
+    A.load()
+    torch.cuda.set_device(torch.device("cuda", 0))
+    peaks = None if args.no_peaks else measure_peaks()
+    out = measure(args, args.config, peaks)
+    if args.config == 2 and not args.no_also:
+        # the metric's other headline workload, timed the same way in the same run
+        torch.cuda.empty_cache()
+        sub = measure(args, 4, peaks)
+        out["also"] = {sub["config"]["workload"]: {
+            k: sub[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s", "step_ms",
+                                "pct_roofline", "roofline", "config", "unmasked_flop_per_step")}}
+    if peaks is not None:
+        out["peaks_measured"] = peaks
+    if not args.no_cpu_baseline:
+        w = inputs.WORKLOADS[args.config]
+        out["cpu_baseline"] = cpu_baseline(w, inputs.seq_lengths(w), list(w.steps))
+    print(json.dumps(out))
+
+
+def measure_peaks():
+    """The chip's attainable peaks on the plainest workloads, from the library's probes: bf16
+    matrix-core TFLOP/s (2048 workgroups = 8 waves per CU, operands in registers) and HBM
+    stream-copy GB/s (1 GiB copied, read + write bytes), best of 5 runs each."""
+    import torch
+    from masked_attention_eagle_amd import ttt_attn as A
+    wgs, iters = 2048, 4096
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        return min(ts)
+
+    t_mfma = best(lambda: A.probe_mfma_bf16(sink, wgs, iters))
+    t_copy = best(lambda: A.probe_copy(src, dst))
+    mfma = wgs * 4 * iters * 8 * 32768 / t_mfma / 1e12
+    copy = 2 * src.numel() * 2 / t_copy / 1e9
+    return {"mfma_bf16_tflops": round(mfma, 1), "mfma_frac_of_spec": round(mfma / PEAK_BF16_TFLOPS, 4),
+            "copy_gbs": round(copy, 1), "copy_frac_of_spec": round(copy / PEAK_HBM_GBS, 4),
+            "how": "library probes: 32x32x16 bf16 MFMA on 4 register chains per wave, 8 waves "
+                   "per CU; 1 GiB device copy, 32 KB per workgroup, 16-byte non-temporal loads/stores; best of 5"}
+
+
+def measure(args, config, peaks=None):
+    """Times the sweep of one workload; returns the JSON record (without the CPU baseline)."""
+    import torch
+    from masked_attention_eagle_amd import inputs
+    from masked_attention_eagle_amd import ttt_attn as A
     lib = A.load()
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    w = inputs.WORKLOADS[args.config]
+    w = inputs.WORKLOADS[config]
     assert w.dtype == "bf16"
     T = inputs.seq_lengths(w)
     steps = list(w.steps)
@@ -283,6 +348,23 @@ def main():
         A.timing_enable(False)
         kernels = A.timing_read()
 
+    # per-kernel averages with the caches flushed (1 GiB overwritten) before every launch: the
+    # bandwidth-bound kernels then read everything from HBM, none of it from the last-level
+    # cache that the kernel before them filled
+    kernels_cold = {}
+    if args.cold_steps > 0 and not args.no_kernel_timing:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        A.timing_reset()
+        A.timing_flush(flush)
+        A.timing_enable(True)
+        for _ in range(args.cold_steps):
+            one_step()
+        torch.cuda.synchronize()
+        A.timing_enable(False)
+        A.timing_flush(None)
+        kernels_cold = A.timing_read()
+        del flush
+
     # the same step captured once in a HIP graph and replayed (launch gaps removed); reported
     # beside the eager figure, which stays the headline
     graph_sec = None
@@ -312,9 +394,6 @@ def main():
     flops = sum(14 * w.d * p for p in pairs_step)
     value = flops / sec / 1e12
     tokens = w.B * w.L / sec
-
-    kstats = {name: {"launches": n, "avg_ms": ms / n, "total_ms_per_step": ms / args.steps}
-              for name, (n, ms) in kernels.items()}
     # algorithmic matrix-core flops of each causal kernel per TTT step: dK/dV kernel does the
     # S, dP, dV and dK products (8d per pair), dQ kernel the dQ product (2d), forward 4d.  The
     # rate is the kernel's flops per sweep over its time per sweep: per launch for the
@@ -323,56 +402,67 @@ def main():
     alg = {"bwd_dkdv_mfma": 8 * w.d * causal, "bwd_dq_mfma": 2 * w.d * causal,
            "bwd_dq_ds": 2 * w.d * causal, "fwd_causal_mfma": 4 * w.d * causal}
     nsteps = len(steps)
+    rows_q = w.B * w.Hq * w.L
+    live_q = int(sum(int(t) for t in T)) * w.Hq
+    live_kv = int(sum(int(t) for t in T)) * w.Hkv
+    kk = [k for k in steps if k > 0]
+    L32 = w.L // 32
+    # algorithmic HBM bytes per launch of the bandwidth-bound kernels, averaged over the steps
+    # each one runs at
+    alg_bytes = {}
+    if kk:
+        # forward standalone suffix kernel: q of the live rows, the fp32 causal state (o_c,
+        # lse_c), the diagonal K/V rows; o and lse written
+        alg_bytes["fwd_suffix"] = np.mean([live_q * w.d * 2 + rows_q * (w.d * 4 + 4) +
+                                           live_kv * k * 2 * w.d * 2 + rows_q * (w.d * 2 + 4)
+                                           for k in kk])
+        # suffix backward: q, dO, lse, D of the live rows, the fp32 dQ accumulator read and dq
+        # written, the diagonal K/V rows read and all dK/dV rows of blocks 1..k written
+        alg_bytes["bwd_suffix"] = np.mean([2 * live_q * w.d * 2 + 2 * live_q * 4 + rows_q * w.d * 4 +
+                                           rows_q * w.d * 2 + live_kv * k * 2 * w.d * 2 +
+                                           w.B * w.Hkv * k * w.L * 2 * w.d * 2 for k in kk])
+        # whole TTT, one launch: the same rows for every step k >= 1, the diagonal K/V rows of
+        # every block t = 1..K-1 read once and its dK/dV rows written once
+        alg_bytes["bwd_suffix_sweep"] = (
+            len(kk) * (2 * live_q * w.d * 2 + 2 * live_q * 4 + rows_q * w.d * 4 + rows_q * w.d * 2) +
+            max(kk) * (live_kv * 2 * w.d * 2 + w.B * w.Hkv * w.L * 2 * w.d * 2))
+    # stored-dS dQ kernel: the 2 KB dS blocks it reads (key block kb <= query block qb, 32 kb <
+    # T), K of block 0 once per KV group, dQ written (fp32 accumulator for k >= 1, bf16 at k = 0)
+    blocks = w.Hq * sum(min(qb + 1, -(-int(t) // 32)) for t in T for qb in range(L32))
+    alg_bytes["bwd_dq_ds"] = np.mean([blocks * 2048 + w.B * w.Hkv * w.L * w.d * 2 +
+                                      rows_q * w.d * (4 if k else 2) for k in steps])
+    # row dot: o and dO read, D and lse * log2(e) written (lse read)
+    alg_bytes["bwd_rowdot"] = rows_q * (2 * w.d * 2 + 12)
+
+    def annotate(raw, nstep):
+        st = {name: {"launches": n, "avg_ms": ms / n, "total_ms_per_step": ms / nstep}
+              for name, (n, ms) in raw.items()}
+        for n in alg:
+            if n in st:
+                a = nsteps * alg[n] / (st[n]["total_ms_per_step"] / 1e3) / 1e12
+                st[n]["alg_tflops"] = round(a, 1)
+                st[n]["frac_mfma_peak"] = round(a / PEAK_BF16_TFLOPS, 4)
+        for n, b in alg_bytes.items():
+            if n in st:
+                gbs = b / (st[n]["avg_ms"] / 1e3) / 1e9
+                st[n].update(alg_bytes=int(b), alg_gbs=round(gbs, 1),
+                             frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+        return st
+
+    kstats = annotate(kernels, args.steps)
+    kcold = annotate(kernels_cold, args.cold_steps) if kernels_cold else None
     roofline = None
     if kstats:
         mfma = {n: s for n, s in kstats.items() if n in alg}
         dom = max(mfma, key=lambda n: mfma[n]["total_ms_per_step"])
         achieved = nsteps * alg[dom] / (mfma[dom]["total_ms_per_step"] / 1e3) / 1e12
         # the counters were taken on the per-step calls' launches
-        traffic = measured_traffic(args.config, dom) if not args.sweep else None
+        traffic = measured_traffic(config, dom) if not args.sweep else None
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
-        for n in alg:
-            if n in kstats:
-                a = nsteps * alg[n] / (kstats[n]["total_ms_per_step"] / 1e3) / 1e12
-                kstats[n]["alg_tflops"] = round(a, 1)
-                kstats[n]["frac_mfma_peak"] = round(a / PEAK_BF16_TFLOPS, 4)
-        # suffix kernels: algorithmic HBM bytes per launch averaged over the steps with k >= 1
-        rows_q = w.B * w.Hq * w.L
-        live_q = int(sum(int(t) for t in T)) * w.Hq
-        live_kv = int(sum(int(t) for t in T)) * w.Hkv
-        kk = [k for k in steps if k > 0]
-        if kk and "fwd_suffix" in kstats:
-            b = np.mean([live_q * w.d * 2 + rows_q * (w.d * 4 + 4) + live_kv * k * 2 * w.d * 2 +
-                         rows_q * (w.d * 2 + 4) for k in kk])
-            gbs = b / (kstats["fwd_suffix"]["avg_ms"] / 1e3) / 1e9
-            kstats["fwd_suffix"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
-        if "bwd_dq_ds" in kstats:
-            # stored-dS dQ kernel (HBM-bound): the 2 KB dS blocks it reads (key block kb <= query
-            # block qb, 32 kb < T), K of block 0 once per KV group, dQ written (fp32 accumulator
-            # for k >= 1, bf16 at k = 0), averaged over the steps
-            L32 = w.L // 32
-            blocks = w.Hq * sum(min(qb + 1, -(-int(t) // 32)) for t in T for qb in range(L32))
-            b = np.mean([blocks * 2048 + w.B * w.Hkv * w.L * w.d * 2 + rows_q * w.d * (4 if k else 2)
-                         for k in steps])
-            gbs = b / (kstats["bwd_dq_ds"]["avg_ms"] / 1e3) / 1e9
-            kstats["bwd_dq_ds"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
-        if kk and "bwd_suffix" in kstats:
-            # q, dO, lse, D of the live rows, the fp32 dQ accumulator read and dq written, the
-            # diagonal K/V rows read and all dK/dV rows of blocks 1..k written
-            b = np.mean([2 * live_q * w.d * 2 + 2 * live_q * 4 + rows_q * w.d * 4 + rows_q * w.d * 2 +
-                         live_kv * k * 2 * w.d * 2 + w.B * w.Hkv * k * w.L * 2 * w.d * 2 for k in kk])
-            gbs = b / (kstats["bwd_suffix"]["avg_ms"] / 1e3) / 1e9
-            kstats["bwd_suffix"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
-        if kk and "bwd_suffix_sweep" in kstats:
-            # whole TTT, one launch: the same rows for every step k >= 1 (q, dO, lse, D, the fp32
-            # dQ accumulator read, dq written), the diagonal K/V rows of every block t = 1..K-1
-            # read once and its dK/dV rows written once
-            b = (len(kk) * (2 * live_q * w.d * 2 + 2 * live_q * 4 + rows_q * w.d * 4 + rows_q * w.d * 2) +
-                 max(kk) * (live_kv * 2 * w.d * 2 + w.B * w.Hkv * w.L * 2 * w.d * 2))
-            gbs = b / (kstats["bwd_suffix_sweep"]["avg_ms"] / 1e3) / 1e9
-            kstats["bwd_suffix_sweep"].update(alg_bytes=int(b), alg_gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+        if peaks:
+            roofline["frac_of_measured_peak"] = round(achieved / peaks["mfma_bf16_tflops"], 4)
 
     # % roofline of the whole sweep: the time the causal flops would take at the matrix-core
     # peak, plus the suffix's marginal bytes (diagonal K/V rows read by the forward, read and
@@ -407,12 +497,10 @@ def main():
         "unmasked_flop_per_step": flops,
         "roofline": roofline,
         "kernels": kstats,
+        "kernels_cold_cache": kcold,
         "setup_s": round(setup_s, 1),
     }
-
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, T, steps)
-    print(json.dumps(out))
+    return out
 
 
 def bench_loss(args):
@@ -483,17 +571,36 @@ def cpu_baseline_loss(V):
     t0 = time.perf_counter()
     LO.loss_and_grad(z, p, g)
     sec = time.perf_counter() - t0
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    host = host_cores()
     return {"value": round((3 * rows * V * 2 + 2 * rows * 4) / sec / 1e9, 4), "unit": "GB/s",
-            "cores": cores, "kind": "oracle", "seconds": round(sec, 3),
+            "cores": host["threads"], "kind": "oracle", "host": host, "seconds": round(sec, 3),
             "sample": f"loss and gradient of {rows} rows x {V} columns"}
 
 
 CPU_SAMPLE_SECONDS = 25.0
+
+
+def host_cores() -> dict:
+    """The host side of the CPU baseline: cores this process may run on (its affinity), the
+    machine's logical CPU count, the BLAS threads the oracle's matrix products use (the cores
+    actually used), and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [affinity])
+    except Exception:
+        threads = affinity
+    return {"affinity_cores": affinity, "logical_cpus": os.cpu_count(), "threads": threads,
+            "cpu_model": model}
 
 
 def cpu_baseline(w, T, steps):
@@ -505,11 +612,7 @@ def cpu_baseline(w, T, steps):
     from masked_attention_eagle_amd import inputs
     from oracle import ttt_oracle as O
     G = w.Hq // w.Hkv
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
+    host = host_cores()
     sec, flops, done, ks, vs = 0.0, 0, [], [], []
     for k in steps:
         q = inputs.q_at(w, k)[0:1, 0:G]
@@ -526,8 +629,8 @@ def cpu_baseline(w, T, steps):
         done.append(k)
         if sec > CPU_SAMPLE_SECONDS:
             break
-    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(sec, 2),
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": host["threads"],
+            "kind": "oracle", "host": host, "seconds": round(sec, 2),
             "sample": f"fwd+bwd of KV group 0 ({G} query heads) of sequence 0 at TTT steps "
                       f"{done[0]}..{done[-1]}"}
 

@@ -90,8 +90,11 @@ enum ttt_attn_status {
 
 /*
  * Problem description.  Supported combinations:
- *   dtype F32 : head_dim in {64, 128}, any q_len >= 1.
- *   dtype BF16: head_dim == 128, q_len a multiple of 128.
+ *   dtype F32 : head_dim in {64, 128}, any q_len >= 1 (vector-ALU kernels).
+ *   dtype BF16: head_dim in {64, 128}, any q_len >= 1.  head_dim 128 with q_len a multiple of
+ *               128 runs on the matrix-core kernels (the fast path, and the only one the
+ *               whole-TTT calls and the flags below apply to); other bf16 shapes run on the
+ *               vector-ALU kernels (bf16 storage, fp32 arithmetic).
  * scale multiplies q.k before masking (1/sqrt(head_dim) in the usual setting); it must be
  * finite and positive (the streaming softmax tracks the row maximum of the raw q.k).
  */
@@ -129,10 +132,16 @@ int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const v
 
 /*
  * Backward: gradients of sum(dout * o) for the o/lse produced by ttt_attn_fwd on the same
- * inputs.  P is recomputed from lse (nothing else is saved), the softmax Jacobian gives
- * dS = P * (dP - rowsum(dout * o)), and dk/dv of every KV row are produced by exactly one
- * workgroup summing the query heads of its GQA group in a fixed order (bitwise
+ * inputs.  The review's §3 "Sparse Tree Attention" computes the attention flash-style so the
+ * logits are never stored; so P is recomputed here from lse (nothing else is saved by the
+ * forward), and the softmax Jacobian, the identity the review's §4 "In-place backward" writes
+ * out for the loss, gives dS = P * (dP - rowsum(dout * o)) with dP = dout v^T; then
+ * dq = scale * dS k, dk = scale * dS^T q, dv = P^T dout.  dk/dv of every KV row are produced by
+ * exactly one workgroup summing the query heads of its GQA group in a fixed order (bitwise
  * deterministic).  dq rows are likewise owned by one workgroup each.
+ * Arguments: p, q, k, v, seq_T as for ttt_attn_fwd; o and lse the forward's outputs; dout
+ * the gradient of o (layout of q); dq (layout of q), dk and dv (layout of k) are written;
+ * workspace of at least ttt_attn_bwd_workspace_size(p) bytes.  Errors as for ttt_attn_fwd.
  */
 int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
                  const int32_t* seq_T, const void* o, const float* lse, const void* dout,
@@ -187,6 +196,14 @@ typedef struct ttt_attn_kernel_time {
 int ttt_attn_timing_enable(int on);                       /* returns previous setting      */
 int ttt_attn_timing_read(ttt_attn_kernel_time* out, int max_entries); /* entries written, <0 on error */
 void ttt_attn_timing_reset(void);
+/*
+ * Cold-cache timing: while timing is enabled and a buffer is set, every timed launch is
+ * preceded (outside its events) by a kernel that overwrites `bytes` of `buf` with plain
+ * stores, so each kernel starts with caches that hold none of its data (give more than the
+ * 256 MB last-level cache).  buf is caller-owned device memory, 16-byte aligned, bytes a
+ * non-zero multiple of 16 (else TTT_E_ALIGN); NULL turns it off.  Not thread-safe.
+ */
+int ttt_attn_timing_flush(void* buf, size_t bytes);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libttt_attn.so")
-SOURCES = ["host.hip", "kernels_aux.hip", "kernels_fwd.hip", "kernels_bwd.hip", "kernels_loss.hip"]
+SOURCES = ["host.hip", "kernels_aux.hip", "kernels_fwd.hip", "kernels_bwd.hip", "kernels_loss.hip",
+           "probes.hip"]
 ARCH = "gfx950"
 
 

@@ -18,6 +18,8 @@ struct TimingRecord {
   hipEvent_t start, stop;
 };
 bool g_timing_on = false;
+void* g_flush_buf = nullptr;  // with timing on: overwritten before every timed launch
+size_t g_flush_bytes = 0;
 std::vector<TimingRecord> g_records;  // events recorded since the last read/reset
 size_t g_used = 0;
 
@@ -38,6 +40,7 @@ LaunchTimer::LaunchTimer(const char* name, hipStream_t st) : name_(name), st_(st
   }
   slot_ = (int)g_used++;
   g_records[slot_].name = name;
+  if (g_flush_buf) launch_flush_fill(g_flush_buf, g_flush_bytes, st);  // outside the timed span
   hipEventRecord(g_records[slot_].start, st);
 }
 
@@ -65,6 +68,12 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// bf16 shapes the matrix-core kernels tile (head_dim 128, q_len a multiple of 128); other
+// bf16 shapes and all fp32 ones run on the vector-ALU kernels.
+bool mfma_path(const ttt_attn_params* p) {
+  return p->dtype == TTT_DTYPE_BF16 && p->head_dim == 128 && p->q_len % 128 == 0;
+}
+
 int validate(const ttt_attn_params* p) {
   if (!p) return TTT_E_NULL;
   if (p->batch <= 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->q_len <= 0 ||
@@ -72,21 +81,20 @@ int validate(const ttt_attn_params* p) {
     return TTT_E_SHAPE;
   if (p->heads_q % p->heads_kv != 0) return TTT_E_SHAPE;
   if (!isfinite(p->scale) || !(p->scale > 0.f)) return TTT_E_SHAPE;
-  const int64_t kv = (int64_t)(p->ttt_step + 1) * p->q_len;
+  const int64_t kv = ((int64_t)p->ttt_step + 1) * p->q_len;  // widened before the add
   if (kv > INT32_MAX) return TTT_E_SHAPE;
   // Thread counts of the largest grids must stay below 2^32 and element counts below 2^40.
   const int64_t rows_q = (int64_t)p->batch * p->heads_q * p->q_len;
   const int64_t rows_kv = (int64_t)p->batch * p->heads_kv * kv;
   if (rows_q * p->head_dim > (1ll << 40) || rows_kv * p->head_dim > (1ll << 40)) return TTT_E_SHAPE;
-  if (p->dtype == TTT_DTYPE_F32) {
-    if (p->head_dim != 64 && p->head_dim != 128) return TTT_E_UNSUPPORTED;
-    if (rows_q * 64 >= (1ll << 32) || (int64_t)p->batch * p->heads_kv * p->q_len * 64 >= (1ll << 32))
-      return TTT_E_SHAPE;
-  } else if (p->dtype == TTT_DTYPE_BF16) {
-    if (p->head_dim != 128 || p->q_len % 128 != 0) return TTT_E_UNSUPPORTED;
+  if (p->dtype != TTT_DTYPE_F32 && p->dtype != TTT_DTYPE_BF16) return TTT_E_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return TTT_E_UNSUPPORTED;
+  if (mfma_path(p)) {
     if ((int64_t)p->batch * p->heads_kv * p->q_len * 16 >= (1ll << 32)) return TTT_E_SHAPE;
   } else {
-    return TTT_E_UNSUPPORTED;
+    // one 64-lane workgroup per query row (per key row in the dK/dV kernel)
+    if (rows_q * 64 >= (1ll << 32) || (int64_t)p->batch * p->heads_kv * p->q_len * 64 >= (1ll << 32))
+      return TTT_E_SHAPE;
   }
   if (p->flags & ~(TTT_FLAG_SEPARATE_SUFFIX | TTT_FLAG_RECOMPUTE_DQ | TTT_FLAG_DENSE_DIAGONAL))
     return TTT_E_UNSUPPORTED;
@@ -95,19 +103,30 @@ int validate(const ttt_attn_params* p) {
   return TTT_OK;
 }
 
+// Whole-TTT calls: the matrix-core shapes only, and the step-stacked q/o/dout/dq tensors
+// (K times the per-step rows) within the same element and grid limits.
+int validate_sweep(const ttt_attn_params* p) {
+  const int rc = validate(p);
+  if (rc != TTT_OK) return rc;
+  if (!mfma_path(p)) return TTT_E_UNSUPPORTED;
+  const int64_t rows_all = ((int64_t)p->ttt_step + 1) * p->batch * p->heads_q * p->q_len;
+  if (rows_all * p->head_dim > (1ll << 40) || rows_all / 16 >= (1ll << 31)) return TTT_E_SHAPE;
+  return TTT_OK;
+}
+
 // bf16 backward with the diagonal keys as masked matrix-core tiles (measurement variant).
 bool dense_bwd(const ttt_attn_params* p) {
-  return p->dtype == TTT_DTYPE_BF16 && (p->flags & TTT_FLAG_DENSE_DIAGONAL) && p->ttt_step > 0;
+  return mfma_path(p) && (p->flags & TTT_FLAG_DENSE_DIAGONAL) && p->ttt_step > 0;
 }
 // bf16 backward: the dQ kernel reads dS stored by the dK/dV kernel unless asked to recompute
 // (the dense-diagonal backward always recomputes: its dQ kernel also takes the diagonal tiles).
 bool stored_ds(const ttt_attn_params* p) {
-  return p->dtype == TTT_DTYPE_BF16 && !(p->flags & TTT_FLAG_RECOMPUTE_DQ) && !dense_bwd(p);
+  return mfma_path(p) && !(p->flags & TTT_FLAG_RECOMPUTE_DQ) && !dense_bwd(p);
 }
 // The forward merges the suffix inside the causal kernel unless asked for the separate
-// suffix kernel; the fp32 path always runs it.
+// suffix kernel; the vector-ALU path always runs it.
 bool fused_fwd(const ttt_attn_params* p) {
-  return p->dtype == TTT_DTYPE_BF16 && !(p->flags & TTT_FLAG_SEPARATE_SUFFIX);
+  return mfma_path(p) && !(p->flags & TTT_FLAG_SEPARATE_SUFFIX);
 }
 
 Shape make_shape(const ttt_attn_params* p) {
@@ -167,14 +186,14 @@ size_t ds_step_elems(const Shape& s) {
   const size_t n = s.L / 32;
   return (size_t)s.B * s.Hq * (n * (n + 1) / 2) * 32 * 32;
 }
-BwdLayout bwd_layout(const Shape& s, int dtype, bool with_ds, bool dense = false) {
+BwdLayout bwd_layout(const Shape& s, bool mfma, bool with_ds, bool dense = false) {
   BwdLayout w;
   const size_t rows_1 = (size_t)s.B * s.Hq * s.L;
   const size_t rows_q = rows_1 * s.nst;
   size_t off = 0;
   w.Dd = off;
   off += round_up(rows_q * 4);
-  if (dtype == TTT_DTYPE_BF16) {
+  if (mfma) {
     w.lse2 = off;
     off += round_up(rows_q * 4);
     w.nsplit = dkdv_nsplit(s);
@@ -211,7 +230,7 @@ const char* ttt_attn_status_string(int status) {
     case TTT_OK: return "ok";
     case TTT_E_NULL: return "null pointer argument";
     case TTT_E_SHAPE: return "invalid shape (non-positive size, heads_q % heads_kv != 0, ttt_step < 0, scale not finite and positive, or size overflow)";
-    case TTT_E_UNSUPPORTED: return "unsupported configuration (f32: head_dim 64 or 128; bf16: head_dim 128 and q_len % 128 == 0; unknown or conflicting flags)";
+    case TTT_E_UNSUPPORTED: return "unsupported configuration (head_dim other than 64 or 128, unknown dtype, unknown or conflicting flags, or a whole-TTT call outside bf16 with head_dim 128 and q_len % 128 == 0)";
     case TTT_E_ALIGN: return "pointer not 16-byte aligned";
     case TTT_E_WORKSPACE: return "workspace smaller than required";
     case TTT_E_HIP: return "HIP kernel launch failed";
@@ -226,13 +245,51 @@ size_t ttt_attn_fwd_workspace_size(const ttt_attn_params* p) {
 
 size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p) {
   if (validate(p) != TTT_OK) return 0;
-  return bwd_layout(make_shape(p), p->dtype, stored_ds(p), dense_bwd(p)).total;
+  return bwd_layout(make_shape(p), mfma_path(p), stored_ds(p), dense_bwd(p)).total;
 }
 
 }  // extern "C"
 
 namespace ttt {
 namespace {
+
+// Vector-ALU steps (fp32, and bf16 shapes outside the matrix-core tiling): element loads
+// convert to fp32, all arithmetic is fp32, outputs are rounded once on the write.
+template <typename T>
+hipError_t fwd_valu(const Shape& s, const void* q, const void* k, const void* v,
+                    const int32_t* seq_T, void* o, float* lse, float* oc, float* lsec,
+                    bool final_causal, hipStream_t st) {
+  const T* qt = (const T*)q;
+  const T* kt = (const T*)k;
+  const T* vt = (const T*)v;
+  hipError_t e = launch_fwd_causal_valu<T>(s, qt, kt, vt, seq_T, final_causal ? o : (void*)oc,
+                                           lsec, final_causal, st);
+  if (e != hipSuccess || final_causal) return e;
+  return launch_fwd_suffix<T>(s, qt, kt, vt, seq_T, oc, lsec, (T*)o, lse, st);
+}
+
+template <typename T>
+hipError_t bwd_valu(const Shape& s, const void* q, const void* k, const void* v,
+                    const int32_t* seq_T, const void* o, const float* lse, const void* dout,
+                    void* dq, void* dk, void* dv, float* Dd, float* dqacc, bool final_causal,
+                    hipStream_t st) {
+  const T* qt = (const T*)q;
+  const T* kt = (const T*)k;
+  const T* vt = (const T*)v;
+  const T* dot = (const T*)dout;
+  hipError_t e;
+  if ((e = launch_bwd_rowdot<T>(s, (const T*)o, dot, Dd, nullptr, nullptr, st)) != hipSuccess)
+    return e;
+  if ((e = launch_bwd_dkdv_valu<T>(s, qt, kt, vt, dot, lse, Dd, seq_T, (T*)dk, (T*)dv, st)) !=
+      hipSuccess)
+    return e;
+  if ((e = launch_bwd_dq_valu<T>(s, qt, kt, vt, dot, lse, Dd, seq_T,
+                                 final_causal ? dq : (void*)dqacc, final_causal, st)) != hipSuccess)
+    return e;
+  if (final_causal) return e;
+  return launch_bwd_suffix<T>(s, qt, kt, vt, dot, lse, Dd, seq_T, dqacc, (T*)dq, (T*)dk, (T*)dv,
+                              st);
+}
 
 // One forward step on validated arguments (s.KV is the row stride of k and v per KV group).
 int run_fwd(const ttt_attn_params* p, const Shape& s, const void* q, const void* k,
@@ -243,7 +300,7 @@ int run_fwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
   float* oc = final_causal ? nullptr : (float*)(ws + w.oc);
   float* lsec = final_causal ? lse : (float*)(ws + w.lsec);
   hipError_t e;
-  if (p->dtype == TTT_DTYPE_BF16) {
+  if (mfma_path(p)) {
     const bf16* qb = (const bf16*)q;
     const bf16* kb = (const bf16*)k;
     const bf16* vb = (const bf16*)v;
@@ -253,15 +310,10 @@ int run_fwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     if (e != hipSuccess) return TTT_E_HIP;
     if (!final_causal)
       e = launch_fwd_suffix<bf16>(s, qb, kb, vb, seq_T, oc, lsec, (bf16*)o, lse, st);
+  } else if (p->dtype == TTT_DTYPE_BF16) {
+    e = fwd_valu<bf16>(s, q, k, v, seq_T, o, lse, oc, lsec, final_causal, st);
   } else {
-    const float* qf = (const float*)q;
-    const float* kf = (const float*)k;
-    const float* vf = (const float*)v;
-    e = launch_fwd_causal_valu<float>(s, qf, kf, vf, seq_T, final_causal ? o : (void*)oc, lsec,
-                                      final_causal, st);
-    if (e != hipSuccess) return TTT_E_HIP;
-    if (!final_causal)
-      e = launch_fwd_suffix<float>(s, qf, kf, vf, seq_T, oc, lsec, (float*)o, lse, st);
+    e = fwd_valu<float>(s, q, k, v, seq_T, o, lse, oc, lsec, final_causal, st);
   }
   return hip_status(e);
 }
@@ -272,12 +324,12 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
             const void* dout, void* dq, void* dk, void* dv, char* ws, hipStream_t st) {
   const bool with_ds = stored_ds(p);
   const bool dense = dense_bwd(p);
-  const BwdLayout w = bwd_layout(s, p->dtype, with_ds, dense);
+  const BwdLayout w = bwd_layout(s, mfma_path(p), with_ds, dense);
   float* Dd = (float*)(ws + w.Dd);
   const bool final_causal = s.step == 0 || dense;
   float* dqacc = final_causal ? nullptr : (float*)(ws + w.dqacc);
   hipError_t e;
-  if (p->dtype == TTT_DTYPE_BF16) {
+  if (mfma_path(p)) {
     const bf16* qb = (const bf16*)q;
     const bf16* kb = (const bf16*)k;
     const bf16* vb = (const bf16*)v;
@@ -303,22 +355,10 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     if (!final_causal)
       e = launch_bwd_suffix<bf16>(s, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq, (bf16*)dk,
                                   (bf16*)dv, st);
+  } else if (p->dtype == TTT_DTYPE_BF16) {
+    e = bwd_valu<bf16>(s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, Dd, dqacc, final_causal, st);
   } else {
-    const float* qf = (const float*)q;
-    const float* kf = (const float*)k;
-    const float* vf = (const float*)v;
-    const float* dof = (const float*)dout;
-    if ((e = launch_bwd_rowdot<float>(s, (const float*)o, dof, Dd, nullptr, nullptr, st)) != hipSuccess)
-      return TTT_E_HIP;
-    if ((e = launch_bwd_dkdv_valu<float>(s, qf, kf, vf, dof, lse, Dd, seq_T, (float*)dk,
-                                         (float*)dv, st)) != hipSuccess)
-      return TTT_E_HIP;
-    if ((e = launch_bwd_dq_valu<float>(s, qf, kf, vf, dof, lse, Dd, seq_T,
-                                       final_causal ? dq : (void*)dqacc, final_causal, st)) != hipSuccess)
-      return TTT_E_HIP;
-    if (!final_causal)
-      e = launch_bwd_suffix<float>(s, qf, kf, vf, dof, lse, Dd, seq_T, dqacc, (float*)dq,
-                                   (float*)dk, (float*)dv, st);
+    e = bwd_valu<float>(s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, Dd, dqacc, final_causal, st);
   }
   return hip_status(e);
 }
@@ -379,7 +419,7 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
   if (rc != TTT_OK) return rc;
   if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
   const Shape s = make_shape(p);
-  const BwdLayout w = bwd_layout(s, p->dtype, stored_ds(p), dense_bwd(p));
+  const BwdLayout w = bwd_layout(s, mfma_path(p), stored_ds(p), dense_bwd(p));
   if (w.total > 0 && !workspace) return TTT_E_NULL;
   if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
@@ -391,22 +431,21 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
 }
 
 size_t ttt_attn_fwd_sweep_workspace_size(const ttt_attn_params* p) {
-  if (validate(p) != TTT_OK || p->dtype != TTT_DTYPE_BF16) return 0;
+  if (validate_sweep(p) != TTT_OK) return 0;
   return sweep_fwd_ws(p);
 }
 
 size_t ttt_attn_bwd_sweep_workspace_size(const ttt_attn_params* p) {
-  if (validate(p) != TTT_OK || p->dtype != TTT_DTYPE_BF16) return 0;
+  if (validate_sweep(p) != TTT_OK) return 0;
   const ttt_attn_params pb = sweep_bwd_params(p);
-  return bwd_layout(sweep_all_shape(p), p->dtype, stored_ds(&pb)).total;
+  return bwd_layout(sweep_all_shape(p), true, stored_ds(&pb)).total;
 }
 
 int ttt_attn_fwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
                        const int32_t* seq_T, void* o, float* lse, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  int rc = validate(p);
+  int rc = validate_sweep(p);
   if (rc != TTT_OK) return rc;
-  if (p->dtype != TTT_DTYPE_BF16) return TTT_E_UNSUPPORTED;
   if (!q || !k || !v || !seq_T || !o || !lse) return TTT_E_NULL;
   const size_t need = sweep_fwd_ws(p);
   if (need > 0 && !workspace) return TTT_E_NULL;
@@ -428,15 +467,14 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
                        const int32_t* seq_T, const void* o, const float* lse, const void* dout,
                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  int rc = validate(p);
+  int rc = validate_sweep(p);
   if (rc != TTT_OK) return rc;
-  if (p->dtype != TTT_DTYPE_BF16) return TTT_E_UNSUPPORTED;
   if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
   if (!workspace) return TTT_E_NULL;
   const ttt_attn_params pb = sweep_bwd_params(p);
   const bool with_ds = stored_ds(&pb);
   const Shape sa = sweep_all_shape(p);
-  const BwdLayout w = bwd_layout(sa, p->dtype, with_ds);
+  const BwdLayout w = bwd_layout(sa, true, with_ds);
   if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
@@ -531,6 +569,13 @@ int ttt_attn_timing_read(ttt_attn_kernel_time* out, int max_entries) {
     ++n;
   }
   return n;
+}
+
+int ttt_attn_timing_flush(void* buf, size_t bytes) {
+  if (buf && (((uintptr_t)buf & 15) || bytes % 16 || bytes == 0)) return TTT_E_ALIGN;
+  g_flush_buf = buf;
+  g_flush_bytes = buf ? bytes : 0;
+  return TTT_OK;
 }
 
 void ttt_attn_timing_reset(void) {

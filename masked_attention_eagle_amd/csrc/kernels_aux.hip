@@ -49,4 +49,17 @@ template hipError_t launch_bwd_rowdot<float>(const Shape&, const float*, const f
 template hipError_t launch_bwd_rowdot<bf16>(const Shape&, const bf16*, const bf16*, float*,
                                             const float*, float*, hipStream_t);
 
+// Writes `bytes` (a multiple of 16) of buf with plain stores: run before a timed launch, it
+// replaces what the caches (L2 and the memory-side last-level cache) hold.
+__global__ __launch_bounds__(256) void flush_fill_kernel(f32x4* __restrict__ buf, size_t n) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) buf[i] = z;
+}
+
+hipError_t launch_flush_fill(void* buf, size_t bytes, hipStream_t st) {
+  flush_fill_kernel<<<dim3(2048), 256, 0, st>>>(reinterpret_cast<f32x4*>(buf), bytes / 16);
+  return hipGetLastError();
+}
+
 }  // namespace ttt

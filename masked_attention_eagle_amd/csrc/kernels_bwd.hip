@@ -674,7 +674,8 @@ hipError_t launch_bwd_dq_ds(const Shape& s, const bf16* k, const bf16* ds, const
 }
 
 // ----------------------------------------------------------------------------------------
-// Vector-ALU backward of block 0 (fp32 path).
+// Vector-ALU backward of block 0 (fp32, and bf16 shapes outside the matrix-core tiling;
+// arithmetic in fp32).
 // dkdv: one wave per key row j of block 0; lanes take 64 queries at a time for p and ds,
 //       then split the head dimension for dV += p dO and dK += ds q (heads in order).
 // dq:   one wave per query row; lanes take 64 keys at a time, then split d for dQ += ds k.
@@ -761,6 +762,10 @@ template hipError_t launch_bwd_dkdv_valu<float>(const Shape&, const float*, cons
                                                 const float*, const float*, const float*,
                                                 const float*, const int32_t*, float*, float*,
                                                 hipStream_t);
+template hipError_t launch_bwd_dkdv_valu<bf16>(const Shape&, const bf16*, const bf16*,
+                                               const bf16*, const bf16*, const float*,
+                                               const float*, const int32_t*, bf16*, bf16*,
+                                               hipStream_t);
 
 template <typename T, int D, bool FINAL>
 __global__ __launch_bounds__(64) void bwd_dq_valu_kernel(
@@ -840,6 +845,9 @@ template hipError_t launch_bwd_dq_valu<float>(const Shape&, const float*, const 
                                               const float*, const float*, const float*,
                                               const float*, const int32_t*, void*, bool,
                                               hipStream_t);
+template hipError_t launch_bwd_dq_valu<bf16>(const Shape&, const bf16*, const bf16*, const bf16*,
+                                             const bf16*, const float*, const float*,
+                                             const int32_t*, void*, bool, hipStream_t);
 
 // ----------------------------------------------------------------------------------------
 // Suffix backward + dQ finalisation.  One group of 16 lanes per (b, KV group, row i).

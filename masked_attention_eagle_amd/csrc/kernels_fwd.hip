@@ -347,7 +347,8 @@ hipError_t launch_fwd_causal_mfma(const Shape& s, const bf16* q, const bf16* k, 
 }
 
 // ----------------------------------------------------------------------------------------
-// Causal block-0 forward on the vector ALUs (fp32 path).  One wave per query row: lanes take
+// Causal block-0 forward on the vector ALUs (fp32, and bf16 shapes outside the matrix-core
+// tiling; arithmetic in fp32).  One wave per query row: lanes take
 // 64 keys at a time for the logits, then split the head dimension for P V.
 // ----------------------------------------------------------------------------------------
 template <typename T, int D, bool FINAL>
@@ -427,6 +428,9 @@ hipError_t launch_fwd_causal_valu(const Shape& s, const T* q, const T* k, const 
 template hipError_t launch_fwd_causal_valu<float>(const Shape&, const float*, const float*,
                                                   const float*, const int32_t*, void*, float*,
                                                   bool, hipStream_t);
+template hipError_t launch_fwd_causal_valu<bf16>(const Shape&, const bf16*, const bf16*,
+                                                 const bf16*, const int32_t*, void*, float*, bool,
+                                                 hipStream_t);
 
 // ----------------------------------------------------------------------------------------
 // Suffix forward: the diagonal keys t*Q_LEN + i (t = 1..k) of query row i < T.

@@ -72,6 +72,9 @@ hipError_t launch_bwd_suffix_sweep(const Shape& s, const bf16* q, const bf16* k,
                                    const int32_t* seq_T, float* dq_acc, bf16* dq, bf16* dk,
                                    bf16* dv, hipStream_t st);
 
+// Cache flush for measurement: overwrites `bytes` (a multiple of 16) of buf.
+hipError_t launch_flush_fill(void* buf, size_t bytes, hipStream_t st);
+
 // In-place masked softmax-loss gradient.
 template <typename T>
 hipError_t launch_loss_grad(int64_t rows, int V, T* z, const T* p, const float* g, float* loss,

@@ -34,9 +34,10 @@ EXPORTS = (
     "ttt_attn_fwd_sweep_workspace_size", "ttt_attn_bwd_sweep_workspace_size",
     "ttt_attn_fwd_sweep", "ttt_attn_bwd_sweep",
     "ttt_attn_status_string", "ttt_attn_version", "ttt_attn_timing_enable",
-    "ttt_attn_timing_read", "ttt_attn_timing_reset",
+    "ttt_attn_timing_read", "ttt_attn_timing_reset", "ttt_attn_timing_flush",
 )
 LOSS_EXPORTS = ("ttt_loss_grad_inplace",)
+PROBE_EXPORTS = ("ttt_probe_mfma_bf16", "ttt_probe_copy")
 
 
 class TTTError(RuntimeError):
@@ -100,6 +101,12 @@ def load() -> ctypes.CDLL:
     lib.ttt_attn_timing_read.restype = ctypes.c_int
     lib.ttt_attn_timing_reset.argtypes = []
     lib.ttt_attn_timing_reset.restype = None
+    lib.ttt_attn_timing_flush.argtypes = [vp, sz]
+    lib.ttt_attn_timing_flush.restype = ctypes.c_int
+    lib.ttt_probe_mfma_bf16.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp]
+    lib.ttt_probe_mfma_bf16.restype = ctypes.c_int
+    lib.ttt_probe_copy.argtypes = [vp, vp, sz, vp]
+    lib.ttt_probe_copy.restype = ctypes.c_int
     lib.ttt_loss_grad_inplace.argtypes = [ctypes.POINTER(LossParams), vp, vp, vp, vp, vp]
     lib.ttt_loss_grad_inplace.restype = ctypes.c_int
     _lib = lib
@@ -305,6 +312,32 @@ def timing_enable(on: bool) -> bool:
 
 def timing_reset() -> None:
     load().ttt_attn_timing_reset()
+
+
+def timing_flush(buf) -> None:
+    """With timing enabled, overwrite the uint8 device tensor `buf` before every timed launch
+    (cold caches for each kernel); None turns it off."""
+    if buf is None:
+        _check(load().ttt_attn_timing_flush(None, 0))
+    else:
+        _check(load().ttt_attn_timing_flush(buf.data_ptr(), buf.numel() * buf.element_size()))
+
+
+def probe_mfma_bf16(sink, workgroups: int, iters: int) -> None:
+    """Enqueue the bf16 matrix-core probe (flops = workgroups * 4 * iters * 8 * 32768) on the
+    current stream; sink is an fp32 device tensor of at least workgroups * 256 elements."""
+    if sink.dtype.itemsize != 4 or sink.numel() < workgroups * 256 or not sink.is_cuda:
+        raise ValueError("sink: fp32 device tensor of workgroups * 256 elements")
+    _check(load().ttt_probe_mfma_bf16(sink.data_ptr(), workgroups, iters, _stream()))
+
+
+def probe_copy(src, dst) -> None:
+    """Enqueue the stream-copy probe dst <- src (same byte size, device tensors) on the current
+    stream; moves 2 * nbytes."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n or not (src.is_cuda and dst.is_cuda):
+        raise ValueError("src and dst: device tensors of the same byte size")
+    _check(load().ttt_probe_copy(src.data_ptr(), dst.data_ptr(), n, _stream()))
 
 
 def timing_read() -> dict:

@@ -29,6 +29,28 @@ def test_library_exports_every_declared_symbol():
     assert set(loss_declared) == set(A.LOSS_EXPORTS)
     for name in loss_declared:
         assert hasattr(lib, name), name
+    probe_declared = header_functions("ttt_probe.h", "ttt_probe_")
+    assert set(probe_declared) == set(A.PROBE_EXPORTS)
+    for name in probe_declared:
+        assert hasattr(lib, name), name
+
+
+def test_probe_and_flush_argument_errors():
+    """Errors of the probes and the cold-cache timing hook come before any launch."""
+    lib = A.load()
+    good, odd = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 4)
+    assert lib.ttt_probe_mfma_bf16(None, 8, 8, None) == -1
+    assert lib.ttt_probe_mfma_bf16(good, 0, 8, None) == -2
+    assert lib.ttt_probe_mfma_bf16(good, 8, 0, None) == -2
+    assert lib.ttt_probe_mfma_bf16(odd, 8, 8, None) == -4
+    assert lib.ttt_probe_copy(None, good, 1024, None) == -1
+    assert lib.ttt_probe_copy(good, good, 0, None) == -2
+    assert lib.ttt_probe_copy(good, good, 1000, None) == -2
+    assert lib.ttt_probe_copy(odd, good, 1024, None) == -4
+    assert lib.ttt_attn_timing_flush(odd, 1 << 20) == -4
+    assert lib.ttt_attn_timing_flush(good, 1000) == -4
+    assert lib.ttt_attn_timing_flush(good, 0) == -4
+    assert lib.ttt_attn_timing_flush(None, 0) == 0
 
 
 @pytest.mark.parametrize("rows,vocab,dtype,code", [
@@ -115,6 +137,14 @@ def test_workspace_sizes():
     rowsf = 2 * 32 * 4000
     for f in (0, sep, rec):
         assert A.bwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, L=4000, flags=f)) == rowsf * 4 + rowsf * d * 4
+    # bf16 outside the matrix-core tiling (head_dim 64, or Q_LEN not a multiple of 128): the
+    # vector-ALU kernels, with the fp32 path's workspaces (causal state; D + dQ accumulator)
+    for kw in (dict(d=64), dict(L=4032), dict(d=64, L=192)):
+        pv = P(**kw)
+        rv = 2 * 32 * pv.q_len
+        assert A.fwd_workspace_size(pv) == rv * pv.head_dim * 4 + rv * 4
+        assert A.bwd_workspace_size(pv) == rv * 4 + rv * pv.head_dim * 4
+        assert A.bwd_workspace_size(P(step=0, **kw)) == rv * 4
     assert A.fwd_workspace_size(P(Hq=30)) == 0  # invalid params -> 0
     assert A.bwd_workspace_size(P(Hq=30)) == 0
 
@@ -123,9 +153,13 @@ def test_workspace_sizes():
     (dict(B=0), -2), (dict(Hq=30), -2), (dict(step=-1), -2), (dict(L=-4), -2),
     (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2), (dict(scale=0.0), -2),
     (dict(scale=-0.088), -2),
-    (dict(d=64), -3), (dict(L=4000), -3), (dict(dtype=7), -3),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(dtype=7), -3),
     (dict(dtype=A.TTT_DTYPE_F32, d=96), -3), (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10), -2),
     (dict(flags=8), -3), (dict(flags=-1), -3), (dict(flags=5), -3),
+    # ttt_step + 1 must not wrap before it is widened; (k+1) * Q_LEN must fit in int32
+    (dict(step=2**31 - 1), -2), (dict(step=2**31 - 1, L=1), -2), (dict(step=(2**31 - 1) // 4096), -2),
+    # the vector-ALU path (bf16 outside the matrix-core tiling) launches one workgroup per row
+    (dict(d=64, B=1 << 12, Hq=1 << 8, Hkv=1 << 8, L=64), -2),
 ])
 def test_validation_errors(kw, code):
     lib = A.load()
@@ -203,6 +237,17 @@ def test_sweep_workspace_and_errors():
     assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(pf)) == 0
     good = ctypes.c_void_p(1 << 20)
     args = [good] * 11
+    # whole-TTT calls take the matrix-core shapes only
+    for bad in (P(step=2, d=64), P(step=2, L=4032)):
+        assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(bad)) == 0
+        assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(bad)) == 0
+        assert lib.ttt_attn_fwd_sweep(ctypes.byref(bad), *args[:7], 1 << 40, None) == -3
+        assert lib.ttt_attn_bwd_sweep(ctypes.byref(bad), *args, 1 << 40, None) == -3
+    # the step-stacked q/o/dout/dq (K times the per-step rows) must stay within 2^40 elements
+    big = P(B=1 << 10, Hq=1 << 8, Hkv=1, L=1 << 12, step=127)  # one step: 2^37 elements
+    assert A.bwd_workspace_size(big) > 0  # valid as one step
+    assert lib.ttt_attn_fwd_sweep(ctypes.byref(big), *args[:7], 1 << 40, None) == -2
+    assert lib.ttt_attn_bwd_sweep(ctypes.byref(big), *args, 1 << 40, None) == -2
     assert lib.ttt_attn_fwd_sweep(ctypes.byref(pf), *args[:7], 1 << 40, None) == -3
     assert lib.ttt_attn_bwd_sweep(ctypes.byref(pf), *args, 1 << 40, None) == -3
     assert lib.ttt_attn_bwd_sweep(ctypes.byref(p), *args, 16, None) == -5

@@ -1,8 +1,10 @@
 """The four bf16 draft-layer workloads at full size, through the C ABI in the same launch
 configuration the benchmark times.
 
-* one KV group (all of its query heads) per case, chosen from the seed, is compared element by
-  element with the oracle (a whole group is needed: dK/dV sum over its heads);
+* one KV group (all of its query heads) per sequence is compared element by element with the
+  oracle (a whole group is needed: dK/dV sum over its heads): the group is chosen from the seed,
+  for one sequence chosen from the seed, or for every sequence of the padding-heavy workload
+  (each of its eight sequences has its own valid length);
 * over every group: sum_j dK[b,g,j] = 0 (rows of dS sum to zero) and sum_j dV[b,g,j] =
   sum of dO over the group's non-empty query rows (rows of P sum to one), to fp32 rounding
   relative to sum|dK| and sum|dV|;
@@ -18,7 +20,7 @@ from tests.helpers import check, to_dev, to_np
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-CASES = [(2, 0), (2, 6), (3, 0), (3, 6), (4, 6), (5, 3), (5, 12)]
+CASES = [(2, 0), (2, 3), (2, 6), (3, 0), (3, 6), (4, 0), (4, 6), (5, 3), (5, 12)]
 
 
 def _run(lib, w, step, dq_mode="stored", suffix="fused"):
@@ -61,18 +63,21 @@ def test_workload_sampled_group_and_properties(gpu_lib, cfg, step, dq_mode, suff
         rows = torch.arange(w.kv_len(step), device="cuda") % L >= int(T[b])
         assert not bool(dk[b][:, rows].any()) and not bool(dv[b][:, rows].any())
 
-    # one KV group against the oracle
+    # KV groups against the oracle: one per sequence for the padding-heavy workload (every
+    # valid length), else one sequence
     rng = np.random.default_rng(np.random.SeedSequence([cfg, step, 77]))
-    b, g = int(rng.integers(w.B)), int(rng.integers(w.Hkv))
-    hs = slice(g * G, (g + 1) * G)
-    qs, ks, vs, dos = q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], do[b:b + 1, hs]
-    ro, rlse = O.forward(qs, ks, vs, T[b:b + 1], w.scale)
-    rdq, rdk, rdv = O.backward(qs, ks, vs, T[b:b + 1], w.scale, dos, ro)
-    got = dict(o=to_np(o[b:b + 1, hs]), lse=to_np(lse[b:b + 1, hs]), dq=to_np(dq[b:b + 1, hs]),
-               dk=to_np(dk[b:b + 1, g:g + 1]), dv=to_np(dv[b:b + 1, g:g + 1]))
-    e = check(got, dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv), "bf16",
-              f"cfg={cfg} step={step} b={b} g={g} T={int(T[b])}")
-    print("errors", e, flush=True)
+    seqs = list(range(w.B)) if len(set(int(t) for t in T)) > 1 else [int(rng.integers(w.B))]
+    for b in seqs:
+        g = int(rng.integers(w.Hkv))
+        hs = slice(g * G, (g + 1) * G)
+        qs, ks, vs, dos = q[b:b + 1, hs], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], do[b:b + 1, hs]
+        ro, rlse = O.forward(qs, ks, vs, T[b:b + 1], w.scale)
+        rdq, rdk, rdv = O.backward(qs, ks, vs, T[b:b + 1], w.scale, dos, ro)
+        got = dict(o=to_np(o[b:b + 1, hs]), lse=to_np(lse[b:b + 1, hs]), dq=to_np(dq[b:b + 1, hs]),
+                   dk=to_np(dk[b:b + 1, g:g + 1]), dv=to_np(dv[b:b + 1, g:g + 1]))
+        e = check(got, dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv), "bf16",
+                  f"cfg={cfg} step={step} b={b} g={g} T={int(T[b])}")
+        print("errors", b, g, int(T[b]), e, flush=True)
 
 
 def test_backward_bitwise_reproducible_full_size(gpu_lib):

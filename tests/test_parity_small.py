@@ -53,6 +53,16 @@ def test_fp32_group_of_eight(gpu_lib, d):
     run_case(gpu_lib, 110 + d, 2, 8, 1, d, 96, 3, (90, 33), "f32")
 
 
+# ------------------------------------------------------------------ bf16 vector-ALU path
+# bf16 shapes outside the matrix-core tiling (head_dim 64, Q_LEN not a multiple of 128) run on
+# the vector-ALU kernels: bf16 storage, fp32 arithmetic, the bf16 tolerances.
+@pytest.mark.parametrize("step,T,d,L,Hq,Hkv", [
+    (0, (37, 0), 64, 128, 4, 2), (2, (128, 77), 64, 128, 4, 2), (3, (64, 65), 128, 192, 4, 2),
+    (2, (190, 1), 64, 320, 8, 1), (1, (40, 64), 128, 64, 2, 2), (4, (100, 96), 64, 96, 2, 1)])
+def test_bf16_valu_shapes(gpu_lib, step, T, d, L, Hq, Hkv):
+    run_case(gpu_lib, 120 + step + L, 2, Hq, Hkv, d, L, step, T, "bf16")
+
+
 # ------------------------------------------------------------------ bf16 matrix-core path
 # Paths of the bf16 library: dq_mode "stored" (the dK/dV kernel hands dS to the dQ kernel
 # through the workspace) or "recompute" (the dQ kernel recomputes S and dP); suffix "fused"
