@@ -85,7 +85,8 @@ enum ttt_attn_status {
   TTT_E_UNSUPPORTED = -3, /* head_dim/dtype/q_len combination not built (see below)  */
   TTT_E_ALIGN = -4,       /* a pointer is not 16-byte aligned                        */
   TTT_E_WORKSPACE = -5,   /* workspace smaller than *_workspace_size()               */
-  TTT_E_HIP = -6          /* a kernel launch failed (hipGetLastError)                */
+  TTT_E_HIP = -6,         /* a kernel launch failed (hipGetLastError)                */
+  TTT_E_SCRATCH = -7      /* ttt_attn_bwd_noalloc: the call needs more than TTT_NOALLOC_SCRATCH_BYTES */
 };
 
 /*
@@ -174,6 +175,27 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
                        const int32_t* seq_T, const void* o, const float* lse, const void* dout,
                        void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * No-allocation backward, for callers that cannot allocate device memory or take a workspace
+ * argument (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as ttt_attn_bwd without the workspace: the
+ * backward's scratch (D, lse * log2(e), split dK/dV partials, the fp32 dQ accumulator) lives in
+ * a device array of TTT_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the dQ kernel recomputes S and dP (TTT_FLAG_RECOMPUTE_DQ is implied:
+ * the stored-dS path needs a logits-sized buffer), so dq, dk and dv are bitwise those of
+ * ttt_attn_bwd with that flag.  The call allocates nothing, apart from hipEvents when the
+ * timing API below is enabled.  Calls whose scratch need exceeds the maximum return
+ * TTT_E_SCRATCH before anything is launched (the five workloads of this library, up to
+ * B 8 x Hq 32 x Q_LEN 2048 and B 2 x Hq 32 x Q_LEN 4096, fit).  The array belongs to the
+ * current HIP device, which must be the device of `stream` and of the tensors.  Every call on
+ * one GPU shares that GPU's array, so calls that may overlap on one GPU (several streams or
+ * threads) race and must be ordered by the caller.
+ */
+#define TTT_NOALLOC_SCRATCH_BYTES ((size_t)320 << 20)
+int ttt_attn_bwd_noalloc(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                         const int32_t* seq_T, const void* o, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv, void* stream);
 
 /* Static text for a status code. */
 const char* ttt_attn_status_string(int status);

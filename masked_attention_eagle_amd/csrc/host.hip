@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "launch.h"
@@ -216,6 +217,30 @@ BwdLayout bwd_layout(const Shape& s, bool mfma, bool with_ds, bool dense = false
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_E_HIP; }
 
+// ------------------------------------------------------------------ no-allocation scratch
+// The backward's scratch for ttt_attn_bwd_noalloc: a file-scope device array, one copy per
+// GPU.  Host code never uses the array's name as an address (on the host it only names the
+// symbol); the device address of each GPU's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is what the kernels receive.
+static __device__ __align__(256) char scratch[TTT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TTT_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TTT_E_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return TTT_OK;
+}
+
 }  // namespace
 }  // namespace ttt
 
@@ -234,6 +259,7 @@ const char* ttt_attn_status_string(int status) {
     case TTT_E_ALIGN: return "pointer not 16-byte aligned";
     case TTT_E_WORKSPACE: return "workspace smaller than required";
     case TTT_E_HIP: return "HIP kernel launch failed";
+    case TTT_E_SCRATCH: return "the no-allocation backward needs more scratch than its fixed maximum (TTT_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -428,6 +454,25 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
     return TTT_E_ALIGN;
   return run_bwd(p, s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, (char*)workspace,
                  (hipStream_t)stream);
+}
+
+int ttt_attn_bwd_noalloc(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                         const int32_t* seq_T, const void* o, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv, void* stream) {
+  int rc = validate(p);
+  if (rc != TTT_OK) return rc;
+  if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
+  ttt_attn_params pr = *p;
+  pr.flags |= TTT_FLAG_RECOMPUTE_DQ;  // no logits-sized dS buffer
+  const Shape s = make_shape(&pr);
+  const BwdLayout w = bwd_layout(s, mfma_path(&pr), stored_ds(&pr), dense_bwd(&pr));
+  if (w.total > TTT_NOALLOC_SCRATCH_BYTES) return TTT_E_SCRATCH;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return TTT_E_ALIGN;
+  char* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws)) != TTT_OK) return rc;
+  return run_bwd(&pr, s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, ws, (hipStream_t)stream);
 }
 
 size_t ttt_attn_fwd_sweep_workspace_size(const ttt_attn_params* p) {

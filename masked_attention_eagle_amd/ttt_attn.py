@@ -25,7 +25,7 @@ DQ_MODES = {"stored": 0, "recompute": TTT_FLAG_RECOMPUTE_DQ}
 
 STATUS = {
     0: "TTT_OK", -1: "TTT_E_NULL", -2: "TTT_E_SHAPE", -3: "TTT_E_UNSUPPORTED",
-    -4: "TTT_E_ALIGN", -5: "TTT_E_WORKSPACE", -6: "TTT_E_HIP",
+    -4: "TTT_E_ALIGN", -5: "TTT_E_WORKSPACE", -6: "TTT_E_HIP", -7: "TTT_E_SCRATCH",
 }
 
 # Every symbol the header declares.
@@ -35,6 +35,7 @@ EXPORTS = (
     "ttt_attn_fwd_sweep", "ttt_attn_bwd_sweep",
     "ttt_attn_status_string", "ttt_attn_version", "ttt_attn_timing_enable",
     "ttt_attn_timing_read", "ttt_attn_timing_reset", "ttt_attn_timing_flush",
+    "ttt_attn_bwd_noalloc",
 )
 LOSS_EXPORTS = ("ttt_loss_grad_inplace",)
 PROBE_EXPORTS = ("ttt_probe_mfma_bf16", "ttt_probe_copy")
@@ -101,6 +102,8 @@ def load() -> ctypes.CDLL:
     lib.ttt_attn_timing_read.restype = ctypes.c_int
     lib.ttt_attn_timing_reset.argtypes = []
     lib.ttt_attn_timing_reset.restype = None
+    lib.ttt_attn_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ttt_attn_bwd_noalloc.restype = ctypes.c_int
     lib.ttt_attn_timing_flush.argtypes = [vp, sz]
     lib.ttt_attn_timing_flush.restype = ctypes.c_int
     lib.ttt_probe_mfma_bf16.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp]

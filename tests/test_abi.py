@@ -191,6 +191,27 @@ def test_null_align_workspace_errors():
     assert lib.ttt_attn_bwd(ctypes.byref(p), *args, 1 << 40, None) == -1
 
 
+def test_noalloc_argument_errors():
+    """ttt_attn_bwd_noalloc validates like ttt_attn_bwd and refuses, before touching the device,
+    a call whose scratch (D, lse * log2(e), split partials, fp32 dQ accumulator; no stored dS)
+    exceeds its fixed maximum."""
+    lib = A.load()
+    good, odd = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 8)
+    args = [good] * 10
+    assert lib.ttt_attn_bwd_noalloc(None, *args, None) == -1
+    assert lib.ttt_attn_bwd_noalloc(ctypes.byref(P(Hq=30)), *args, None) == -2
+    assert lib.ttt_attn_bwd_noalloc(ctypes.byref(P(d=96)), *args, None) == -3
+    # B 8 x Hq 32 x Q_LEN 4096, k > 0: the fp32 dQ accumulator alone is 512 MiB, above the
+    # 320 MiB maximum
+    assert lib.ttt_attn_bwd_noalloc(ctypes.byref(P(B=8)), *args, None) == -7
+    assert lib.ttt_attn_bwd_noalloc(ctypes.byref(P(B=16, L=2048)), *args, None) == -7
+    bad = list(args)
+    bad[5] = None
+    assert lib.ttt_attn_bwd_noalloc(ctypes.byref(P()), *bad, None) == -1
+    bad[5] = odd
+    assert lib.ttt_attn_bwd_noalloc(ctypes.byref(P()), *bad, None) == -4
+
+
 def test_timing_api_without_launches():
     was = A.timing_enable(True)
     A.timing_reset()
