@@ -36,6 +36,7 @@ constexpr int FD = 128;  // head dim
 constexpr int FBM = 128; // queries per workgroup
 constexpr int FBN = 64;  // keys per tile
 constexpr float kRescaleLog2 = 8.f;  // headroom of the unnormalised probabilities (base 2)
+constexpr float kFastSumLimit = 65536.f;  // fast path: largest per-lane tile sum of P kept
 
 // DIAG (measurement variant, with FINAL): instead of the per-lane gather, the diagonal keys
 // of blocks 1..k go through the matrix cores the way a BlockMask-driven kernel handles them:
@@ -147,60 +148,87 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
             if (st * 32 + acc_row(i, 0) > lim) sacc[st][i] = kNegInf;
         }
       }
-      float rmax = fmaxf(sacc[0][0], sacc[1][0]);
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int i = 1; i < 15; i += 2) rmax = fmaxf(fmaxf(rmax, sacc[st][i]), sacc[st][i + 1]);
-        rmax = fmaxf(rmax, sacc[st][15]);
-      }
-      rmax = half_max(rmax);
-      // The reference max m of a row moves only when the tile's max exceeds it by more than
-      // kRescaleLog2 in base-2 units.  Until then the tile's probabilities exp2((s - m) c2)
-      // stay below 2^kRescaleLog2, which fp32 sums and bf16 P carry with the same relative
-      // precision as values below 1, so the accumulator is rescaled only on the rare tiles
-      // where some row's logits jump that far (always on a row's first visible key).
-      const bool grow = rmax * c2 > m * c2 + kRescaleLog2;
-      if (__any(grow)) {
-        const float m_new = grow ? rmax : m;
-        const float alpha = grow ? exp2_fast((m - m_new) * c2) : 1.f;
-        l *= alpha;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] *= alpha;
-        m = m_new;
-      }
-      const float mc = (m == kNegInf) ? 0.f : m * c2;
+      // Fast path (full tiles and tiles whose rows all see >= 64 keys, once every row of the
+      // wave has a reference max): P against the current reference max, no tile max.  Each P
+      // of a lane is at most the lane's sum over its 32 keys, so the sum alone shows whether
+      // some probability has grown past 2^16 (or overflowed); only then is the tile redone
+      // through the max-and-rescale path below.  The sum stays fp32 over the unrounded P
+      // (a sum of the bf16-rounded P would move lse by up to 2^-9 on short rows).
       float lsum = 0.f;
-      bf16x8 pf[4];
-      if (full || wide) {
+      bf16x8 pf[4], pl[4];
+      bool fast = (full || wide) && __all(m != kNegInf);
+      if (fast) {
+        const float mc = m * c2;
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
             const float pv = exp2_fast(__builtin_fmaf(sacc[c >> 1][8 * (c & 1) + jj], c2, -mc));
-            lsum += pv;
+            if (jj & 1) s1 += pv; else s0 += pv;
             pf[c][jj] = (bf16)pv;
           }
         }
+        lsum = s0 + s1;
+        fast = !__any(!(lsum <= kFastSumLimit));
+      }
+      if (!fast) {
+        float rmax = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int i = 1; i < 15; i += 2) rmax = fmaxf(fmaxf(rmax, sacc[st][i]), sacc[st][i + 1]);
+          rmax = fmaxf(rmax, sacc[st][15]);
+        }
+        rmax = half_max(rmax);
+        // The reference max m of a row moves only when the tile's max exceeds it by more than
+        // kRescaleLog2 in base-2 units.  Until then the tile's probabilities exp2((s - m) c2)
+        // stay below 2^kRescaleLog2, which fp32 sums and bf16 P carry with the same relative
+        // precision as values below 1, so the accumulator is rescaled only on the rare tiles
+        // where some row's logits jump that far (always on a row's first visible key).
+        const bool grow = rmax * c2 > m * c2 + kRescaleLog2;
+        if (__any(grow)) {
+          const float m_new = grow ? rmax : m;
+          const float alpha = grow ? exp2_fast((m - m_new) * c2) : 1.f;
+          l *= alpha;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] *= alpha;
+          m = m_new;
+        }
+        const float mc = (m == kNegInf) ? 0.f : m * c2;
+        lsum = 0.f;
+        if (full || wide) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              const float pv = exp2_fast(__builtin_fmaf(sacc[c >> 1][8 * (c & 1) + jj], c2, -mc));
+              lsum += pv;
+              pf[c][jj] = (bf16)pv;
+            }
+          }
+        } else {  // P = hi + lo in bf16, the sum in fp32
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              const float pv = exp2_fast(__builtin_fmaf(sacc[c >> 1][8 * (c & 1) + jj], c2, -mc));
+              lsum += pv;
+              const bf16 ph = (bf16)pv;
+              pf[c][jj] = ph;
+              pl[c][jj] = (bf16)(pv - (float)ph);
+            }
+          }
+        }
+      }
+      if (full || wide) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
           for (int c = 0; c < 4; ++c)
             acc[u] = mfma32(frag_col(cV, c, u, fl), pf[c], acc[u]);
         }
-      } else {  // P = hi + lo in bf16: both parts go through the same V operands
-        bf16x8 pl[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const float pv = exp2_fast(__builtin_fmaf(sacc[c >> 1][8 * (c & 1) + jj], c2, -mc));
-            lsum += pv;
-            const bf16 ph = (bf16)pv;
-            pf[c][jj] = ph;
-            pl[c][jj] = (bf16)(pv - (float)ph);
-          }
-        }
+      } else {  // both parts of P go through the same V operands
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
