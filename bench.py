@@ -101,9 +101,10 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="time the whole-TTT calls (one forward and one backward call over one KV "
                          "cache, dK/dV summed over the steps) instead of the per-step calls")
-    ap.add_argument("--dq-mode", choices=("stored", "recompute"), default="stored",
+    ap.add_argument("--dq-mode", choices=("stored", "recompute", "fused-suffix"), default="stored",
                     help="dS handed from the dK/dV kernel to the dQ kernel through the workspace, "
-                         "or recomputed in the dQ kernel")
+                         "or recomputed in the dQ kernel, or handed over with the diagonal keys' "
+                         "rows taken by the dK/dV kernel (no suffix kernel)")
     ap.add_argument("--loss", action="store_true",
                     help="measure the in-place masked softmax-loss gradient on the draft LM head "
                          "of one TTT step (N = 8192 tokens, V = 32000, bf16) instead")
@@ -247,7 +248,7 @@ def measure_peaks():
     return {"mfma_bf16_tflops": round(mfma, 1), "mfma_frac_of_spec": round(mfma / PEAK_BF16_TFLOPS, 4),
             "copy_gbs": round(copy, 1), "copy_frac_of_spec": round(copy / PEAK_HBM_GBS, 4),
             "how": "library probes: 32x32x16 bf16 MFMA on 4 register chains per wave, 8 waves "
-                   "per CU; 1 GiB device copy, 32 KB per workgroup, 16-byte non-temporal loads/stores; best of 5"}
+                   "per CU; 1 GiB device copy, 16 KB per workgroup, 16-byte loads/stores; best of 5"}
 
 
 def measure(args, config, peaks=None):
@@ -399,7 +400,8 @@ def measure(args, config, peaks=None):
     # rate is the kernel's flops per sweep over its time per sweep: per launch for the
     # per-step calls (one launch per step), and the same for the whole-TTT dK/dV launch, which
     # covers every step.
-    alg = {"bwd_dkdv_mfma": 8 * w.d * causal, "bwd_dq_mfma": 2 * w.d * causal,
+    alg = {"bwd_dkdv_mfma": 8 * w.d * causal, "bwd_dkdv_suffix_mfma": 8 * w.d * causal,
+           "bwd_dq_mfma": 2 * w.d * causal,
            "bwd_dq_ds": 2 * w.d * causal, "fwd_causal_mfma": 4 * w.d * causal}
     nsteps = len(steps)
     rows_q = w.B * w.Hq * w.L

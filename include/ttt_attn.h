@@ -69,13 +69,19 @@ enum ttt_attn_dtype {
  *   and the dQ kernel recomputes S and dP over the causal tiles and two masked tiles per
  *   block t, writing the final dq (no suffix kernel, no stored dS).  Cannot be combined with
  *   TTT_FLAG_SEPARATE_SUFFIX; the whole-TTT backward ignores it.
+ * TTT_FLAG_FUSED_SUFFIX_BWD (backward, k > 0): the dK/dV workgroup of each 128-key tile of
+ *   block 0 also computes the suffix key rows t*Q_LEN + i (t = 1..k) of the same rows i: their
+ *   dK/dV, and the fp32 dQ term of each head, which the stored-dS dQ kernel adds before it
+ *   writes the final dq (no suffix kernel).  Not with TTT_FLAG_RECOMPUTE_DQ or
+ *   TTT_FLAG_DENSE_DIAGONAL; the whole-TTT backward ignores it.
  * Otherwise, in the backward the suffix kernel adds the diagonal keys' terms for k > 0.  The
  * workspace sizes below depend on the flags.
  */
 enum ttt_attn_flags {
   TTT_FLAG_SEPARATE_SUFFIX = 1,
   TTT_FLAG_RECOMPUTE_DQ = 2,
-  TTT_FLAG_DENSE_DIAGONAL = 4
+  TTT_FLAG_DENSE_DIAGONAL = 4,
+  TTT_FLAG_FUSED_SUFFIX_BWD = 8
 };
 
 enum ttt_attn_status {

@@ -28,9 +28,9 @@ extern "C" {
 int ttt_probe_mfma_bf16(float* sink, int32_t workgroups, int32_t iters, void* stream);
 
 /*
- * HBM stream-copy probe: dst[0, bytes) = src[0, bytes) with 16-byte non-temporal loads and
- * stores, one workgroup of 256 lanes per 32 KB chunk, eight loads in flight per lane before
- * its stores.  Bytes moved = 2 * bytes.
+ * HBM stream-copy probe: dst[0, bytes) = src[0, bytes) with 16-byte loads and stores, one
+ * workgroup of 256 lanes per 16 KB chunk, four loads in flight per lane before its stores.
+ * Bytes moved = 2 * bytes.
  * src and dst are device memory, 16-byte aligned, not overlapping; bytes a multiple of 16.
  * Errors: TTT_E_NULL, TTT_E_SHAPE (bytes 0, not a multiple of 16, or 2^31 chunks or more),
  * TTT_E_ALIGN, TTT_E_HIP.

@@ -97,9 +97,14 @@ int validate(const ttt_attn_params* p) {
     if (rows_q * 64 >= (1ll << 32) || (int64_t)p->batch * p->heads_kv * p->q_len * 64 >= (1ll << 32))
       return TTT_E_SHAPE;
   }
-  if (p->flags & ~(TTT_FLAG_SEPARATE_SUFFIX | TTT_FLAG_RECOMPUTE_DQ | TTT_FLAG_DENSE_DIAGONAL))
+  if (p->flags & ~(TTT_FLAG_SEPARATE_SUFFIX | TTT_FLAG_RECOMPUTE_DQ | TTT_FLAG_DENSE_DIAGONAL |
+                   TTT_FLAG_FUSED_SUFFIX_BWD))
     return TTT_E_UNSUPPORTED;
   if ((p->flags & TTT_FLAG_SEPARATE_SUFFIX) && (p->flags & TTT_FLAG_DENSE_DIAGONAL))
+    return TTT_E_UNSUPPORTED;
+  // the fused backward suffix hands its dQ term to the stored-dS dQ kernel
+  if ((p->flags & TTT_FLAG_FUSED_SUFFIX_BWD) &&
+      (p->flags & (TTT_FLAG_RECOMPUTE_DQ | TTT_FLAG_DENSE_DIAGONAL)))
     return TTT_E_UNSUPPORTED;
   return TTT_OK;
 }
@@ -123,6 +128,10 @@ bool dense_bwd(const ttt_attn_params* p) {
 // (the dense-diagonal backward always recomputes: its dQ kernel also takes the diagonal tiles).
 bool stored_ds(const ttt_attn_params* p) {
   return mfma_path(p) && !(p->flags & TTT_FLAG_RECOMPUTE_DQ) && !dense_bwd(p);
+}
+// bf16 backward whose dK/dV kernel also takes the suffix key rows (no suffix kernel).
+bool fused_bwd_suffix(const ttt_attn_params* p) {
+  return mfma_path(p) && (p->flags & TTT_FLAG_FUSED_SUFFIX_BWD) && p->ttt_step > 0;
 }
 // The forward merges the suffix inside the causal kernel unless asked for the separate
 // suffix kernel; the vector-ALU path always runs it.
@@ -366,19 +375,24 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     float* lse2 = (float*)(ws + w.lse2);
     if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, lse, lse2, st)) != hipSuccess)
       return TTT_E_HIP;
+    // fused: the dK/dV kernel writes the suffix rows and the suffix dQ term (into the dQ
+    // accumulator's space), and the dQ kernel adds that term and writes the final dq
+    const bool fused = fused_bwd_suffix(p);
     if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, dob, lse2, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
-                                  w.nsplit, dsb, dense, st)) != hipSuccess)
+                                  w.nsplit, dsb, dense, fused ? dqacc : nullptr, st)) != hipSuccess)
       return TTT_E_HIP;
     if (w.nsplit > 1 &&
         (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
       return TTT_E_HIP;
-    if (with_ds)
-      e = launch_bwd_dq_ds(s, kb, dsb, seq_T, dq_causal, final_causal, st);
+    if (fused)
+      e = launch_bwd_dq_ds(s, kb, dsb, seq_T, dq, true, dqacc, st);
+    else if (with_ds)
+      e = launch_bwd_dq_ds(s, kb, dsb, seq_T, dq_causal, final_causal, nullptr, st);
     else
       e = launch_bwd_dq_mfma(s, qb, kb, vb, dob, lse, Dd, seq_T, dq_causal, final_causal, dense,
                              st);
     if (e != hipSuccess) return TTT_E_HIP;
-    if (!final_causal)
+    if (!final_causal && !fused)
       e = launch_bwd_suffix<bf16>(s, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq, (bf16*)dk,
                                   (bf16*)dv, st);
   } else if (p->dtype == TTT_DTYPE_BF16) {
@@ -401,11 +415,12 @@ size_t sweep_fwd_ws(const ttt_attn_params* p) {
   for (int k = 0; k <= p->ttt_step; ++k) m = std::max(m, fwd_layout(sweep_shape(p, k), fused_fwd(p)).total);
   return m;
 }
-// The whole-TTT backward ignores TTT_FLAG_DENSE_DIAGONAL (its dK/dV sums go through the
-// suffix kernel): its paths and workspace follow the flags without that bit.
+// The whole-TTT backward ignores TTT_FLAG_DENSE_DIAGONAL and TTT_FLAG_FUSED_SUFFIX_BWD (its
+// dK/dV sums over the steps go through its own suffix kernel): its paths and workspace follow
+// the flags without those bits.
 ttt_attn_params sweep_bwd_params(const ttt_attn_params* p) {
   ttt_attn_params q = *p;
-  q.flags &= ~TTT_FLAG_DENSE_DIAGONAL;
+  q.flags &= ~(TTT_FLAG_DENSE_DIAGONAL | TTT_FLAG_FUSED_SUFFIX_BWD);
   return q;
 }
 // The whole-TTT backward's shape for the launches that cover every step at once (row-dot,
@@ -544,7 +559,7 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
   if ((e = launch_bwd_rowdot<bf16>(sa, (const bf16*)o, dob, Dd, lse, lse2, st)) != hipSuccess)
     return TTT_E_HIP;
   if ((e = launch_bwd_dkdv_mfma(sa, qb, kb, vb, dob, lse2, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
-                                w.nsplit, dsb, false, st)) != hipSuccess)
+                                w.nsplit, dsb, false, nullptr, st)) != hipSuccess)
     return TTT_E_HIP;
   if (w.nsplit > 1 &&
       (e = launch_bwd_dkdv_reduce(sa, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
@@ -554,7 +569,8 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
     const Shape s = sweep_shape(p, kk);
     void* dq_causal = kk == 0 ? (void*)((bf16*)dq) : (void*)(dqacc + (kk - 1) * qel);
     if (with_ds)
-      e = launch_bwd_dq_ds(s, kb, dsb + kk * ds_step_elems(s), seq_T, dq_causal, kk == 0, st);
+      e = launch_bwd_dq_ds(s, kb, dsb + kk * ds_step_elems(s), seq_T, dq_causal, kk == 0, nullptr,
+                           st);
     else
       e = launch_bwd_dq_mfma(s, qb + kk * qel, kb, vb, dob + kk * qel, lse + kk * rows,
                              Dd + kk * rows, seq_T, dq_causal, kk == 0, false, st);

@@ -60,6 +60,96 @@ __device__ __forceinline__ unsigned ds_read_offset(int lane, int c, int r) {
   return (unsigned)(1024 * qh + 16 * (slot ^ (8 * qh)) + 8 * (a >> 1));
 }
 
+// Diagonal keys of the suffix blocks for the query rows [r0, r0 + nrows) (NEXT-1 in the
+// backward: the dK/dV workgroup of a block-0 key tile also owns the key rows t*Q_LEN + i of
+// blocks t = 1..k for the same i).  16 lanes per row, 16 rows per round; each lane holds 8 of
+// the 128 elements.  Two passes, so that neither the step count nor the group size sets the
+// register footprint:
+//   dQ:    per head, dq_suf[h, i] = scale * sum_t ds_t k_t (fp32, for the dQ kernel to add);
+//   dK/dV: per block t, dK_t = scale * sum_h ds_h q_h and dV_t = sum_h p_h dO_h, written once
+//          (this workgroup is the only writer of these rows).
+// with p = exp2(scale*log2(e) q.k_t - lse*log2(e)), ds = p (dO.v_t - D).  Rows i >= T get no
+// suffix key: zero dK/dV rows and a zero dQ term.  q and dO rows are read twice (the second
+// time mostly from L2).
+__device__ __forceinline__ void dkdv_suffix_rows(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dd,
+    float* __restrict__ dq_suf, bf16* __restrict__ dk, bf16* __restrict__ dv, const Shape& s,
+    int b, int bg, int hg0, int T, int r0, int nrows) {
+  constexpr int E = BD / 16;
+  const int sub = threadIdx.x & 15;
+  for (int rr = threadIdx.x >> 4; rr < nrows; rr += 16) {
+    const int i = r0 + rr;
+    const bool live = i < T;
+    const size_t kv_base = ((size_t)bg * s.KV + i) * BD + sub * E;
+    // dQ term, head by head
+    for (int h = 0; h < s.G; ++h) {
+      const size_t row = (size_t)(b * s.Hq + hg0 + h) * s.L + i;
+      float acc[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = 0.f;
+      if (live) {
+        float qv[E], ov[E];
+        load_vec<bf16, E>(q + row * BD + sub * E, qv);
+        load_vec<bf16, E>(dO + row * BD + sub * E, ov);
+        const float l2 = lse2[row], Di = Dd[row];
+        for (int t = 1; t <= s.step; ++t) {
+          float kc[E], vc[E];
+          load_vec<bf16, E>(k + kv_base + (size_t)t * s.L * BD, kc);
+          load_vec<bf16, E>(v + kv_base + (size_t)t * s.L * BD, vc);
+          float sd = 0.f, pd = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            sd += qv[e] * kc[e];
+            pd += ov[e] * vc[e];
+          }
+          const float p = exp2_fast(sum16(sd) * s.scale_log2 - l2);
+          const float ds = p * (sum16(pd) - Di);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] += ds * kc[e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] *= s.scale;
+      }
+      store_vec<float, E>(dq_suf + row * BD + sub * E, acc);
+    }
+    // dK, dV of the key rows t*Q_LEN + i, block by block
+    for (int t = 1; t <= s.step; ++t) {
+      float aK[E], aV[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) aK[e] = aV[e] = 0.f;
+      if (live) {
+        float kc[E], vc[E];
+        load_vec<bf16, E>(k + kv_base + (size_t)t * s.L * BD, kc);
+        load_vec<bf16, E>(v + kv_base + (size_t)t * s.L * BD, vc);
+        for (int h = 0; h < s.G; ++h) {
+          const size_t row = (size_t)(b * s.Hq + hg0 + h) * s.L + i;
+          float qv[E], ov[E];
+          load_vec<bf16, E>(q + row * BD + sub * E, qv);
+          load_vec<bf16, E>(dO + row * BD + sub * E, ov);
+          float sd = 0.f, pd = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            sd += qv[e] * kc[e];
+            pd += ov[e] * vc[e];
+          }
+          const float p = exp2_fast(sum16(sd) * s.scale_log2 - lse2[row]);
+          const float ds = p * (sum16(pd) - Dd[row]);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            aV[e] += p * ov[e];
+            aK[e] += ds * qv[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) aK[e] *= s.scale;
+      }
+      store_vec<bf16, E, true>(dk + kv_base + (size_t)t * s.L * BD, aK);
+      store_vec<bf16, E, true>(dv + kv_base + (size_t)t * s.L * BD, aV);
+    }
+  }
+}
+
 // Key tile kt is seen by every query row >= 128 * kt (padded rows see every key < T), so the
 // work of tile kt falls linearly with kt.  A workgroup takes the complementary pair
 // (p, n - 1 - p) of key tiles, which makes every workgroup's work equal.
@@ -69,12 +159,15 @@ __device__ __forceinline__ unsigned ds_read_offset(int lane, int c, int r) {
 // [k0, k0 + 128) of every head of the group as masked tiles whose mask keeps key row
 // t*Q_LEN + i for query i < T; each 32-query tile meets the keys of one wave, the other three
 // skip it.  These workgroups write their dK/dV rows directly (no split, no dS hand-over).
-template <bool DIAG>
+// SUF: the workgroup also takes the suffix key rows of its key tiles (dkdv_suffix_rows), with
+// the dQ term written to dq_suf.
+template <bool DIAG, bool SUF>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, bf16* __restrict__ dk, bf16* __restrict__ dv,
-    float* __restrict__ part, int nsplit, bf16* __restrict__ ds_out, Shape s) {
+    float* __restrict__ part, int nsplit, bf16* __restrict__ ds_out, float* __restrict__ dq_suf,
+    Shape s) {
   // Two stages in distinct arrays (the copy into one never stalls reads of the other).
   __shared__ __attribute__((aligned(1024))) bf16 sQ0[KBM * BD];
   __shared__ __attribute__((aligned(1024))) bf16 sO0[KBM * BD];
@@ -293,23 +386,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
         }
       }
     }
+    // the suffix key rows t*Q_LEN + [k0, k0 + 128), split by rows over the nsp workgroups
+    // that share this key tile
+    if constexpr (SUF && !DIAG) {
+      const int per = KBN / nsp;
+      dkdv_suffix_rows(q, k, v, dO, lse2, Dd, dq_suf, dk, dv, s, b, bg, hg0, T, k0 + split * per,
+                       per);
+    }
   }
 }
 
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse2, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
-                                int nsplit, bf16* ds_out, bool dense_diagonal, hipStream_t st) {
+                                int nsplit, bf16* ds_out, bool dense_diagonal, float* dq_suf,
+                                hipStream_t st) {
   const int pairs = s.B * s.Hkv * nsplit * ((s.L / KBN + 1) / 2);
-  LaunchTimer timer("bwd_dkdv_mfma", st);
+  LaunchTimer timer(dq_suf ? "bwd_dkdv_suffix_mfma" : "bwd_dkdv_mfma", st);
   if (dense_diagonal && s.step > 0) {
     const dim3 grid(pairs + s.B * s.Hkv * (s.L / KBN) * s.step);
-    bwd_dkdv_mfma_kernel<true><<<grid, 256, 0, st>>>(q, k, v, dout, lse2, Dd, seq_T, dk, dv, part,
-                                                     nsplit, nullptr, s);
+    bwd_dkdv_mfma_kernel<true, false><<<grid, 256, 0, st>>>(q, k, v, dout, lse2, Dd, seq_T, dk, dv,
+                                                            part, nsplit, nullptr, nullptr, s);
     return hipGetLastError();
   }
-  bwd_dkdv_mfma_kernel<false><<<dim3(pairs), 256, 0, st>>>(q, k, v, dout, lse2, Dd, seq_T, dk, dv,
-                                                           part, nsplit, ds_out, s);
+  if (dq_suf && s.step > 0)
+    bwd_dkdv_mfma_kernel<false, true><<<dim3(pairs), 256, 0, st>>>(
+        q, k, v, dout, lse2, Dd, seq_T, dk, dv, part, nsplit, ds_out, dq_suf, s);
+  else
+    bwd_dkdv_mfma_kernel<false, false><<<dim3(pairs), 256, 0, st>>>(
+        q, k, v, dout, lse2, Dd, seq_T, dk, dv, part, nsplit, ds_out, nullptr, s);
   return hipGetLastError();
 }
 
@@ -521,11 +626,15 @@ hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, cons
 // Only blocks the wave's rows can see enter the products: key block kb <= the wave's query
 // block and 32 kb < T; masked entries inside them were stored as zero.
 // ----------------------------------------------------------------------------------------
+// With FINAL and dq_add set, the fp32 dQ term in dq_add (the diagonal keys' part, written by
+// the dK/dV kernel that also owns the suffix rows) is added before the bf16 write.
 template <bool FINAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const bf16* __restrict__ k,
                                                            const bf16* __restrict__ ds,
                                                            const int32_t* __restrict__ seq_T,
-                                                           void* __restrict__ dq_out, Shape s) {
+                                                           void* __restrict__ dq_out,
+                                                           const float* __restrict__ dq_add,
+                                                           Shape s) {
   __shared__ __attribute__((aligned(1024))) bf16 sK0[QBN * BD];
   __shared__ __attribute__((aligned(1024))) bf16 sK1[QBN * BD];
   __shared__ __attribute__((aligned(1024))) bf16 sK2[QBN * BD];
@@ -637,13 +746,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const bf16* __restric
   const size_t row = (size_t)bh * s.L + q0 + 32 * wave + (lane & 31);
   if constexpr (FINAL) {
     bf16* orow = reinterpret_cast<bf16*>(dq_out) + row * BD + 4 * hi;
+    const float* arow = dq_add ? dq_add + row * BD + 4 * hi : nullptr;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int b4 = 0; b4 < 4; ++b4) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        if (arow) a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(arow + 32 * u + 8 * b4));
         bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[u][4 * b4 + e] * s.scale);
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[u][4 * b4 + e] * s.scale + a[e]);
         *reinterpret_cast<bf16x4*>(orow + 32 * u + 8 * b4) = w;
       }
     }
@@ -663,13 +775,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const bf16* __restric
 }
 
 hipError_t launch_bwd_dq_ds(const Shape& s, const bf16* k, const bf16* ds, const int32_t* seq_T,
-                            void* dq, bool final_out, hipStream_t st) {
+                            void* dq, bool final_out, const float* dq_add, hipStream_t st) {
   const dim3 grid(s.B * s.Hq * (s.L / QBM));
   LaunchTimer timer("bwd_dq_ds", st);
   if (final_out)
-    bwd_dq_ds_kernel<true><<<grid, 256, 0, st>>>(k, ds, seq_T, dq, s);
+    bwd_dq_ds_kernel<true><<<grid, 256, 0, st>>>(k, ds, seq_T, dq, dq_add, s);
   else
-    bwd_dq_ds_kernel<false><<<grid, 256, 0, st>>>(k, ds, seq_T, dq, s);
+    bwd_dq_ds_kernel<false><<<grid, 256, 0, st>>>(k, ds, seq_T, dq, nullptr, s);
   return hipGetLastError();
 }
 

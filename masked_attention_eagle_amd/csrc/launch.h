@@ -40,18 +40,22 @@ template <typename T>
 hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* Dd,
                              const float* lse, float* lse2, hipStream_t st);
 // lse2 = lse * log2(e) (from launch_bwd_rowdot).
+// With dq_suf set (and k > 0) each workgroup also takes the suffix key rows t*Q_LEN + i of
+// its key tile's rows i: their dK/dV, and the fp32 dQ term of every head written to dq_suf.
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse2, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
-                                int nsplit, bf16* ds_out, bool dense_diagonal, hipStream_t st);
+                                int nsplit, bf16* ds_out, bool dense_diagonal, float* dq_suf,
+                                hipStream_t st);
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
                                   bf16* dv, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                               const bf16* dout, const float* lse, const float* Dd,
                               const int32_t* seq_T, void* dq, bool final_out,
                               bool dense_diagonal, hipStream_t st);
+// final_out with dq_add: adds the fp32 term dq_add before the bf16 write.
 hipError_t launch_bwd_dq_ds(const Shape& s, const bf16* k, const bf16* ds, const int32_t* seq_T,
-                            void* dq, bool final_out, hipStream_t st);
+                            void* dq, bool final_out, const float* dq_add, hipStream_t st);
 template <typename T>
 hipError_t launch_bwd_dkdv_valu(const Shape& s, const T* q, const T* k, const T* v,
                                 const T* dout, const float* lse, const float* Dd,

@@ -32,19 +32,21 @@ __global__ __launch_bounds__(256, 2) void probe_mfma_kernel(float* __restrict__ 
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-// Each workgroup copies one contiguous 32 KB chunk: every lane issues its eight 16-byte loads
-// (each one a coalesced 4 KB row of the chunk across the workgroup) before its eight stores,
-// so the grid keeps the whole buffer's worth of requests flowing with no loop.
+// Each workgroup copies one contiguous 16 KB chunk: every lane issues its four 16-byte loads
+// (each one a coalesced 4 KB row of the chunk across the workgroup) before its four stores, so
+// the grid keeps the whole buffer's worth of requests flowing with no loop.  Plain loads and
+// stores: on this chip they stream faster than the non-temporal forms for a pure copy
+// (5.8 against 4.4-5.3 TB/s for 16-32 KB chunks).
 __global__ __launch_bounds__(256) void probe_copy_kernel(const f32x4* __restrict__ src,
                                                          f32x4* __restrict__ dst, size_t n) {
-  const size_t base = (size_t)blockIdx.x * 2048 + threadIdx.x;
-  f32x4 r[8];
+  const size_t base = (size_t)blockIdx.x * 1024 + threadIdx.x;
+  f32x4 r[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    if (base + 256 * u < n) r[u] = __builtin_nontemporal_load(src + base + 256 * u);
+  for (int u = 0; u < 4; ++u)
+    if (base + 256 * u < n) r[u] = src[base + 256 * u];
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    if (base + 256 * u < n) __builtin_nontemporal_store(r[u], dst + base + 256 * u);
+  for (int u = 0; u < 4; ++u)
+    if (base + 256 * u < n) dst[base + 256 * u] = r[u];
 }
 
 }  // namespace ttt
@@ -63,7 +65,7 @@ int ttt_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (!src || !dst) return TTT_E_NULL;
   if (bytes == 0 || bytes % 16) return TTT_E_SHAPE;
   if (((uintptr_t)src | (uintptr_t)dst) & 15) return TTT_E_ALIGN;
-  const size_t n = bytes / 16, wgs = (n + 2047) / 2048;
+  const size_t n = bytes / 16, wgs = (n + 1023) / 1024;
   if (wgs >= (1ull << 31)) return TTT_E_SHAPE;
   ttt::probe_copy_kernel<<<dim3((unsigned)wgs), 256, 0, (hipStream_t)stream>>>(
       (const f32x4*)src, (f32x4*)dst, n);

@@ -20,8 +20,12 @@ TTT_DTYPE_BF16 = 1
 TTT_FLAG_SEPARATE_SUFFIX = 1
 TTT_FLAG_RECOMPUTE_DQ = 2
 TTT_FLAG_DENSE_DIAGONAL = 4
+TTT_FLAG_FUSED_SUFFIX_BWD = 8
 SUFFIX_PATHS = {"fused": 0, "separate": TTT_FLAG_SEPARATE_SUFFIX, "dense": TTT_FLAG_DENSE_DIAGONAL}
-DQ_MODES = {"stored": 0, "recompute": TTT_FLAG_RECOMPUTE_DQ}
+# backward paths: "stored" (dS handed from the dK/dV kernel to the dQ kernel, suffix kernel for
+# the diagonal keys), "recompute" (the dQ kernel recomputes S and dP), "fused-suffix" (stored dS,
+# and the dK/dV kernel also takes the diagonal keys' rows; no suffix kernel)
+DQ_MODES = {"stored": 0, "recompute": TTT_FLAG_RECOMPUTE_DQ, "fused-suffix": TTT_FLAG_FUSED_SUFFIX_BWD}
 
 STATUS = {
     0: "TTT_OK", -1: "TTT_E_NULL", -2: "TTT_E_SHAPE", -3: "TTT_E_UNSUPPORTED",
@@ -132,7 +136,8 @@ def make_params(B: int, Hq: int, Hkv: int, L: int, d: int, step: int, scale: flo
 
 def path_flags(suffix: str = "fused", dq_mode: str = "stored") -> int:
     """ttt_attn_params.flags for a forward suffix path ("fused" | "separate" | "dense") and a backward
-    dQ mode ("stored": dS handed from the dK/dV kernel to the dQ kernel | "recompute")."""
+    dQ mode ("stored": dS handed from the dK/dV kernel to the dQ kernel | "recompute" |
+    "fused-suffix": stored dS with the diagonal keys taken by the dK/dV kernel)."""
     if suffix not in SUFFIX_PATHS:
         raise ValueError(f"suffix must be one of {sorted(SUFFIX_PATHS)}, not {suffix!r}")
     if dq_mode not in DQ_MODES:

@@ -155,7 +155,8 @@ def test_workspace_sizes():
     (dict(scale=-0.088), -2),
     (dict(d=96), -3), (dict(d=256), -3), (dict(dtype=7), -3),
     (dict(dtype=A.TTT_DTYPE_F32, d=96), -3), (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10), -2),
-    (dict(flags=8), -3), (dict(flags=-1), -3), (dict(flags=5), -3),
+    (dict(flags=16), -3), (dict(flags=-1), -3), (dict(flags=5), -3), (dict(flags=8 | 2), -3),
+    (dict(flags=8 | 4), -3),
     # ttt_step + 1 must not wrap before it is widened; (k+1) * Q_LEN must fit in int32
     (dict(step=2**31 - 1), -2), (dict(step=2**31 - 1, L=1), -2), (dict(step=(2**31 - 1) // 4096), -2),
     # the vector-ALU path (bf16 outside the matrix-core tiling) launches one workgroup per row

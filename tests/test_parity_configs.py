@@ -39,10 +39,13 @@ def _run(lib, w, step, dq_mode="stored", suffix="fused"):
 
 # The default path merges the suffix inside the causal forward kernel and hands dS from the
 # dK/dV kernel to the dQ kernel; the extra cases run the backward whose dQ kernel recomputes
-# S and dP (small workspace) and the forward's standalone suffix kernel.
+# S and dP (small workspace), the forward's standalone suffix kernel, and the backward whose
+# dK/dV kernel also takes the diagonal keys' rows (heads split over workgroups at the 70B shape).
 @pytest.mark.parametrize("cfg,step,dq_mode,suffix", [c + ("stored", "fused") for c in CASES] +
                          [(2, 6, "recompute", "fused"), (3, 6, "recompute", "fused"),
-                          (2, 6, "stored", "separate"), (5, 12, "stored", "separate")])
+                          (2, 6, "stored", "separate"), (5, 12, "stored", "separate"),
+                          (2, 6, "fused-suffix", "fused"), (3, 6, "fused-suffix", "fused"),
+                          (4, 6, "fused-suffix", "fused"), (5, 12, "fused-suffix", "fused")])
 def test_workload_sampled_group_and_properties(gpu_lib, cfg, step, dq_mode, suffix):
     import torch
     w = inputs.WORKLOADS[cfg]

@@ -65,10 +65,12 @@ def test_bf16_valu_shapes(gpu_lib, step, T, d, L, Hq, Hkv):
 
 # ------------------------------------------------------------------ bf16 matrix-core path
 # Paths of the bf16 library: dq_mode "stored" (the dK/dV kernel hands dS to the dQ kernel
-# through the workspace) or "recompute" (the dQ kernel recomputes S and dP); suffix "fused"
+# through the workspace), "recompute" (the dQ kernel recomputes S and dP) or "fused-suffix"
+# (stored dS, and the dK/dV kernel also takes the diagonal keys' rows); suffix "fused"
 # (diagonal keys merged inside the causal forward kernel) or "separate" (the forward's
 # standalone suffix kernel on an fp32 state).
-PATHS = [("stored", "fused"), ("recompute", "fused"), ("stored", "separate")]
+PATHS = [("stored", "fused"), ("recompute", "fused"), ("stored", "separate"),
+         ("fused-suffix", "fused")]
 
 
 @pytest.mark.parametrize("dq_mode,suffix", PATHS)
@@ -118,9 +120,32 @@ def test_bf16_dense_diagonal_backward_block0_bitwise(gpu_lib):
 @pytest.mark.parametrize("step", [5, 12])
 def test_bf16_long_ttt(gpu_lib, step):
     """Many suffix blocks (the long-TTT workload runs to k = 12): fused, separate and dense
-    (masked diagonal matrix-core tiles) paths."""
+    (masked diagonal matrix-core tiles) paths, and the backward with the diagonal keys taken by
+    the dK/dV kernel."""
     for suffix in ("fused", "separate", "dense"):
         run_case(gpu_lib, 60 + step, 1, 4, 1, 128, 256, step, 201, "bf16", suffix=suffix)
+    run_case(gpu_lib, 60 + step, 1, 4, 1, 128, 256, step, 201, "bf16", dq_mode="fused-suffix")
+
+
+def test_bf16_fused_suffix_backward_agrees(gpu_lib):
+    """The backward with the diagonal keys taken by the dK/dV kernel against the default one:
+    block-0 dK/dV bitwise equal (same products), the diagonal rows and dq within the sum of
+    their bounds against the oracle; with the heads of a group split over workgroups (B=1)."""
+    import torch
+    from tests.helpers import to_dev
+    L = 512
+    q, k, v, do, T = inputs.make_case(58, 1, 8, 2, 128, L, 3, 433, "bf16")
+    qd, kd, vd, dod = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+    Td = torch.as_tensor(T, device="cuda")
+    o, lse = gpu_lib.ttt_attn_fwd(qd, kd, vd, Td)
+    a = gpu_lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod, dq_mode="fused-suffix")
+    b = gpu_lib.ttt_attn_bwd(qd, kd, vd, Td, o, lse, dod)
+    for x, y in ((a[1], b[1]), (a[2], b[2])):
+        assert torch.equal(x[:, :, :L].view(torch.int16), y[:, :, :L].view(torch.int16))
+        den = float(y.float().abs().max())
+        assert float((x.float() - y.float()).abs().max()) <= 4e-2 * den
+    den = float(b[0].float().abs().max())
+    assert float((a[0].float() - b[0].float()).abs().max()) <= 4e-2 * den
 
 
 def test_bf16_suffix_paths_agree(gpu_lib):
