@@ -194,7 +194,9 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
  * timing API below is enabled.  Calls whose scratch need exceeds the maximum return
  * TTT_E_SCRATCH before anything is launched (the five workloads of this library, up to
  * B 8 x Hq 32 x Q_LEN 2048 and B 2 x Hq 32 x Q_LEN 4096, fit).  The array belongs to the
- * current HIP device, which must be the device of `stream` and of the tensors.  Every call on
+ * current HIP device, which must be the device of `stream` and of the tensors; the first call
+ * on a device looks up the array's address (hipGetSymbolAddress) and is best made before any
+ * graph capture, later calls only enqueue kernels.  Every call on
  * one GPU shares that GPU's array, so calls that may overlap on one GPU (several streams or
  * threads) race and must be ordered by the caller.
  */

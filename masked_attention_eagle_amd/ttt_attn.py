@@ -259,6 +259,28 @@ def ttt_attn_bwd(q, k, v, seq_T, o, lse, dout, scale: Optional[float] = None, dq
     return dq, dk, dv
 
 
+def ttt_attn_bwd_noalloc(q, k, v, seq_T, o, lse, dout, scale: Optional[float] = None, dq=None,
+                         dk=None, dv=None):
+    """The backward on the library's own scratch array (no workspace; the dQ kernel recomputes S
+    and dP).  Outputs are allocated here unless given, so code that cannot allocate passes
+    dq, dk, dv.  Returns (dq, dk, dv)."""
+    import torch
+    lib = load()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    p = _params_from(q, k, scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _require(t, name, like.dtype, tuple(like.shape))
+    _check(lib.ttt_attn_bwd_noalloc(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    seq_T.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    _stream()))
+    return dq, dk, dv
+
+
 def _sweep_params(q, k, scale, flags: int) -> Params:
     """Params of a whole-TTT sweep: q [K, B, Hq, L, d] over the cache k [B, Hkv, K*L, d]."""
     if q.dim() != 5:

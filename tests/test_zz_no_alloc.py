@@ -56,3 +56,38 @@ def test_noalloc_backward_matches_workspace_backward(gpu_lib):
         for name, a, b in zip(("dq", "dk", "dv"), got, want):
             bits = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
             assert torch.equal(a.view(bits), b.view(bits)), f"{label}: {name} differs"
+
+
+def test_noalloc_backward_replays_in_a_graph(gpu_lib):
+    """The use the no-allocation backward is for: captured in a HIP graph (after one eager call,
+    which looks up the scratch array's address) with caller-owned outputs and no workspace, then
+    replayed three times with eager fills of the outputs between the replays; every replay
+    matches the eager call bitwise."""
+    import torch
+    q, k, v, do, T = inputs.make_case(85, 2, 8, 2, 128, 512, 3, (512, 377), "bf16")
+    print("graph no-alloc case B=2 Hq=8 Hkv=2 L=512 k=3", flush=True)
+    qd, kd, vd, dod = (to_dev(x, torch.bfloat16) for x in (q, k, v, do))
+    Td = torch.as_tensor(T, device="cuda")
+    o, lse = gpu_lib.ttt_attn_fwd(qd, kd, vd, Td)
+    refs = gpu_lib.ttt_attn_bwd_noalloc(qd, kd, vd, Td, o, lse, dod)
+    torch.cuda.synchronize()
+    outs = tuple(torch.empty_like(r) for r in refs)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gpu_lib.ttt_attn_bwd_noalloc(qd, kd, vd, Td, o, lse, dod, dq=outs[0], dk=outs[1], dv=outs[2])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gpu_lib.ttt_attn_bwd_noalloc(qd, kd, vd, Td, o, lse, dod, dq=outs[0], dk=outs[1], dv=outs[2])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, ref in zip(("dq", "dk", "dv"), outs, refs):
+            assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {rep}: {name}"
