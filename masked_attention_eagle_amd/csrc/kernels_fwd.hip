@@ -222,20 +222,34 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
         }
       }
       if (full || wide) {
+        // four V fragments in flight: slot c is refilled with column block u + 1 right
+        // after product (u, c) is issued, four products before it is needed
+        bf16x8 vf[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            acc[u] = mfma32(frag_col(cV, c, u, fl), pf[c], acc[u]);
-        }
-      } else {  // both parts of P go through the same V operands
+        for (int c = 0; c < 4; ++c) vf[c] = frag_col(cV, c, 0, fl);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const bf16x8 a = frag_col(cV, c, u, fl);
-            acc[u] = mfma32(a, pf[c], acc[u]);
-            acc[u] = mfma32(a, pl[c], acc[u]);
+            acc[u] = mfma32(vf[c], pf[c], acc[u]);
+            if (u < 3) vf[c] = frag_col(cV, c, u + 1, fl);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      } else {  // both parts of P go through the same V operands (same four slots)
+        bf16x8 vf[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vf[c] = frag_col(cV, c, 0, fl);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[u] = mfma32(vf[c], pf[c], acc[u]);
+            acc[u] = mfma32(vf[c], pl[c], acc[u]);
+            if (u < 3) vf[c] = frag_col(cV, c, u + 1, fl);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
