@@ -171,17 +171,27 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
 
-// Asynchronous global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
-// lane l of the wave writes lds_base + 16 * l; lds_base must be the same for the whole wave.
-__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// Buffer resource for raw loads of `bytes` bytes starting at `base` (wave-uniform); loads at
+// offsets past `bytes` return zero instead of reading memory.  0x00020000 is the gfx9 third
+// descriptor word for untyped 32-bit data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Same, 4 bytes per lane (global_load_lds_dword): lane l writes lds_base + 4 * l.
-__device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+// Asynchronous global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane l
+// reads byte offset voff of the buffer and writes lds_base + 16 * l; lds_base must be the same
+// for the whole wave.  The buffer form (rather than global_load_lds) lets the compiler keep
+// counting LDS reads precisely while the copy is in flight: it treats the global form like a
+// flat access and then waits for every outstanding LDS read.
+__device__ __forceinline__ void g2lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           voff, 0, 0, 0);
+}
+
+// Same, 4 bytes per lane (buffer_load_dword ... lds): lane l writes lds_base + 4 * l.
+__device__ __forceinline__ void g2lds4(__amdgpu_buffer_rsrc_t rs, unsigned voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 4,
+                                           voff, 0, 0, 0);
 }
 
 // 16-byte load from global memory at base + off (base wave-uniform, off per lane), kept a
@@ -246,16 +256,16 @@ __device__ __forceinline__ void load_tile(const bf16* g, int ld, bf16* lds, int 
   static_assert(NWAVES % 4 == 0, "swizzle term must be constant per wave");
   const int rl = lane >> 4;
   const unsigned lane_off = (unsigned)(rl * ld + (((lane & 15) ^ ((rl << 2) | (wave & 3))) << 3));
-  // Scalar base + 32-bit per-lane byte offset: the copies use the saddr form and hold no
+  // Scalar resource (the tile's rows) + 32-bit per-lane byte offset: the copies hold no
   // 64-bit per-lane addresses in vector registers.
-  const char* base = reinterpret_cast<const char*>(uniform_ptr(g));
+  const auto rs = buffer_rsrc(uniform_ptr(g), 2u * NROWS * ld);
   static_assert((NROWS / 4) % NWAVES == 0, "whole 4-row groups per wave");
 #pragma unroll
   for (int r = 0; r < NROWS / 4 / NWAVES; ++r) {  // a fixed count: no branches per copy
     const int i = wave + r * NWAVES;
     unsigned off = 2u * ((unsigned)(4 * i * ld) + lane_off);
     asm volatile("" : "+v"(off));  // keeps the 32-bit offset form (no 64-bit copies to hold)
-    g2lds16(base + off, lds + i * 512);
+    g2lds16(rs, off, lds + i * 512);
   }
 }
 

@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
       if (wave < 2 && lane < KBM) {  // wave 0: lse * log2(e) of the 32 rows to dLD[0, 32); wave 1: D to dLD[32, 64)
         unsigned off = 4u * lane;
         asm volatile("" : "+v"(off));
-        g2lds4(reinterpret_cast<const char*>(uniform_ptr((wave == 0 ? lse2 : Dd) + row0)) + off,
+        g2lds4(buffer_rsrc(uniform_ptr((wave == 0 ? lse2 : Dd) + row0), 4u * KBM), off,
                dLD + KBM * wave);
       }
     };
@@ -325,18 +325,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
           store16_global_nt(dst, off0, dsb[0]);
           store16_global_nt(dst, off1, dsb[1]);
         }
+        // dV then dK products, i = 0..15 (i < 8: dV, (u, c) = (i / 2, i % 2) from the dO
+        // tile; then dK from the Q tile); operand fragments four products ahead in slots i % 4
+        auto frag_dvk = [&](int i) {
+          return frag_col(i < 8 ? cO : cQ, i & 1, (i >> 1) & 3, fl);
+        };
+        bf16x8 fr[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            dVacc[u] = mfma32(pb[c], frag_col(cO, c, u, fl), dVacc[u]);
-        }
+        for (int i = 0; i < 4; ++i) fr[i] = frag_dvk(i);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            dKacc[u] = mfma32(dsb[c], frag_col(cQ, c, u, fl), dKacc[u]);
+        for (int i = 0; i < 16; ++i) {
+          const int u = (i >> 1) & 3, c = i & 1;
+          if (i < 8)
+            dVacc[u] = mfma32(pb[c], fr[i & 3], dVacc[u]);
+          else
+            dKacc[u] = mfma32(dsb[c], fr[i & 3], dKacc[u]);
+          if (i + 4 < 16) fr[i & 3] = frag_dvk(i + 4);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       wait_vmem();
