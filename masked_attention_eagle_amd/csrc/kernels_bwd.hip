@@ -302,9 +302,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
         pb[0] = to_bf16x8(acc, 0);
         pb[1] = to_bf16x8(acc, 8);
         acc = f32x16{};
+        // dO fragments 2 products ahead (slot t % 2 refilled right after product t issues)
+        bf16x8 ofr[2];
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-          acc = mfma32(frag_row(cO, 0, t, fl), vf[t], acc);
+        for (int t = 0; t < 2; ++t) ofr[t] = frag_row(cO, 0, t, fl);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          acc = mfma32(ofr[t % 2], vf[t], acc);
+          if (t + 2 < 8) ofr[t % 2] = frag_row(cO, 0, t + 2, fl);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         // dS from the bf16 P that the dV product uses
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
