@@ -124,6 +124,10 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+      // the first four V fragments of the P V products, read while P is formed
+      bf16x8 vf[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) vf[c] = frag_col(cV, c, 0, fl);
       const bool full = !diag && (k0 + FBN - 1 <= qw) && (k0 + FBN <= T);
       // every row of the wave sees at least 64 keys of block 0 (rows i < T see min(i + 1, T),
       // rows i >= T see T): one bf16 rounding of P then costs O no more than on full tiles
@@ -224,9 +228,6 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
       if (full || wide) {
         // four V fragments in flight: slot c is refilled with column block u + 1 right
         // after product (u, c) is issued, four products before it is needed
-        bf16x8 vf[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) vf[c] = frag_col(cV, c, 0, fl);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -238,9 +239,6 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
           }
         }
       } else {  // both parts of P go through the same V operands (same four slots)
-        bf16x8 vf[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) vf[c] = frag_col(cV, c, 0, fl);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
