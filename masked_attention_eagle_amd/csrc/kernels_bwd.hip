@@ -539,13 +539,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
     const int k0 = diag ? q0 + QBN * ((j - ncausal) & 1) : j * QBN;
     if (diag ? (k0 <= qw + 31 && qw <= k0 + QBN - 1) : (k0 <= qw + 31)) {
       f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
+      // product i = 4t + 2st + (0: S from K, 1: dP from V); its K or V fragment is read
+      // four products ahead into slot i % 4
+      auto frag_sp = [&](int i) {
+        return frag_row((i & 1) ? cV : cK, ((i >> 1) & 1) * 32, i >> 2, fl);
+      };
+      bf16x8 fr[4];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int i = 0; i < 4; ++i) fr[i] = frag_sp(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          sacc[st] = mfma32(frag_row(cK, st * 32, t, fl), qf[t], sacc[st]);
-          pacc[st] = mfma32(frag_row(cV, st * 32, t, fl), df[t], pacc[st]);
-        }
+      for (int i = 0; i < 32; ++i) {
+        const int t = i >> 2, st = (i >> 1) & 1;
+        if (i & 1)
+          pacc[st] = mfma32(fr[i & 3], df[t], pacc[st]);
+        else
+          sacc[st] = mfma32(fr[i & 3], qf[t], sacc[st]);
+        if (i + 4 < 32) fr[i & 3] = frag_sp(i + 4);
+        __builtin_amdgcn_sched_barrier(0);
       }
       const bool full = !diag && (k0 + QBN - 1 <= qw) && (k0 + QBN <= T);
       bf16x8 dsb[4];
@@ -564,11 +575,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_mfma_kernel(
           dsb[2 * st + (i >> 3)][i & 7] = (bf16)(pv * (pacc[st][i] - Dq));
         }
       }
+      // K fragments four products ahead: slot c refilled with column block u + 1 right after
+      // product (u, c) is issued
+      bf16x8 kfr[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kfr[c] = frag_col(cK, c, 0, fl);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[u] = mfma32(frag_col(cK, c, u, fl), dsb[c], acc[u]);
+        for (int c = 0; c < 4; ++c) {
+          acc[u] = mfma32(kfr[c], dsb[c], acc[u]);
+          if (u < 3) kfr[c] = frag_col(cK, c, u + 1, fl);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     wait_vmem();
