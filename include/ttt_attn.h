@@ -215,7 +215,11 @@ int ttt_attn_version(void);
  * Optional per-kernel timing, for measurement.  When enabled, every kernel launch of
  * ttt_attn_fwd/bwd is bracketed by hipEvents on the launch stream; ttt_attn_timing_read
  * synchronises those events and returns, per kernel name, the number of launches and the
- * summed milliseconds since the last reset.  Not thread-safe; off by default.
+ * summed milliseconds since the last reset.  Off by default.  Thread-safe: launches from
+ * several threads may be timed at once, and a read or reset counts the launches that have
+ * returned from their library call by then (one still inside its call is counted by the next
+ * read).  While enabled, each timed launch takes a pair of hipEvents from a pool that grows as
+ * needed and lasts until the process ends.
  */
 typedef struct ttt_attn_kernel_time {
   char name[48];
@@ -231,7 +235,8 @@ void ttt_attn_timing_reset(void);
  * preceded (outside its events) by a kernel that overwrites `bytes` of `buf` with plain
  * stores, so each kernel starts with caches that hold none of its data (give more than the
  * 256 MB last-level cache).  buf is caller-owned device memory, 16-byte aligned, bytes a
- * non-zero multiple of 16 (else TTT_E_ALIGN); NULL turns it off.  Not thread-safe.
+ * non-zero multiple of 16 (else TTT_E_ALIGN); NULL turns it off.  The buffer is shared by every
+ * thread's timed launches: launches on different streams then overwrite it concurrently.
  */
 int ttt_attn_timing_flush(void* buf, size_t bytes);
 

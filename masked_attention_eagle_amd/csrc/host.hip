@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -13,16 +14,20 @@
 namespace ttt {
 
 // ------------------------------------------------------------------ per-launch timing hook
+// Launches from several threads may be timed at once: all state below is guarded by g_mu, and a
+// timer keeps its own events until its launch is done, so a read or reset from another thread
+// never takes events that a launch still uses.
 namespace {
 struct TimingRecord {
   const char* name;
   hipEvent_t start, stop;
 };
-bool g_timing_on = false;
+std::mutex g_mu;
+std::atomic<bool> g_timing_on{false};
 void* g_flush_buf = nullptr;  // with timing on: overwritten before every timed launch
 size_t g_flush_bytes = 0;
-std::vector<TimingRecord> g_records;  // events recorded since the last read/reset
-size_t g_used = 0;
+std::vector<TimingRecord> g_free;  // event pairs ready for reuse
+std::vector<TimingRecord> g_done;  // launches whose stop event is recorded, not yet read
 
 struct Accum {
   char name[48];
@@ -32,21 +37,31 @@ struct Accum {
 std::vector<Accum> g_accum;
 }  // namespace
 
-LaunchTimer::LaunchTimer(const char* name, hipStream_t st) : name_(name), st_(st), slot_(-1) {
-  if (!g_timing_on) return;
-  if (g_used == g_records.size()) {
-    TimingRecord r{name, nullptr, nullptr};
-    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
-    g_records.push_back(r);
+LaunchTimer::LaunchTimer(const char* name, hipStream_t st)
+    : name_(name), st_(st), start_(nullptr), stop_(nullptr), on_(false) {
+  if (!g_timing_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_free.empty()) {
+    start_ = g_free.back().start;
+    stop_ = g_free.back().stop;
+    g_free.pop_back();
+  } else {
+    if (hipEventCreate(&start_) != hipSuccess) return;
+    if (hipEventCreate(&stop_) != hipSuccess) {
+      hipEventDestroy(start_);
+      return;
+    }
   }
-  slot_ = (int)g_used++;
-  g_records[slot_].name = name;
+  on_ = true;
   if (g_flush_buf) launch_flush_fill(g_flush_buf, g_flush_bytes, st);  // outside the timed span
-  hipEventRecord(g_records[slot_].start, st);
+  hipEventRecord(start_, st);
 }
 
 LaunchTimer::~LaunchTimer() {
-  if (slot_ >= 0) hipEventRecord(g_records[slot_].stop, st_);
+  if (!on_) return;
+  hipEventRecord(stop_, st_);
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_done.push_back(TimingRecord{name_, start_, stop_});
 }
 
 static void accumulate(const char* name, double ms) {
@@ -605,19 +620,22 @@ int ttt_loss_grad_inplace(const ttt_loss_params* p, void* z, const void* target,
 }
 
 int ttt_attn_timing_enable(int on) {
-  const int prev = g_timing_on ? 1 : 0;
-  g_timing_on = on != 0;
-  return prev;
+  return g_timing_on.exchange(on != 0) ? 1 : 0;
 }
 
 int ttt_attn_timing_read(ttt_attn_kernel_time* out, int max_entries) {
-  for (size_t i = 0; i < g_used; ++i) {
-    if (hipEventSynchronize(g_records[i].stop) != hipSuccess) return TTT_E_HIP;
+  std::lock_guard<std::mutex> lock(g_mu);
+  int status = TTT_OK;
+  for (const auto& r : g_done) {
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, g_records[i].start, g_records[i].stop) != hipSuccess) return TTT_E_HIP;
-    accumulate(g_records[i].name, ms);
+    if (status == TTT_OK && (hipEventSynchronize(r.stop) != hipSuccess ||
+                             hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess))
+      status = TTT_E_HIP;
+    if (status == TTT_OK) accumulate(r.name, ms);
+    g_free.push_back(r);
   }
-  g_used = 0;
+  g_done.clear();
+  if (status != TTT_OK) return status;
   int n = 0;
   for (const auto& a : g_accum) {
     if (n >= max_entries) break;
@@ -634,14 +652,19 @@ int ttt_attn_timing_read(ttt_attn_kernel_time* out, int max_entries) {
 
 int ttt_attn_timing_flush(void* buf, size_t bytes) {
   if (buf && (((uintptr_t)buf & 15) || bytes % 16 || bytes == 0)) return TTT_E_ALIGN;
+  std::lock_guard<std::mutex> lock(g_mu);
   g_flush_buf = buf;
   g_flush_bytes = buf ? bytes : 0;
   return TTT_OK;
 }
 
 void ttt_attn_timing_reset(void) {
-  for (size_t i = 0; i < g_used; ++i) hipEventSynchronize(g_records[i].stop);
-  g_used = 0;
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (const auto& r : g_done) {
+    hipEventSynchronize(r.stop);
+    g_free.push_back(r);
+  }
+  g_done.clear();
   g_accum.clear();
 }
 

@@ -8,13 +8,15 @@
 
 namespace ttt {
 
-// Per-launch timing hook (implemented by the host library).
+// Per-launch timing hook (implemented by the host library).  While timing is enabled it holds
+// its own pair of events from the start of the launch to the end of the scope.
 struct LaunchTimer {
   LaunchTimer(const char* name, hipStream_t st);
   ~LaunchTimer();
   const char* name_;
   hipStream_t st_;
-  int slot_;
+  hipEvent_t start_, stop_;
+  bool on_;
 };
 
 // Forward.

@@ -53,3 +53,47 @@ def test_cold_cache_timing_keeps_results(gpu_lib):
     for a, b in zip(got, ref):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert bool((flush == 0).all())  # the flush wrote zeros over the whole buffer
+
+
+def test_timing_counts_launches_from_two_threads(gpu_lib):
+    """Timed launches from two threads on their own streams: every launch is counted once and
+    the results are those of an untimed call."""
+    import threading
+    import torch
+    q, k, v, _, T = inputs.make_case(92, 2, 4, 2, 128, 256, 2, (256, 170), "bf16")
+    qd, kd, vd = (to_dev(x, torch.bfloat16) for x in (q, k, v))
+    Td = torch.as_tensor(T, device="cuda")
+    ref_o, ref_lse = gpu_lib.ttt_attn_fwd(qd, kd, vd, Td)
+    torch.cuda.synchronize()
+    n_calls, results, errors = 6, {}, []
+
+    def worker(tag):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [gpu_lib.ttt_attn_fwd(qd, kd, vd, Td) for _ in range(n_calls)]
+            s.synchronize()
+            results[tag] = outs
+        except Exception as e:  # reported below, in the test's thread
+            errors.append(e)
+
+    gpu_lib.timing_reset()
+    gpu_lib.timing_enable(True)
+    try:
+        threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+    finally:
+        gpu_lib.timing_enable(False)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    times = gpu_lib.timing_read()
+    assert times["fwd_causal_mfma"][0] == 2 * n_calls
+    assert times["fwd_causal_mfma"][1] > 0
+    for outs in results.values():
+        for o, lse in outs:
+            assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
+            assert torch.equal(lse, ref_lse)
+    assert gpu_lib.timing_read()["fwd_causal_mfma"][0] == 2 * n_calls  # nothing read twice
