@@ -168,7 +168,9 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
  * gradient of all of them); every sum is kept in fp32 inside the kernels (block 0's in one
  * dK/dV launch over the queries of all steps, blocks 1..k in one suffix launch over all steps)
  * and rounded to bf16 once.  The backward's workspace holds D, lse * log2(e), the fp32 block-0
- * dQ of steps 1..k and (stored-dS path) the dS blocks of every step.
+ * dQ of steps 1..k and (stored-dS path) the dS blocks of every step: 8.5 GB at B 2, Hq 32,
+ * Q_LEN 4096, K 7, against 0.95 GB with TTT_FLAG_RECOMPUTE_DQ (which then recomputes S and dP
+ * in the dQ kernel, about 6% more time for that workload).
  * Launches run in order on `stream`; flags select the paths as for the per-step calls.
  * Same error codes; fp32 data returns TTT_E_UNSUPPORTED.
  */
