@@ -210,7 +210,11 @@ int ttt_attn_bwd_noalloc(const ttt_attn_params* p, const void* q, const void* k,
 /* Static text for a status code. */
 const char* ttt_attn_status_string(int status);
 
-/* ABI version (major * 100 + minor). */
+/*
+ * ABI version (major * 100 + minor).  1.03 added ttt_attn_bwd_noalloc (with TTT_E_SCRATCH),
+ * TTT_FLAG_FUSED_SUFFIX_BWD and ttt_attn_timing_flush, and made the timing calls thread-safe;
+ * 1.02 changed the whole-TTT backward's workspace size.
+ */
 int ttt_attn_version(void);
 
 /*

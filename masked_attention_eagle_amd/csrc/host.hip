@@ -272,7 +272,7 @@ using namespace ttt;
 
 extern "C" {
 
-int ttt_attn_version(void) { return 102; }
+int ttt_attn_version(void) { return 103; }
 
 const char* ttt_attn_status_string(int status) {
   switch (status) {

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(A.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.ttt_attn_version() == 102
+    assert lib.ttt_attn_version() == 103
     loss_declared = header_functions("ttt_loss.h", "ttt_loss_")
     assert set(loss_declared) == set(A.LOSS_EXPORTS)
     for name in loss_declared:
