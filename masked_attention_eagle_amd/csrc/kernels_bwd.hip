@@ -153,6 +153,9 @@ __device__ __forceinline__ void dkdv_suffix_rows(
 // Key tile kt is seen by every query row >= 128 * kt (padded rows see every key < T), so the
 // work of tile kt falls linearly with kt.  A workgroup takes the complementary pair
 // (p, n - 1 - p) of key tiles, which makes every workgroup's work equal.
+// The register file is full (dK/dV accumulators 128, K/V fragments 64 of 256), so operand
+// reads run only as far ahead as the spare registers allow: the dO fragments of the dP
+// products two ahead, the dO and Q fragments of the dV and dK products four ahead.
 // DIAG (measurement variant of the backward, the way a BlockMask-driven kernel handles the
 // suffix): after the workgroups of block 0, one workgroup per (b, KV group, block t = 1..k,
 // 128-key tile) takes the key rows [t*Q_LEN + k0, t*Q_LEN + k0 + 128) and the query rows

@@ -30,7 +30,10 @@ namespace ttt {
 //
 // K and V tiles are copied global -> LDS without passing through registers (two stages),
 // which keeps the wave under 256 registers: two workgroups share a CU and the matrix cores
-// of one overlap the softmax of the other.
+// of one overlap the softmax of the other.  Operand fragments are read from LDS ahead of
+// their products so that no product waits for its own read: the K fragments two to three
+// products ahead (scheduling groups), the V fragments four ahead in register slots, the
+// first four of them while the softmax runs.
 // ----------------------------------------------------------------------------------------
 constexpr int FD = 128;  // head dim
 constexpr int FBM = 128; // queries per workgroup
