@@ -207,7 +207,8 @@ def main():
         torch.cuda.empty_cache()
         sub = measure(args, 4, peaks)
         out["also"] = {sub["config"]["workload"]: {
-            k: sub[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s", "step_ms",
+            k: sub[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s",
+                                "valid_tokens_per_s", "step_ms",
                                 "pct_roofline", "roofline", "config", "unmasked_flop_per_step")}}
     if peaks is not None:
         out["peaks_measured"] = peaks
@@ -488,6 +489,8 @@ def measure(args, config, peaks=None):
         "dq_mode": args.dq_mode, "suffix": args.suffix,
         "api": "sweep" if args.sweep else "per-step",
         "tokens_per_s": round(tokens, 1),
+        # tokens inside the sequences' lengths (sum of T over the batch), per second
+        "valid_tokens_per_s": round(float(sum(int(t) for t in T)) / sec, 1),
         "pct_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof / sec, 4),
                          "causal_flop": f_causal, "suffix_bytes": b_suffix, "preprocess_bytes": b_pre},
         "step_ms": {"median": round(float(np.median(step_ms)), 4), "min": round(step_ms[0], 4),
