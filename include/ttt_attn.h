@@ -124,6 +124,8 @@ size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p);
 /*
  * The default bf16 backward workspace holds the dS of block 0: B * Hq * n(n+1)/2 blocks of
  * 2 KB, n = Q_LEN / 32 (1.08 GB at B 2, Hq 32, Q_LEN 4096); TTT_FLAG_RECOMPUTE_DQ avoids it.
+ * It also holds the dK/dV kernel's work-queue counters, another reason why calls in flight
+ * at the same time need distinct workspaces.
  */
 
 /*

@@ -183,9 +183,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // for the whole wave.  The buffer form (rather than global_load_lds) lets the compiler keep
 // counting LDS reads precisely while the copy is in flight: it treats the global form like a
 // flat access and then waits for every outstanding LDS read.
-__device__ __forceinline__ void g2lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, void* lds_base) {
+__device__ __forceinline__ void g2lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, void* lds_base,
+                                        int soff = 0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                           voff, 0, 0, 0);
+                                           voff, soff, 0, 0);
 }
 
 // Same, 4 bytes per lane (buffer_load_dword ... lds): lane l writes lds_base + 4 * l.
@@ -266,6 +267,24 @@ __device__ __forceinline__ void load_tile(const bf16* g, int ld, bf16* lds, int 
     unsigned off = 2u * ((unsigned)(4 * i * ld) + lane_off);
     asm volatile("" : "+v"(off));  // keeps the 32-bit offset form (no 64-bit copies to hold)
     g2lds16(rs, off, lds + i * 512);
+  }
+}
+
+// load_tile with one per-lane offset register for all of the wave's copies: the 4-row group's
+// offset goes into the buffer instruction's scalar offset instead.  For kernels short of
+// vector registers (in the forward the scalar form measured slower).
+template <int NROWS, int NWAVES>
+__device__ __forceinline__ void load_tile_soff(const bf16* g, int ld, bf16* lds, int wave, int lane) {
+  static_assert(NWAVES % 4 == 0, "swizzle term must be constant per wave");
+  static_assert((NROWS / 4) % NWAVES == 0, "whole 4-row groups per wave");
+  const int rl = lane >> 4;
+  unsigned off = 2u * (unsigned)(rl * ld + (((lane & 15) ^ ((rl << 2) | (wave & 3))) << 3));
+  asm volatile("" : "+v"(off));
+  const auto rs = buffer_rsrc(uniform_ptr(g), 2u * NROWS * ld);
+#pragma unroll
+  for (int r = 0; r < NROWS / 4 / NWAVES; ++r) {
+    const int i = wave + r * NWAVES;
+    g2lds16(rs, off, lds + i * 512, 8 * i * ld);
   }
 }
 

@@ -200,7 +200,7 @@ FwdLayout fwd_layout(const Shape& s, bool fused) {
 }
 
 struct BwdLayout {
-  size_t Dd = 0, lse2 = 0, part = 0, ds = 0, dqacc = 0, total = 0;
+  size_t Dd = 0, lse2 = 0, sched = 0, part = 0, ds = 0, dqacc = 0, total = 0;
   int nsplit = 1;
 };
 // D; (bf16) lse * log2(e) for the dK/dV kernel and the split dK/dV partials (heads of a group
@@ -221,6 +221,8 @@ BwdLayout bwd_layout(const Shape& s, bool mfma, bool with_ds, bool dense = false
   if (mfma) {
     w.lse2 = off;
     off += round_up(rows_q * 4);
+    w.sched = off;  // the dK/dV kernel's queue counters, one per 128-byte line
+    off += round_up(8 * 128);
     w.nsplit = dkdv_nsplit(s);
     if (w.nsplit > 1) {
       w.part = off;
@@ -328,7 +330,8 @@ hipError_t bwd_valu(const Shape& s, const void* q, const void* k, const void* v,
   const T* vt = (const T*)v;
   const T* dot = (const T*)dout;
   hipError_t e;
-  if ((e = launch_bwd_rowdot<T>(s, (const T*)o, dot, Dd, nullptr, nullptr, st)) != hipSuccess)
+  if ((e = launch_bwd_rowdot<T>(s, (const T*)o, dot, Dd, nullptr, nullptr, nullptr, st)) !=
+      hipSuccess)
     return e;
   if ((e = launch_bwd_dkdv_valu<T>(s, qt, kt, vt, dot, lse, Dd, seq_T, (T*)dk, (T*)dv, st)) !=
       hipSuccess)
@@ -388,13 +391,16 @@ int run_bwd(const ttt_attn_params* p, const Shape& s, const void* q, const void*
     bf16* dsb = with_ds ? (bf16*)(ws + w.ds) : nullptr;
     void* dq_causal = final_causal ? dq : (void*)dqacc;
     float* lse2 = (float*)(ws + w.lse2);
-    if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, lse, lse2, st)) != hipSuccess)
+    unsigned* sched = (unsigned*)(ws + w.sched);
+    if ((e = launch_bwd_rowdot<bf16>(s, (const bf16*)o, dob, Dd, lse, lse2, sched, st)) !=
+        hipSuccess)
       return TTT_E_HIP;
     // fused: the dK/dV kernel writes the suffix rows and the suffix dQ term (into the dQ
     // accumulator's space), and the dQ kernel adds that term and writes the final dq
     const bool fused = fused_bwd_suffix(p);
     if ((e = launch_bwd_dkdv_mfma(s, qb, kb, vb, dob, lse2, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
-                                  w.nsplit, dsb, dense, fused ? dqacc : nullptr, st)) != hipSuccess)
+                                  w.nsplit, dsb, dense, fused ? dqacc : nullptr, sched, st)) !=
+        hipSuccess)
       return TTT_E_HIP;
     if (w.nsplit > 1 &&
         (e = launch_bwd_dkdv_reduce(s, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
@@ -571,10 +577,11 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
   hipError_t e;
   // Block 0: one row-dot launch, one dK/dV launch and one reduction over the queries of all
   // steps (the keys of block 0 are seen by every step), which writes its dk/dv rows.
-  if ((e = launch_bwd_rowdot<bf16>(sa, (const bf16*)o, dob, Dd, lse, lse2, st)) != hipSuccess)
+  unsigned* sched = (unsigned*)(ws + w.sched);
+  if ((e = launch_bwd_rowdot<bf16>(sa, (const bf16*)o, dob, Dd, lse, lse2, sched, st)) != hipSuccess)
     return TTT_E_HIP;
   if ((e = launch_bwd_dkdv_mfma(sa, qb, kb, vb, dob, lse2, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
-                                w.nsplit, dsb, false, nullptr, st)) != hipSuccess)
+                                w.nsplit, dsb, false, nullptr, sched, st)) != hipSuccess)
     return TTT_E_HIP;
   if (w.nsplit > 1 &&
       (e = launch_bwd_dkdv_reduce(sa, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)

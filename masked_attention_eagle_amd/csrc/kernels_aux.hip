@@ -7,15 +7,19 @@ namespace ttt {
 // D_i = sum_d dO_i * O_i, the row term of the softmax Jacobian (dS = P * (dP - D)).
 // 16 lanes per row.  With lse2 set it also writes lse_i * log2(e), the base-2 row offset of
 // P = exp2(S * scale * log2(e) - lse * log2(e)), so that the matrix-core dK/dV kernel, whose
-// lanes each meet 16 rows per tile, subtracts it without a multiply per element.
+// lanes each meet 16 rows per tile, subtracts it without a multiply per element.  With sched
+// set, workgroup 0 also sets the matrix-core dK/dV kernel's 8 queue counters (one per
+// 128-byte line, sched[32 i]) to zero: that kernel runs next on the same stream.
 // ----------------------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ o,
                                                      const T* __restrict__ dout,
                                                      float* __restrict__ Dd,
                                                      const float* __restrict__ lse,
-                                                     float* __restrict__ lse2, size_t nrows) {
+                                                     float* __restrict__ lse2,
+                                                     unsigned* __restrict__ sched, size_t nrows) {
   constexpr int E = D / 16;
+  if (sched && blockIdx.x == 0 && threadIdx.x < 8) sched[32 * threadIdx.x] = 0u;
   const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   if (row >= nrows) return;
@@ -34,20 +38,20 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ o,
 
 template <typename T>
 hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* Dd,
-                             const float* lse, float* lse2, hipStream_t st) {
+                             const float* lse, float* lse2, unsigned* sched, hipStream_t st) {
   const size_t nrows = (size_t)s.B * s.Hq * s.L * s.nst;
   const dim3 grid((unsigned)((nrows + 15) / 16));
   LaunchTimer timer("bwd_rowdot", st);
   if (s.D == 64)
-    rowdot_kernel<T, 64><<<grid, 256, 0, st>>>(o, dout, Dd, lse, lse2, nrows);
+    rowdot_kernel<T, 64><<<grid, 256, 0, st>>>(o, dout, Dd, lse, lse2, sched, nrows);
   else
-    rowdot_kernel<T, 128><<<grid, 256, 0, st>>>(o, dout, Dd, lse, lse2, nrows);
+    rowdot_kernel<T, 128><<<grid, 256, 0, st>>>(o, dout, Dd, lse, lse2, sched, nrows);
   return hipGetLastError();
 }
 template hipError_t launch_bwd_rowdot<float>(const Shape&, const float*, const float*, float*,
-                                             const float*, float*, hipStream_t);
+                                             const float*, float*, unsigned*, hipStream_t);
 template hipError_t launch_bwd_rowdot<bf16>(const Shape&, const bf16*, const bf16*, float*,
-                                            const float*, float*, hipStream_t);
+                                            const float*, float*, unsigned*, hipStream_t);
 
 // Writes `bytes` (a multiple of 16) of buf with plain stores: run before a timed launch, it
 // replaces what the caches (L2 and the memory-side last-level cache) hold.

@@ -151,8 +151,17 @@ __device__ __forceinline__ void dkdv_suffix_rows(
 }
 
 // Key tile kt is seen by every query row >= 128 * kt (padded rows see every key < T), so the
-// work of tile kt falls linearly with kt.  A workgroup takes the complementary pair
-// (p, n - 1 - p) of key tiles, which makes every workgroup's work equal.
+// work of tile kt falls linearly with kt and is zero from T on.  Workgroups take (key tile,
+// head share) units from a queue in that order, heaviest first, until it is empty, so that
+// one that finishes early takes the next unit (with sequences of different lengths, fixed
+// pairs of tiles would leave some workgroups little or no work).  The queue is a counter in
+// the workspace per XCD (when the KV groups or units spread evenly over the 8 XCDs, so that a
+// group's Q/dO stay in one L2) or one for all; the row-dot kernel, launched just before on
+// the same stream, sets it to zero.  Each unit's dK/dV (or split partial) is summed in the
+// same order whichever workgroup takes it, so the results do not depend on the schedule.
+// The kernel sits at the scalar-register limit, and scalars spilled into vector registers
+// would cost the tile loop its operand read-ahead: the queue's address is kept in an LDS
+// word and the tile position in 32-bit indices.
 // The register file is full (dK/dV accumulators 128, K/V fragments 64 of 256), so operand
 // reads run only as far ahead as the spare registers allow: the dO fragments of the dP
 // products two ahead, the dO and Q fragments of the dV and dK products four ahead.
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dd,
     const int32_t* __restrict__ seq_T, bf16* __restrict__ dk, bf16* __restrict__ dv,
     float* __restrict__ part, int nsplit, bf16* __restrict__ ds_out, float* __restrict__ dq_suf,
-    Shape s) {
+    unsigned* __restrict__ sched, Shape s) {
   // Two stages in distinct arrays (the copy into one never stalls reads of the other).
   __shared__ __attribute__((aligned(1024))) bf16 sQ0[KBM * BD];
   __shared__ __attribute__((aligned(1024))) bf16 sO0[KBM * BD];
@@ -179,34 +188,52 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 sO1[KBM * BD];
   __shared__ __attribute__((aligned(256))) float sLD1[2 * KBM];
 
+  __shared__ int sUnit;
+  __shared__ unsigned* sQueue;  // this workgroup's queue counter (kept out of the registers)
   const int nkt = s.L / KBN;
-  const int n_pair_wgs = s.B * s.Hkv * nsplit * ((nkt + 1) / 2);
+  const int groups = s.B * s.Hkv, n_units = groups * nsplit;
+  const int n_pair_wgs = n_units * ((nkt + 1) / 2);
   const bool dwg = DIAG && (int)blockIdx.x >= n_pair_wgs;  // a diagonal tile of a block t >= 1
-  int unit, pair, tblk = 0, nsp = nsplit;
-  if (dwg) {
-    const int d = (int)blockIdx.x - n_pair_wgs;
-    unit = d % (s.B * s.Hkv);
-    pair = (d / (s.B * s.Hkv)) % nkt;  // the key tile
-    tblk = 1 + d / (s.B * s.Hkv * nkt);
-    nsp = 1;
-  } else {
-    map_block(blockIdx.x, s.B * s.Hkv * nsplit, nsplit, unit, pair);
-  }
-  const int split = unit % nsp, bg = unit / nsp;
-  const int b = bg / s.Hkv;
-  const int T = clamp_T(seq_T, b, s.L);
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int hps = s.G / nsp;              // query heads of this workgroup, at every step
-  const int hg0 = (bg % s.Hkv) * s.G;     // the group's first query head
-  const int hh_begin = split * hps;
-  const size_t krow0 = (size_t)tblk * s.L;  // first K/V row of the block
   const float c2 = s.scale_log2;
   const FragOffsets fo = make_frag_offsets(lane);
+  const int kd0 = wave * 32 + l32 - 4 * hi;  // my_key - k0 - 4 hi: the mask's per-lane term
+  // this workgroup's queue (the dispatcher deals workgroups to the XCDs round robin)
+  const bool per_xcd = groups % 8 == 0 || n_units % 8 == 0;
+  const int queue = per_xcd ? (int)blockIdx.x % 8 : 0;
+  const int qunits = per_xcd ? n_units / 8 : n_units;  // (KV group, split) units per queue
+  if (tid == 0) sQueue = sched + 32 * queue;
 
 #pragma nounroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int kt = (pass == 0 || dwg) ? pair : nkt - 1 - pair;
-    if (pass == 1 && kt == pair) break;  // odd tile count (or a diagonal tile): no partner
+  for (int round = 0;; ++round) {
+    int unit, kt, tblk = 0, nsp = nsplit;
+    if (dwg) {
+      if (round > 0) break;
+      const int d = (int)blockIdx.x - n_pair_wgs;
+      unit = d % groups;
+      kt = (d / groups) % nkt;
+      tblk = 1 + d / (groups * nkt);
+      nsp = 1;
+    } else {
+      if (tid == 0) sUnit = (int)atomicAdd(sQueue, 1u);
+      __syncthreads();
+      const int uq = sUnit;
+      __syncthreads();  // read by all before the next round overwrites it
+      if (uq >= qunits * nkt) break;
+      kt = uq / qunits;  // key tiles in order: the heaviest first
+      const int x = uq % qunits;
+      if (groups % 8 == 0)  // KV groups queue, queue + 8, ... with all their splits
+        unit = (queue + 8 * (x / nsplit)) * nsplit + x % nsplit;
+      else
+        unit = queue * qunits + x;
+    }
+    const int split = unit % nsp, bg = unit / nsp;
+    const int b = bg / s.Hkv;
+    const int T = clamp_T(seq_T, b, s.L);
+    const int hps = s.G / nsp;              // query heads of this unit, at every step
+    const int hg0 = (bg % s.Hkv) * s.G;     // the group's first query head
+    const int hh_begin = split * hps;
+    const size_t krow0 = (size_t)tblk * s.L;  // first K/V row of the block
     const int k0 = kt * KBN;
     const int kw = k0 + wave * 32;
     const int my_key = kw + l32;
@@ -237,12 +264,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     // steps it without dividing.
     struct Pos {
       int j, hh, q0;
-      size_t row0;   // ((j * B + b) * Hq + hg0 + hh) * L + q0
-      size_t dsrow;  // dS block index of (step j, that head, query block q0 / 32, key block 0)
+      unsigned row0;   // ((j * B + b) * Hq + hg0 + hh) * L + q0
+      unsigned dsrow;  // dS block index of (step j, that head, query block q0 / 32, key block 0)
     };
     auto make_pos = [&](int j, int hh, int q0) -> Pos {
       const int sbh = (j * s.B + b) * s.Hq + hg0 + hh;
-      return Pos{j, hh, q0, (size_t)sbh * s.L + q0, ds_block_index(s, sbh, q0 / 32, 0)};
+      return Pos{j, hh, q0, (unsigned)((size_t)sbh * s.L + q0),
+                 (unsigned)ds_block_index(s, sbh, q0 / 32, 0)};
     };
     auto next_pos = [&](Pos p) -> Pos {
       if (p.q0 + KBM >= q_end)
@@ -255,8 +283,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
     };
     auto issue = [&](Pos p, bf16* dQ, bf16* dOt, float* dLD) {
       const size_t row0 = p.row0;
-      load_tile<KBM, 4>(q + row0 * BD, BD, dQ, wave, lane);
-      load_tile<KBM, 4>(dO + row0 * BD, BD, dOt, wave, lane);
+      load_tile_soff<KBM, 4>(q + row0 * BD, BD, dQ, wave, lane);
+      load_tile_soff<KBM, 4>(dO + row0 * BD, BD, dOt, wave, lane);
       if (wave < 2 && lane < KBM) {  // wave 0: lse * log2(e) of the 32 rows to dLD[0, 32); wave 1: D to dLD[32, 64)
         unsigned off = 4u * lane;
         asm volatile("" : "+v"(off));
@@ -291,12 +319,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
         }
         const bool full = !dwg && (kw + 31 <= q0) && (kw + 32 <= T);
         if (dwg) {  // key row t*Q_LEN + my_key serves query my_key only (q0 == kw), if < T
-          const int dkey = my_key >= T ? KBM : my_key - q0 - 4 * hi;
+          const int dkey = my_key >= T ? KBM : kd0 + (k0 - q0);
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (dkey != acc_row(i, 0)) acc[i] = 0.f;
         } else if (!full) {
-          const int dkey = my_key >= T ? KBM : my_key - q0 - 4 * hi;
+          const int dkey = my_key >= T ? KBM : kd0 + (k0 - q0);
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (dkey > acc_row(i, 0)) acc[i] = 0.f;
@@ -329,12 +357,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
         dsb[0] = to_bf16x8(acc, 0);
         dsb[1] = to_bf16x8(acc, 8);
         if (ds_out && !dwg) {  // hand dS to the dQ kernel (layout: ds_store_offset)
-          const size_t blk = p.dsrow + kw / 32;
-          void* dst = const_cast<void*>(uniform_ptr(ds_out + blk * 1024));
-          unsigned off0 = ds_store_offset(lane, 0), off1 = ds_store_offset(lane, 1);
-          asm volatile("" : "+v"(off0), "+v"(off1));
+          const size_t blk = (size_t)p.dsrow + kw / 32;
+          char* dst = reinterpret_cast<char*>(const_cast<void*>(uniform_ptr(ds_out + blk * 1024)));
+          // ds_store_offset(lane, 1) = 1024 + (ds_store_offset(lane, 0) ^ 128)
+          unsigned off0 = ds_store_offset(lane, 0);
+          asm volatile("" : "+v"(off0));
           store16_global_nt(dst, off0, dsb[0]);
-          store16_global_nt(dst, off1, dsb[1]);
+          store16_global_nt(dst + 1024, off0 ^ 128u, dsb[1]);
         }
         // dV then dK products, i = 0..15 (i < 8: dV, (u, c) = (i / 2, i % 2) from the dO
         // tile; then dK from the Q tile); operand fragments four products ahead in slots i % 4
@@ -417,21 +446,21 @@ hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, co
                                 const bf16* dout, const float* lse2, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
                                 int nsplit, bf16* ds_out, bool dense_diagonal, float* dq_suf,
-                                hipStream_t st) {
+                                unsigned* sched, hipStream_t st) {
   const int pairs = s.B * s.Hkv * nsplit * ((s.L / KBN + 1) / 2);
   LaunchTimer timer(dq_suf ? "bwd_dkdv_suffix_mfma" : "bwd_dkdv_mfma", st);
   if (dense_diagonal && s.step > 0) {
     const dim3 grid(pairs + s.B * s.Hkv * (s.L / KBN) * s.step);
     bwd_dkdv_mfma_kernel<true, false><<<grid, 256, 0, st>>>(q, k, v, dout, lse2, Dd, seq_T, dk, dv,
-                                                            part, nsplit, nullptr, nullptr, s);
+                                                            part, nsplit, nullptr, nullptr, sched, s);
     return hipGetLastError();
   }
   if (dq_suf && s.step > 0)
     bwd_dkdv_mfma_kernel<false, true><<<dim3(pairs), 256, 0, st>>>(
-        q, k, v, dout, lse2, Dd, seq_T, dk, dv, part, nsplit, ds_out, dq_suf, s);
+        q, k, v, dout, lse2, Dd, seq_T, dk, dv, part, nsplit, ds_out, dq_suf, sched, s);
   else
     bwd_dkdv_mfma_kernel<false, false><<<dim3(pairs), 256, 0, st>>>(
-        q, k, v, dout, lse2, Dd, seq_T, dk, dv, part, nsplit, ds_out, nullptr, s);
+        q, k, v, dout, lse2, Dd, seq_T, dk, dv, part, nsplit, ds_out, nullptr, sched, s);
   return hipGetLastError();
 }
 

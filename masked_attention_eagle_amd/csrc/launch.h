@@ -37,18 +37,20 @@ hipError_t launch_fwd_suffix(const Shape& s, const T* q, const T* k, const T* v,
 
 
 // Backward.
-// D = rowsum(dout * o); with lse2 set also lse2 = lse * log2(e).
+// D = rowsum(dout * o); with lse2 set also lse2 = lse * log2(e); with sched set also zeroes
+// the dK/dV kernel's queue counters (sched[32 i], i < 8).
 template <typename T>
 hipError_t launch_bwd_rowdot(const Shape& s, const T* o, const T* dout, float* Dd,
-                             const float* lse, float* lse2, hipStream_t st);
-// lse2 = lse * log2(e) (from launch_bwd_rowdot).
+                             const float* lse, float* lse2, unsigned* sched, hipStream_t st);
+// lse2 = lse * log2(e) (from launch_bwd_rowdot); sched: the 8 queue counters (sched[32 i]),
+// zero on entry (launch_bwd_rowdot sets them just before on the same stream).
 // With dq_suf set (and k > 0) each workgroup also takes the suffix key rows t*Q_LEN + i of
 // its key tile's rows i: their dK/dV, and the fp32 dQ term of every head written to dq_suf.
 hipError_t launch_bwd_dkdv_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,
                                 const bf16* dout, const float* lse2, const float* Dd,
                                 const int32_t* seq_T, bf16* dk, bf16* dv, float* part,
                                 int nsplit, bf16* ds_out, bool dense_diagonal, float* dq_suf,
-                                hipStream_t st);
+                                unsigned* sched, hipStream_t st);
 hipError_t launch_bwd_dkdv_reduce(const Shape& s, const float* part, int nsplit, bf16* dk,
                                   bf16* dv, hipStream_t st);
 hipError_t launch_bwd_dq_mfma(const Shape& s, const bf16* q, const bf16* k, const bf16* v,

@@ -106,6 +106,8 @@ def test_workspace_sizes():
     # in two.
     part = 2 * 2 * B * Hkv * L * d * 4
     dqacc = rows * d * 4
+    # the dK/dV kernel's 8 key-tile queue counters, one per 128-byte line (matrix-core path)
+    sched = 8 * 128
     # bf16 default: dS blocks of block 0 (n(n+1)/2 blocks of 32 x 32 per head, n = L / 32)
     # and, for step > 0, the fp32 dQ accumulator the suffix kernel finalises; every offset is
     # a multiple of 256, so no padding.  The forward's suffix path does not change it.
@@ -113,26 +115,26 @@ def test_workspace_sizes():
         n = L // 32
         return B * Hq * n * (n + 1) // 2 * 32 * 32 * 2
     sep, rec = A.TTT_FLAG_SEPARATE_SUFFIX, A.TTT_FLAG_RECOMPUTE_DQ
-    assert A.bwd_workspace_size(p) == rows * 8 + part + ds_bytes(B, Hq, L) + dqacc
+    assert A.bwd_workspace_size(p) == rows * 8 + sched + part + ds_bytes(B, Hq, L) + dqacc
     assert A.bwd_workspace_size(P(flags=sep)) == A.bwd_workspace_size(p)
-    assert A.bwd_workspace_size(P(step=0)) == rows * 8 + part + ds_bytes(B, Hq, L)
+    assert A.bwd_workspace_size(P(step=0)) == rows * 8 + sched + part + ds_bytes(B, Hq, L)
     # dense-diagonal backward (measurement variant): dQ recomputed over the causal and the
     # diagonal tiles in one kernel, written final: no dS blocks and no fp32 dQ accumulator
     dense = A.TTT_FLAG_DENSE_DIAGONAL
-    assert A.bwd_workspace_size(P(flags=dense)) == rows * 8 + part
-    assert A.bwd_workspace_size(P(flags=dense | rec)) == rows * 8 + part
+    assert A.bwd_workspace_size(P(flags=dense)) == rows * 8 + sched + part
+    assert A.bwd_workspace_size(P(flags=dense | rec)) == rows * 8 + sched + part
     assert A.bwd_workspace_size(P(flags=dense, step=0)) == A.bwd_workspace_size(P(step=0))
     # recomputing dQ kernel: no dS blocks
-    assert A.bwd_workspace_size(P(flags=rec)) == rows * 8 + part + dqacc
-    assert A.bwd_workspace_size(P(flags=rec | sep)) == rows * 8 + part + dqacc
-    assert A.bwd_workspace_size(P(flags=rec, step=0)) == rows * 8 + part
+    assert A.bwd_workspace_size(P(flags=rec)) == rows * 8 + sched + part + dqacc
+    assert A.bwd_workspace_size(P(flags=rec | sep)) == rows * 8 + sched + part + dqacc
+    assert A.bwd_workspace_size(P(flags=rec, step=0)) == rows * 8 + sched + part
     # 1 x 8 x 16 = 128 pair workgroups: heads split in four
     rows4 = 64 * L
-    assert A.bwd_workspace_size(P(B=1, Hq=64, flags=rec)) == rows4 * 8 + rows4 * d * 4 + 4 * 2 * 8 * L * d * 4
+    assert A.bwd_workspace_size(P(B=1, Hq=64, flags=rec)) == rows4 * 8 + sched + rows4 * d * 4 + 4 * 2 * 8 * L * d * 4
     # 8 x 8 x 8 = 512 already: no split, no partials
     rows3 = 8 * 32 * 2048
-    assert A.bwd_workspace_size(P(B=8, L=2048, flags=rec)) == rows3 * 8 + rows3 * d * 4
-    assert A.bwd_workspace_size(P(B=8, L=2048)) == rows3 * 8 + ds_bytes(8, 32, 2048) + rows3 * d * 4
+    assert A.bwd_workspace_size(P(B=8, L=2048, flags=rec)) == rows3 * 8 + sched + rows3 * d * 4
+    assert A.bwd_workspace_size(P(B=8, L=2048)) == rows3 * 8 + sched + ds_bytes(8, 32, 2048) + rows3 * d * 4
     # fp32 (vector-ALU path): flags ignored; D + dQ accumulator
     rowsf = 2 * 32 * 4000
     for f in (0, sep, rec):
@@ -231,7 +233,8 @@ def test_oracle_is_not_imported_by_the_product():
 
 def test_sweep_workspace_and_errors():
     """The sweep's backward workspace: D and lse * log2(e) rows and the dS blocks of every step
-    (one dK/dV launch covers all steps), the split dK/dV partials and the fp32 dQ accumulators
+    (one dK/dV launch covers all steps), the dK/dV kernel's queue counters, the split dK/dV
+    partials and the fp32 dQ accumulators
     of steps 1..K-1 (one suffix launch covers all steps); fp32 data is not supported; errors
     come before any launch."""
     lib = A.load()
@@ -242,12 +245,13 @@ def test_sweep_workspace_and_errors():
     ds_step = B * Hq * n * (n + 1) // 2 * 32 * 32 * 2
     # 2 x 8 x 16 = 256 pair workgroups: the 4 query heads of a KV group split in two
     part = 2 * 2 * B * Hkv * L * d * 4
-    whole = K * rows * 8 + part + K * ds_step + (K - 1) * rows * d * 4
+    sched = 8 * 128  # the dK/dV kernel's key-tile queue counters
+    whole = K * rows * 8 + sched + part + K * ds_step + (K - 1) * rows * d * 4
     assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(p)) == whole
     rec = P(step=K - 1, flags=A.TTT_FLAG_RECOMPUTE_DQ)
     assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(rec)) == whole - K * ds_step
     one = P(step=0)  # a single step: no dQ accumulator
-    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(one)) == rows * 8 + part + ds_step
+    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(one)) == rows * 8 + sched + part + ds_step
     assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(p)) == 0  # fused forward
     sep = P(step=K - 1, flags=A.TTT_FLAG_SEPARATE_SUFFIX)
     assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(sep)) == A.fwd_workspace_size(sep)
