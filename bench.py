@@ -459,8 +459,10 @@ def measure(args, config, peaks=None):
         mfma = {n: s for n, s in kstats.items() if n in alg}
         dom = max(mfma, key=lambda n: mfma[n]["total_ms_per_step"])
         achieved = nsteps * alg[dom] / (mfma[dom]["total_ms_per_step"] / 1e3) / 1e12
-        # the counters were taken on the per-step calls' launches
-        traffic = measured_traffic(config, dom) if not args.sweep else None
+        # the counters were taken on the default paths' launches (per-step calls, stored dS,
+        # fused suffix): other paths run the kernels differently (no dS stores, for one)
+        default_paths = not args.sweep and args.dq_mode == "stored" and args.suffix == "fused"
+        traffic = measured_traffic(config, dom) if default_paths else None
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
