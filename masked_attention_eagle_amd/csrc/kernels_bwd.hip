@@ -192,6 +192,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_mfma_kernel(
   __shared__ unsigned* sQueue;  // this workgroup's queue counter (kept out of the registers)
   const int nkt = s.L / KBN;
   const int groups = s.B * s.Hkv, n_units = groups * nsplit;
+  // the queue's workgroups: one per pair of key tiles of a unit (two units each on average)
   const int n_pair_wgs = n_units * ((nkt + 1) / 2);
   const bool dwg = DIAG && (int)blockIdx.x >= n_pair_wgs;  // a diagonal tile of a block t >= 1
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
