@@ -72,6 +72,16 @@ def measured_traffic(config: int, name: str):
     return int(entry["bytes_per_launch"])
 
 
+def run_traffic(config: int, name: str, sweep: bool, dq_mode: str, suffix: str):
+    """measured_traffic for this run's dominant kernel, or None when the run takes other paths
+    than the counters were taken on (per-step calls, stored dS, fused suffix): the whole-TTT
+    dK/dV launch covers every step, and the other dQ and suffix paths run the kernels
+    differently (no dS stores, for one)."""
+    if sweep or dq_mode != "stored" or suffix != "fused":
+        return None
+    return measured_traffic(config, name)
+
+
 def causal_pairs(L: int, T: int) -> int:
     """|M_causal| for one (batch, head): T(T+1)/2 over rows i < T plus T keys for each of the
     L - T padded rows."""
@@ -459,10 +469,7 @@ def measure(args, config, peaks=None):
         mfma = {n: s for n, s in kstats.items() if n in alg}
         dom = max(mfma, key=lambda n: mfma[n]["total_ms_per_step"])
         achieved = nsteps * alg[dom] / (mfma[dom]["total_ms_per_step"] / 1e3) / 1e12
-        # the counters were taken on the default paths' launches (per-step calls, stored dS,
-        # fused suffix): other paths run the kernels differently (no dS stores, for one)
-        default_paths = not args.sweep and args.dq_mode == "stored" and args.suffix == "fused"
-        traffic = measured_traffic(config, dom) if default_paths else None
+        traffic = run_traffic(config, dom, args.sweep, args.dq_mode, args.suffix)
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}

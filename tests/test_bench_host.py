@@ -47,6 +47,17 @@ def test_traffic_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch):
     assert bench.measured_traffic(2, name) is None          # code changed since the counters
 
 
+def test_traffic_only_for_the_profiled_paths(monkeypatch):
+    """The counters were taken on the per-step, stored-dS, fused-suffix launches; other paths
+    run the kernels differently, so they get no traffic figure."""
+    monkeypatch.setattr(bench, "measured_traffic", lambda config, name: 7)
+    assert bench.run_traffic(2, "bwd_dkdv_mfma", False, "stored", "fused") == 7
+    assert bench.run_traffic(2, "bwd_dkdv_mfma", True, "stored", "fused") is None
+    assert bench.run_traffic(2, "bwd_dkdv_mfma", False, "recompute", "fused") is None
+    assert bench.run_traffic(2, "bwd_dkdv_mfma", False, "fused-suffix", "fused") is None
+    assert bench.run_traffic(2, "bwd_dkdv_mfma", False, "stored", "dense") is None
+
+
 def test_digest_ignores_comments(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("int f() { return 1; }  // one\n/* block */\n")
