@@ -172,9 +172,9 @@ Shape make_shape(const ttt_attn_params* p) {
 
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Number of workgroups that share the query heads of one KV group in the dK/dV kernel (each
-// workgroup owns a pair of 128-key tiles): doubled while the grid is below two workgroups per
-// CU and the group still splits evenly.
+// Number of shares the query heads of one KV group are split into in the dK/dV kernel (its
+// queue holds one unit per share and 128-key tile, and its grid one workgroup per two units):
+// doubled while the grid is below two workgroups per CU and the group still splits evenly.
 int dkdv_nsplit(const Shape& s) {
   const int64_t base = (int64_t)s.B * s.Hkv * ((s.L / 128 + 1) / 2);
   int n = 1;

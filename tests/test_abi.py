@@ -101,9 +101,9 @@ def test_workspace_sizes():
     assert A.fwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, step=0)) == 0
     assert A.fwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, L=4000)) == 2 * 32 * 4000 * (d * 4 + 4)
     # D and lse * log2(e) rows (fp32 each) + fp32 dQ accumulator for step > 0 + fp32 dK/dV
-    # partial planes: each workgroup of the dK/dV kernel owns a pair of 128-key tiles, so
-    # 2 x 8 x 16 = 256 workgroups double to 512 by splitting each KV group's 4 query heads
-    # in two.
+    # partial planes: the dK/dV kernel runs one workgroup per two (128-key tile, head share)
+    # units, so 2 x 8 x 16 = 256 workgroups double to 512 by splitting each KV group's 4 query
+    # heads in two.
     part = 2 * 2 * B * Hkv * L * d * 4
     dqacc = rows * d * 4
     # the dK/dV kernel's 8 key-tile queue counters, one per 128-byte line (matrix-core path)
