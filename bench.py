@@ -119,8 +119,9 @@ def parse():
                     help="measure the in-place masked softmax-loss gradient on the draft LM head "
                          "of one TTT step (N = 8192 tokens, V = 32000, bf16) instead")
     ap.add_argument("--no-also", action="store_true",
-                    help="with the default workload, skip the sub-record of the other headline "
-                         "workload (the Llama-3.3-70B-shaped layer)")
+                    help="with the default workload, skip the sub-records of the other workloads "
+                         "(the Llama-3.3-70B-shaped layer, the padding-heavy batch and the "
+                         "long-TTT Qwen3-shaped layer)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured matrix-core and stream-copy peaks")
     ap.add_argument("--cold-steps", type=int, default=2,
@@ -213,13 +214,16 @@ def main():
     peaks = None if args.no_peaks else measure_peaks()
     out = measure(args, args.config, peaks)
     if args.config == 2 and not args.no_also:
-        # the metric's other headline workload, timed the same way in the same run
-        torch.cuda.empty_cache()
-        sub = measure(args, 4, peaks)
-        out["also"] = {sub["config"]["workload"]: {
-            k: sub[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s",
-                                "valid_tokens_per_s", "step_ms",
-                                "pct_roofline", "roofline", "config", "unmasked_flop_per_step")}}
+        # the metric's other headline workload (4), then the padding-heavy (3) and long-TTT (5)
+        # workloads, timed the same way in the same run
+        out["also"] = {}
+        for cfg in (4, 3, 5):
+            torch.cuda.empty_cache()
+            sub = measure(args, cfg, peaks)
+            out["also"][sub["config"]["workload"]] = {
+                k: sub[k] for k in ("value", "unit", "ms_per_step", "tokens_per_s",
+                                    "valid_tokens_per_s", "step_ms", "pct_roofline", "roofline",
+                                    "config", "unmasked_flop_per_step", "kernels") if k in sub}
     if peaks is not None:
         out["peaks_measured"] = peaks
     if not args.no_cpu_baseline:
