@@ -77,6 +77,10 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m masked_attention_eagle_amd.build`")
+    # torch's ROCm wheel carries its own HIP runtime.  Loaded first, that runtime is the one the
+    # library's libamdhip64 dependency binds to; loaded later, the process would hold two HIP
+    # runtimes, and the streams and memory torch hands over would be foreign to the library's.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(Params)
     vp, sz = ctypes.c_void_p, ctypes.c_size_t

@@ -3,12 +3,15 @@ workspace, and rejects bad arguments before touching the GPU."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
 from masked_attention_eagle_amd import ttt_attn as A
 
-INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
 HEADER = os.path.join(INCLUDE, "ttt_attn.h")
 
 
@@ -220,6 +223,22 @@ def test_timing_api_without_launches():
     A.timing_reset()
     assert A.timing_read() == {}
     A.timing_enable(was)
+
+
+def test_library_shares_torchs_hip_runtime():
+    """load() called before anything imports torch still leaves one HIP runtime in the process:
+    torch's wheel carries its own libamdhip64, and the library must bind to that copy, or the
+    streams and memory torch hands over are foreign to the runtime that launches the kernels."""
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from masked_attention_eagle_amd import ttt_attn\n"
+            "assert 'torch' not in sys.modules\n"
+            "ttt_attn.load()\n"
+            "import torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps), sorted(maps))\n" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.startswith("1 "), out.stdout
 
 
 def test_oracle_is_not_imported_by_the_product():
