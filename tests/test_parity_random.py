@@ -1,0 +1,120 @@
+"""Seeded random bf16 cases through the C ABI against the oracle.
+
+The shapes are drawn from a fixed generator: batch 1..3, KV-group counts 1, 2, 3, 4, 5 and 8
+(the dK/dV kernel's work queue runs one shared queue, per-XCD queues by KV group, or per-XCD
+queues by unit depending on whether these counts divide by 8), group sizes 1..8, Q_LEN on and
+off the matrix-core tiling (multiples of 128 and 192), TTT steps 0..3, ragged and out-of-range
+lengths T, and every path flag; every third case is a whole-TTT sweep of 1..5 steps.  The
+tolerances are those of the other bf16 parity tests.
+"""
+import numpy as np
+import pytest
+
+from masked_attention_eagle_amd import inputs
+from oracle import ttt_oracle as O
+from tests.helpers import TOL_GRAD, TOL_LSE, TOL_O, check, gpu_fwd_bwd, to_dev, to_np
+
+N_CASES = 48
+D = 128
+
+
+def _draw_cases(n, seed=20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        while Hkv * G > 16 and G > 1:
+            G //= 2
+        if c % 3 == 2:
+            L = int(rng.choice([128, 256, 384]))
+            K = int(rng.integers(1, 6))
+            T = tuple(int(t) for t in rng.integers(0, L + 6, size=B))
+            dq_mode = str(rng.choice(["stored", "recompute"]))
+            cases.append(dict(kind="sweep", B=B, Hq=Hkv * G, Hkv=Hkv, L=L, K=K, T=T,
+                              dq_mode=dq_mode))
+            continue
+        L = int(rng.choice([128, 192, 256, 384, 512, 1024]))
+        step = int(rng.integers(0, 4))
+        T = tuple(int(t) for t in rng.integers(0, L + 6, size=B))
+        dq_mode = str(rng.choice(["stored", "recompute", "fused-suffix"]))
+        suffix = "fused" if dq_mode == "fused-suffix" else str(rng.choice(["fused", "separate", "dense"]))
+        cases.append(dict(kind="step", B=B, Hq=Hkv * G, Hkv=Hkv, L=L, step=step, T=T,
+                          dq_mode=dq_mode, suffix=suffix))
+    return cases
+
+
+CASES = _draw_cases(N_CASES)
+
+
+def _norm_err(got, ref):
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def _sweep(gpu_lib, seed, B, Hq, Hkv, L, K, T, dq_mode, label):
+    import torch
+    Tn = np.asarray(T, dtype=np.int32)
+    q = np.stack([inputs.round_to_bf16(inputs._normal([seed, s, 20], (B, Hq, L, D), "f32"))
+                  for s in range(K)])
+    kc = inputs._normal([seed, 99, 21], (B, Hkv, K * L, D), "bf16")
+    vc = inputs._normal([seed, 99, 22], (B, Hkv, K * L, D), "bf16")
+    do = np.stack([inputs._normal([seed, s, 23], (B, Hq, L, D), "bf16") for s in range(K)])
+    bf = torch.bfloat16
+    qd, kd, vd, dod = to_dev(q, bf), to_dev(kc, bf), to_dev(vc, bf), to_dev(do, bf)
+    Td = torch.as_tensor(Tn, device="cuda")
+    scale = 1.0 / np.sqrt(D)
+    o, lse = gpu_lib.ttt_attn_fwd_sweep(qd, kd, vd, Td, scale)
+    dq, dk, dv = gpu_lib.ttt_attn_bwd_sweep(qd, kd, vd, Td, o, lse, dod, scale, dq_mode=dq_mode)
+    torch.cuda.synchronize()
+    dk_ref, dv_ref = np.zeros(kc.shape), np.zeros(vc.shape)
+    for s in range(K):
+        m = (s + 1) * L
+        ro, rlse = O.forward(q[s], kc[:, :, :m], vc[:, :, :m], Tn, scale)
+        rdq, rdk, rdv = O.backward(q[s], kc[:, :, :m], vc[:, :, :m], Tn, scale, do[s], ro)
+        dk_ref[:, :, :m] += rdk
+        dv_ref[:, :, :m] += rdv
+        assert float(np.abs(to_np(o[s]) - ro).max()) <= TOL_O, label
+        got_lse, fin = to_np(lse[s]), np.isfinite(rlse)
+        assert np.array_equal(np.isneginf(got_lse), np.isneginf(rlse)), label
+        if fin.any():
+            assert float(np.abs(got_lse[fin] - rlse[fin]).max()) <= TOL_LSE, label
+        if np.abs(rdq).max() > 0:
+            assert _norm_err(to_np(dq[s]), rdq) <= TOL_GRAD, label
+    if np.abs(dk_ref).max() > 0:
+        assert _norm_err(to_np(dk), dk_ref) <= TOL_GRAD, label
+        assert _norm_err(to_np(dv), dv_ref) <= TOL_GRAD, label
+    else:
+        assert not bool(dk.any()) and not bool(dv.any()), label
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("idx", range(N_CASES))
+def test_random_case_against_oracle(gpu_lib, idx):
+    c = CASES[idx]
+    label = f"random case {idx}: {c}"
+    print(label, flush=True)
+    if c["kind"] == "sweep":
+        _sweep(gpu_lib, 500 + idx, c["B"], c["Hq"], c["Hkv"], c["L"], c["K"], c["T"],
+               c["dq_mode"], label)
+        return
+    q, k, v, do, Tn = inputs.make_case(1000 + idx, c["B"], c["Hq"], c["Hkv"], D, c["L"],
+                                       c["step"], c["T"], "bf16")
+    scale = 1.0 / np.sqrt(D)
+    got = gpu_fwd_bwd(gpu_lib, q, k, v, do, Tn, scale, "bf16", dq_mode=c["dq_mode"],
+                      suffix=c["suffix"])
+    ro, rlse = O.forward(q, k, v, Tn, scale)
+    rdq, rdk, rdv = O.backward(q, k, v, Tn, scale, do, ro)
+    check(got, dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv), "bf16", label)
+
+
+def test_random_cases_cover_every_queue_mode_and_path():
+    """The drawn cases reach KV-group counts (batch x KV heads) that divide by 8, odd ones and
+    other even ones, the sweep, and each path flag."""
+    counts = {"div8" if g % 8 == 0 else "odd" if g % 2 else "even"
+              for g in (c["B"] * c["Hkv"] for c in CASES)}
+    assert counts == {"div8", "odd", "even"}, counts
+    assert any(c["kind"] == "sweep" for c in CASES)
+    assert {c.get("dq_mode") for c in CASES} >= {"stored", "recompute", "fused-suffix"}
+    assert {c.get("suffix") for c in CASES} >= {"fused", "separate", "dense"}
+    assert {c["L"] % 128 for c in CASES} >= {0, 64}
