@@ -22,7 +22,9 @@ namespace ttt {
 // straddle the diagonal or the T edge evaluate the mask ("partial"); the rest are "full".
 // On partial tiles of waves whose rows see fewer than 64 keys, P is split into bf16 hi + lo
 // parts so that rows with few keys (where one rounding of P would show in O) keep fp32-level
-// accuracy.
+// accuracy.  Elsewhere P is rounded to bf16 once, and O is normalised by the sum of those
+// rounded values (lse by the fp32 sum of the unrounded ones), so that O stays a convex
+// combination of V rows whose error is small where a few keys carry most of the weight.
 // With FINAL and k > 0 the kernel also merges the suffix keys (one per block 1..k for rows
 // i < T; their K and V rows pass through the same LDS stages before the causal tiles) and
 // writes the final o and lse; without FINAL it writes the fp32 causal state for the
@@ -95,7 +97,12 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
   f32x16 acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
-  float m = kNegInf, l = 0.f;  // running max of the raw logits q.k, and the softmax sum
+  // running max of the raw logits q.k; the softmax sum of the unrounded P (for lse); and the
+  // sum of the P that enter the P V products, bf16-rounded on the full and wide tiles, which
+  // normalises o (o is then a convex combination of V rows: the rounding errors of P cancel
+  // out of the rows dominated by a few keys, where they would otherwise move o by up to
+  // 2^-9 |o|)
+  float m = kNegInf, l = 0.f, lt = 0.f;
   const float c2 = s.scale_log2;
   const FragOffsets fo = make_frag_offsets(lane);
 
@@ -198,6 +205,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
           const float m_new = grow ? rmax : m;
           const float alpha = grow ? exp2_fast((m - m_new) * c2) : 1.f;
           l *= alpha;
+          lt *= alpha;
 #pragma unroll
           for (int u = 0; u < 4; ++u) acc[u] *= alpha;
           m = m_new;
@@ -228,6 +236,22 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
           }
         }
       }
+      // the sum of the P the products take: bf16 pairs through packed dot products with 1
+      // (exact products, fp32 sums); hi + lo (the partial tiles) carries P to 2^-17
+      float rsum = lsum;
+      if (full || wide) {
+        const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
+        float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+          for (int e2 = 0; e2 < 4; e2 += 2) {
+            r0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x8_pair(pf[c], e2), one2, r0, false);
+            r1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x8_pair(pf[c], e2 + 1), one2, r1, false);
+          }
+        }
+        rsum = r0 + r1;
+      }
       if (full || wide) {
         // four V fragments in flight: slot c is refilled with column block u + 1 right
         // after product (u, c) is issued, four products before it is needed
@@ -255,6 +279,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
         }
       }
       l += half_sum(lsum);
+      lt += half_sum(rsum);
     }
     wait_vmem();
     __syncthreads();
@@ -305,12 +330,14 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
           const float m_new = grow ? dot : m;
           const float alpha = grow ? exp2_fast((m - m_new) * c2) : 1.f;  // 0 while m = -inf
           l *= alpha;
+          lt *= alpha;
 #pragma unroll
           for (int u = 0; u < 4; ++u) acc[u] *= alpha;
           m = m_new;
         }
         p = exp2_fast((dot - m) * c2);
         l += p;
+        lt += p;
       }
       wait_vmem();
       __syncthreads();
@@ -340,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void fwd_causal_mfma_kernel(
     if (j + 1 < ntiles) body(j + 1, sK1, sV1, sK0, sV0);
   }
 
-  const float inv_l = l > 0.f ? 1.f / l : 0.f;
+  const float inv_l = lt > 0.f ? 1.f / lt : 0.f;
   const float lse = l > 0.f ? (m * c2 + __log2f(l)) * kLn2 : kNegInf;
   const size_t row = (size_t)bh * s.L + my_q;
   if (hi == 0) lse_out[row] = lse;

@@ -108,6 +108,18 @@ def test_random_case_against_oracle(gpu_lib, idx):
     check(got, dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv), "bf16", label)
 
 
+@pytest.mark.gpu
+def test_sweep_row_concentrated_on_few_keys(gpu_lib):
+    """Padded row 153 of sequence 1 (T = 97) at step 1 sees 97 keys but puts most of its weight
+    on a few, so |o| reaches 2.29, where a bf16 step is 2^-6.  Normalising o by the fp32 sum of
+    the unrounded P left it 0.0036 off in fp32 (the bf16 rounding of P, relative 2^-9, does not
+    cancel in such a row) and the output rounding then landed one step away: 0.0114 > 1e-2.
+    Normalised by the sum of the P the products take, o is a convex combination of the V rows
+    and the error is 0.0049."""
+    _sweep(gpu_lib, 119, 2, 2, 2, 256, 3, (236, 97), "stored",
+           "sweep B=2 Hq=2 Hkv=2 L=256 K=3 T=(236, 97)")
+
+
 def test_random_cases_cover_every_queue_mode_and_path():
     """The drawn cases reach KV-group counts (batch x KV heads) that divide by 8, odd ones and
     other even ones, the sweep, and each path flag."""
