@@ -5,7 +5,8 @@ The shapes are drawn from a fixed generator: batch 1..3, KV-group counts 1, 2, 3
 queues by unit depending on whether these counts divide by 8), group sizes 1..8, Q_LEN on and
 off the matrix-core tiling (multiples of 128 and 192), TTT steps 0..3, ragged and out-of-range
 lengths T, and every path flag; every third case is a whole-TTT sweep of 1..5 steps.  The
-tolerances are those of the other bf16 parity tests.
+tolerances are those of the other bf16 parity tests.  A second draw covers the vector-ALU
+kernels (fp32, bf16 at head_dim 64 or off the matrix-core tiling).
 """
 import numpy as np
 import pytest
@@ -108,6 +109,47 @@ def test_random_case_against_oracle(gpu_lib, idx):
     check(got, dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv), "bf16", label)
 
 
+def _draw_valu_cases(n, seed=20261203):
+    """Shapes of the vector-ALU kernels: fp32 at head_dim 64 or 128 and any Q_LEN, bf16 at head_dim
+    64 or at Q_LEN off the matrix-core tiling."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B = int(rng.integers(1, 3))
+        Hkv = int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 2, 4]))
+        dtype = str(rng.choice(["f32", "bf16"]))
+        d = int(rng.choice([64, 128]))
+        L = int(rng.choice([64, 192, 320])) if (dtype == "bf16" and d == 128) else \
+            int(rng.choice([16, 37, 64, 100, 192, 256]))
+        step = int(rng.integers(0, 4))
+        T = tuple(int(t) for t in rng.integers(0, L + 4, size=B))
+        cases.append(dict(B=B, Hq=Hkv * G, Hkv=Hkv, d=d, L=L, step=step, T=T, dtype=dtype,
+                          suffix=str(rng.choice(["fused", "separate"])),
+                          dq_mode=str(rng.choice(["stored", "recompute"]))))
+    return cases
+
+
+VALU_CASES = _draw_valu_cases(16)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("idx", range(len(VALU_CASES)))
+def test_random_valu_case_against_oracle(gpu_lib, idx):
+    """fp32 to 1e-5 of max|ref| per output, bf16 to the bf16 bounds."""
+    c = VALU_CASES[idx]
+    label = f"random vector-ALU case {idx}: {c}"
+    print(label, flush=True)
+    q, k, v, do, Tn = inputs.make_case(3000 + idx, c["B"], c["Hq"], c["Hkv"], c["d"], c["L"],
+                                       c["step"], c["T"], c["dtype"])
+    scale = 1.0 / np.sqrt(c["d"])
+    got = gpu_fwd_bwd(gpu_lib, q, k, v, do, Tn, scale, c["dtype"], dq_mode=c["dq_mode"],
+                      suffix=c["suffix"])
+    ro, rlse = O.forward(q, k, v, Tn, scale)
+    rdq, rdk, rdv = O.backward(q, k, v, Tn, scale, do, ro)
+    check(got, dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv), c["dtype"], label, f32_relative=True)
+
+
 @pytest.mark.gpu
 def test_sweep_row_concentrated_on_few_keys(gpu_lib):
     """Padded row 153 of sequence 1 (T = 97) at step 1 sees 97 keys but puts most of its weight
@@ -130,3 +172,4 @@ def test_random_cases_cover_every_queue_mode_and_path():
     assert {c.get("dq_mode") for c in CASES} >= {"stored", "recompute", "fused-suffix"}
     assert {c.get("suffix") for c in CASES} >= {"fused", "separate", "dense"}
     assert {c["L"] % 128 for c in CASES} >= {0, 64}
+    assert {(c["dtype"], c["d"]) for c in VALU_CASES} == {("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)}
