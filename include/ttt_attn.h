@@ -100,8 +100,12 @@ enum ttt_attn_status {
  *   dtype F32 : head_dim in {64, 128}, any q_len >= 1 (vector-ALU kernels).
  *   dtype BF16: head_dim in {64, 128}, any q_len >= 1.  head_dim 128 with q_len a multiple of
  *               128 runs on the matrix-core kernels (the fast path, and the only one the
- *               whole-TTT calls and the flags below apply to); other bf16 shapes run on the
- *               vector-ALU kernels (bf16 storage, fp32 arithmetic).
+ *               whole-TTT calls take).  head_dim 64 with q_len a multiple of 128 runs on the
+ *               same kernels in ttt_attn_fwd and ttt_attn_bwd, through head_dim-128 copies of
+ *               the rows whose upper half is zero (exact: the zero half adds nothing to any
+ *               sum), which the workspace holds; the flags below apply to both.  Other bf16
+ *               shapes, and head_dim 64 in ttt_attn_bwd_noalloc, run on the vector-ALU kernels
+ *               (bf16 storage, fp32 arithmetic).
  * scale multiplies q.k before masking (1/sqrt(head_dim) in the usual setting); it must be
  * finite and positive (the streaming softmax tracks the row maximum of the raw q.k).
  */
@@ -125,7 +129,8 @@ size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p);
  * The default bf16 backward workspace holds the dS of block 0: B * Hq * n(n+1)/2 blocks of
  * 2 KB, n = Q_LEN / 32 (1.08 GB at B 2, Hq 32, Q_LEN 4096); TTT_FLAG_RECOMPUTE_DQ avoids it.
  * It also holds the dK/dV kernel's work-queue counters, another reason why calls in flight
- * at the same time need distinct workspaces.
+ * at the same time need distinct workspaces.  At bf16 head_dim 64 on the matrix-core kernels
+ * it starts with head_dim-128 copies of q, k, v, o (backward: also dout, dq, dk, dv).
  */
 
 /*
@@ -213,7 +218,9 @@ int ttt_attn_bwd_noalloc(const ttt_attn_params* p, const void* q, const void* k,
 const char* ttt_attn_status_string(int status);
 
 /*
- * ABI version (major * 100 + minor).  1.03 added ttt_attn_bwd_noalloc (with TTT_E_SCRATCH),
+ * ABI version (major * 100 + minor).  1.04 runs bf16 head_dim 64 with q_len a multiple of 128
+ * on the matrix-core kernels (larger workspaces for those shapes); 1.03 added
+ * ttt_attn_bwd_noalloc (with TTT_E_SCRATCH),
  * TTT_FLAG_FUSED_SUFFIX_BWD and ttt_attn_timing_flush, and made the timing calls thread-safe;
  * 1.02 changed the whole-TTT backward's workspace size.
  */

@@ -90,6 +90,20 @@ bool mfma_path(const ttt_attn_params* p) {
   return p->dtype == TTT_DTYPE_BF16 && p->head_dim == 128 && p->q_len % 128 == 0;
 }
 
+// bf16 at head_dim 64 with q_len a multiple of 128 (per-step calls with a workspace): the same
+// kernels through head_dim-128 copies of the rows whose upper half is zero.  The zero half adds
+// exact zeros to every dot product, so the logits, P, lse and the lower halves of o and of
+// every gradient are those of the head_dim-64 problem, at twice its matrix-core work; the
+// copies sit in the caller's workspace ahead of the kernels' own regions.
+bool pad64_path(const ttt_attn_params* p) {
+  return p->dtype == TTT_DTYPE_BF16 && p->head_dim == 64 && p->q_len % 128 == 0;
+}
+ttt_attn_params widened(const ttt_attn_params* p) {
+  ttt_attn_params w = *p;
+  w.head_dim = 128;
+  return w;
+}
+
 int validate(const ttt_attn_params* p) {
   if (!p) return TTT_E_NULL;
   if (p->batch <= 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->q_len <= 0 ||
@@ -105,7 +119,7 @@ int validate(const ttt_attn_params* p) {
   if (rows_q * p->head_dim > (1ll << 40) || rows_kv * p->head_dim > (1ll << 40)) return TTT_E_SHAPE;
   if (p->dtype != TTT_DTYPE_F32 && p->dtype != TTT_DTYPE_BF16) return TTT_E_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return TTT_E_UNSUPPORTED;
-  if (mfma_path(p)) {
+  if (mfma_path(p) || pad64_path(p)) {
     if ((int64_t)p->batch * p->heads_kv * p->q_len * 16 >= (1ll << 32)) return TTT_E_SHAPE;
   } else {
     // one 64-lane workgroup per query row (per key row in the dK/dV kernel)
@@ -241,6 +255,31 @@ BwdLayout bwd_layout(const Shape& s, bool mfma, bool with_ds, bool dense = false
   return w;
 }
 
+// The head_dim-128 copies of a head_dim-64 call (pad64_path), in bytes from the workspace start:
+// q, k, v and (forward output, backward input) o; for the backward also dO, dq, dk, dv; the
+// kernels' own workspace follows at `inner`.
+struct PadLayout {
+  size_t q = 0, k = 0, v = 0, o = 0, dout = 0, dq = 0, dk = 0, dv = 0, inner = 0;
+};
+PadLayout pad_layout(const Shape& s, bool bwd) {
+  PadLayout w;
+  const size_t rq = round_up((size_t)s.B * s.Hq * s.L * 128 * 2);
+  const size_t rkv = round_up((size_t)s.B * s.Hkv * s.KV * 128 * 2);
+  size_t off = 0;
+  w.q = off; off += rq;
+  w.k = off; off += rkv;
+  w.v = off; off += rkv;
+  w.o = off; off += rq;
+  if (bwd) {
+    w.dout = off; off += rq;
+    w.dq = off; off += rq;
+    w.dk = off; off += rkv;
+    w.dv = off; off += rkv;
+  }
+  w.inner = off;
+  return w;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_E_HIP; }
 
 // ------------------------------------------------------------------ no-allocation scratch
@@ -274,7 +313,7 @@ using namespace ttt;
 
 extern "C" {
 
-int ttt_attn_version(void) { return 103; }
+int ttt_attn_version(void) { return 104; }
 
 const char* ttt_attn_status_string(int status) {
   switch (status) {
@@ -292,11 +331,20 @@ const char* ttt_attn_status_string(int status) {
 
 size_t ttt_attn_fwd_workspace_size(const ttt_attn_params* p) {
   if (validate(p) != TTT_OK) return 0;
+  if (pad64_path(p)) {
+    const ttt_attn_params w = widened(p);
+    return pad_layout(make_shape(p), false).inner + fwd_layout(make_shape(&w), fused_fwd(&w)).total;
+  }
   return fwd_layout(make_shape(p), fused_fwd(p)).total;
 }
 
 size_t ttt_attn_bwd_workspace_size(const ttt_attn_params* p) {
   if (validate(p) != TTT_OK) return 0;
+  if (pad64_path(p)) {
+    const ttt_attn_params w = widened(p);
+    return pad_layout(make_shape(p), true).inner +
+           bwd_layout(make_shape(&w), true, stored_ds(&w), dense_bwd(&w)).total;
+  }
   return bwd_layout(make_shape(p), mfma_path(p), stored_ds(p), dense_bwd(p)).total;
 }
 
@@ -464,13 +512,28 @@ int ttt_attn_fwd(const ttt_attn_params* p, const void* q, const void* k, const v
   if (rc != TTT_OK) return rc;
   if (!q || !k || !v || !seq_T || !o || !lse) return TTT_E_NULL;
   const Shape s = make_shape(p);
-  const FwdLayout w = fwd_layout(s, fused_fwd(p));
-  if (w.total > 0 && !workspace) return TTT_E_NULL;
-  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
+  const size_t need = ttt_attn_fwd_workspace_size(p);
+  if (need > 0 && !workspace) return TTT_E_NULL;
+  if (workspace_bytes < need) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(workspace))
     return TTT_E_ALIGN;
-  return run_fwd(p, s, q, k, v, seq_T, o, lse, (char*)workspace, (hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  if (pad64_path(p)) {
+    const ttt_attn_params p2 = widened(p);
+    const PadLayout w = pad_layout(s, false);
+    char* ws = (char*)workspace;
+    const size_t rq = (size_t)s.B * s.Hq * s.L, rkv = (size_t)s.B * s.Hkv * s.KV;
+    if (launch_pad64(q, ws + w.q, rq, st) != hipSuccess ||
+        launch_pad64(k, ws + w.k, rkv, st) != hipSuccess ||
+        launch_pad64(v, ws + w.v, rkv, st) != hipSuccess)
+      return TTT_E_HIP;
+    rc = run_fwd(&p2, make_shape(&p2), ws + w.q, ws + w.k, ws + w.v, seq_T, ws + w.o, lse,
+                 ws + w.inner, st);
+    if (rc != TTT_OK) return rc;
+    return hip_status(launch_unpad64(ws + w.o, o, rq, st));
+  }
+  return run_fwd(p, s, q, k, v, seq_T, o, lse, (char*)workspace, st);
 }
 
 int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const void* v,
@@ -481,15 +544,35 @@ int ttt_attn_bwd(const ttt_attn_params* p, const void* q, const void* k, const v
   if (rc != TTT_OK) return rc;
   if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
   const Shape s = make_shape(p);
-  const BwdLayout w = bwd_layout(s, mfma_path(p), stored_ds(p), dense_bwd(p));
-  if (w.total > 0 && !workspace) return TTT_E_NULL;
-  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
+  const size_t need = ttt_attn_bwd_workspace_size(p);
+  if (need > 0 && !workspace) return TTT_E_NULL;
+  if (workspace_bytes < need) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || !aligned16(workspace))
     return TTT_E_ALIGN;
-  return run_bwd(p, s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, (char*)workspace,
-                 (hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  if (pad64_path(p)) {
+    const ttt_attn_params p2 = widened(p);
+    const PadLayout w = pad_layout(s, true);
+    char* ws = (char*)workspace;
+    const size_t rq = (size_t)s.B * s.Hq * s.L, rkv = (size_t)s.B * s.Hkv * s.KV;
+    if (launch_pad64(q, ws + w.q, rq, st) != hipSuccess ||
+        launch_pad64(k, ws + w.k, rkv, st) != hipSuccess ||
+        launch_pad64(v, ws + w.v, rkv, st) != hipSuccess ||
+        launch_pad64(o, ws + w.o, rq, st) != hipSuccess ||
+        launch_pad64(dout, ws + w.dout, rq, st) != hipSuccess)
+      return TTT_E_HIP;
+    rc = run_bwd(&p2, make_shape(&p2), ws + w.q, ws + w.k, ws + w.v, seq_T, ws + w.o, lse,
+                 ws + w.dout, ws + w.dq, ws + w.dk, ws + w.dv, ws + w.inner, st);
+    if (rc != TTT_OK) return rc;
+    if (launch_unpad64(ws + w.dq, dq, rq, st) != hipSuccess ||
+        launch_unpad64(ws + w.dk, dk, rkv, st) != hipSuccess ||
+        launch_unpad64(ws + w.dv, dv, rkv, st) != hipSuccess)
+      return TTT_E_HIP;
+    return TTT_OK;
+  }
+  return run_bwd(p, s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, (char*)workspace, st);
 }
 
 int ttt_attn_bwd_noalloc(const ttt_attn_params* p, const void* q, const void* k, const void* v,

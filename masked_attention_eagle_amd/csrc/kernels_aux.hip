@@ -1,4 +1,4 @@
-// Backward row term D_i = rowsum(dO_i * O_i) (bandwidth-bound).
+// Backward row term D_i = rowsum(dO_i * O_i) (bandwidth-bound), and the head_dim-64 row copies.
 #include "launch.h"
 
 namespace ttt {
@@ -52,6 +52,47 @@ template hipError_t launch_bwd_rowdot<float>(const Shape&, const float*, const f
                                              const float*, float*, unsigned*, hipStream_t);
 template hipError_t launch_bwd_rowdot<bf16>(const Shape&, const bf16*, const bf16*, float*,
                                             const float*, float*, unsigned*, hipStream_t);
+
+// bf16 rows of 64 elements (128 bytes) to rows of 128 whose upper half is zero, and back: the
+// head_dim-64 problem on the matrix-core kernels, which tile a 128-element head.  One 16-byte
+// chunk per thread and step; every index stays below rows * 16 (padded) or rows * 8.
+__global__ __launch_bounds__(256) void pad64_kernel(const bf16x8* __restrict__ src,
+                                                    bf16x8* __restrict__ dst, size_t rows) {
+  const size_t n = rows * 16, stride = (size_t)gridDim.x * 256;
+  bf16x8 z;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) z[j] = (bf16)0.f;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    const size_t r = i >> 4;
+    const int c = (int)(i & 15);
+    dst[i] = c < 8 ? src[r * 8 + c] : z;
+  }
+}
+
+__global__ __launch_bounds__(256) void unpad64_kernel(const bf16x8* __restrict__ src,
+                                                      bf16x8* __restrict__ dst, size_t rows) {
+  const size_t n = rows * 8, stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+    dst[i] = src[(i >> 3) * 16 + (i & 7)];
+}
+
+hipError_t launch_pad64(const void* src, void* dst, size_t rows, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const size_t blocks = (rows * 16 + 255) / 256;
+  LaunchTimer timer("pad64", st);
+  pad64_kernel<<<dim3((unsigned)(blocks < 16384 ? blocks : 16384)), 256, 0, st>>>(
+      reinterpret_cast<const bf16x8*>(src), reinterpret_cast<bf16x8*>(dst), rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpad64(const void* src, void* dst, size_t rows, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const size_t blocks = (rows * 8 + 255) / 256;
+  LaunchTimer timer("unpad64", st);
+  unpad64_kernel<<<dim3((unsigned)(blocks < 16384 ? blocks : 16384)), 256, 0, st>>>(
+      reinterpret_cast<const bf16x8*>(src), reinterpret_cast<bf16x8*>(dst), rows);
+  return hipGetLastError();
+}
 
 // Writes `bytes` (a multiple of 16) of buf with plain stores: run before a timed launch, it
 // replaces what the caches (L2 and the memory-side last-level cache) hold.

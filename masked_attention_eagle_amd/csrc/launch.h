@@ -80,6 +80,11 @@ hipError_t launch_bwd_suffix_sweep(const Shape& s, const bf16* q, const bf16* k,
                                    const int32_t* seq_T, float* dq_acc, bf16* dq, bf16* dk,
                                    bf16* dv, hipStream_t st);
 
+// bf16 rows of 64 elements into rows of 128 whose upper half is zero (pad), and the first 64
+// elements of each 128-element row back (unpad); rows = number of rows.
+hipError_t launch_pad64(const void* src, void* dst, size_t rows, hipStream_t st);
+hipError_t launch_unpad64(const void* src, void* dst, size_t rows, hipStream_t st);
+
 // Cache flush for measurement: overwrites `bytes` (a multiple of 16) of buf.
 hipError_t launch_flush_fill(void* buf, size_t bytes, hipStream_t st);
 

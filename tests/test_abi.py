@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(A.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.ttt_attn_version() == 103
+    assert lib.ttt_attn_version() == 104
     loss_declared = header_functions("ttt_loss.h", "ttt_loss_")
     assert set(loss_declared) == set(A.LOSS_EXPORTS)
     for name in loss_declared:
@@ -142,14 +142,23 @@ def test_workspace_sizes():
     rowsf = 2 * 32 * 4000
     for f in (0, sep, rec):
         assert A.bwd_workspace_size(P(dtype=A.TTT_DTYPE_F32, L=4000, flags=f)) == rowsf * 4 + rowsf * d * 4
-    # bf16 outside the matrix-core tiling (head_dim 64, or Q_LEN not a multiple of 128): the
-    # vector-ALU kernels, with the fp32 path's workspaces (causal state; D + dQ accumulator)
-    for kw in (dict(d=64), dict(L=4032), dict(d=64, L=192)):
+    # bf16 outside the matrix-core tiling (Q_LEN not a multiple of 128): the vector-ALU
+    # kernels, with the fp32 path's workspaces (causal state; D + dQ accumulator)
+    for kw in (dict(L=4032), dict(d=64, L=192)):
         pv = P(**kw)
         rv = 2 * 32 * pv.q_len
         assert A.fwd_workspace_size(pv) == rv * pv.head_dim * 4 + rv * 4
         assert A.bwd_workspace_size(pv) == rv * 4 + rv * pv.head_dim * 4
         assert A.bwd_workspace_size(P(step=0, **kw)) == rv * 4
+    # bf16 at head_dim 64 with Q_LEN a multiple of 128: head_dim-128 copies of q, k, v, o (and
+    # for the backward dO, dq, dk, dv) ahead of the head_dim-128 call's own workspace
+    for st in (0, 1, 3):
+        for f in (0, sep, rec):
+            rq, rkv = 2 * 32 * 4096 * 256, 2 * 8 * (st + 1) * 4096 * 256
+            assert A.fwd_workspace_size(P(d=64, step=st, flags=f)) == \
+                2 * rq + 2 * rkv + A.fwd_workspace_size(P(step=st, flags=f))
+            assert A.bwd_workspace_size(P(d=64, step=st, flags=f)) == \
+                4 * rq + 4 * rkv + A.bwd_workspace_size(P(step=st, flags=f))
     assert A.fwd_workspace_size(P(Hq=30)) == 0  # invalid params -> 0
     assert A.bwd_workspace_size(P(Hq=30)) == 0
 

@@ -54,10 +54,10 @@ def test_fp32_group_of_eight(gpu_lib, d):
 
 
 # ------------------------------------------------------------------ bf16 vector-ALU path
-# bf16 shapes outside the matrix-core tiling (head_dim 64, Q_LEN not a multiple of 128) run on
-# the vector-ALU kernels: bf16 storage, fp32 arithmetic, the bf16 tolerances.
+# bf16 shapes outside the matrix-core tiling (Q_LEN not a multiple of 128) run on the
+# vector-ALU kernels: bf16 storage, fp32 arithmetic, the bf16 tolerances.
 @pytest.mark.parametrize("step,T,d,L,Hq,Hkv", [
-    (0, (37, 0), 64, 128, 4, 2), (2, (128, 77), 64, 128, 4, 2), (3, (64, 65), 128, 192, 4, 2),
+    (0, (37, 0), 64, 192, 4, 2), (2, (64, 60), 64, 64, 4, 2), (3, (64, 65), 128, 192, 4, 2),
     (2, (190, 1), 64, 320, 8, 1), (1, (40, 64), 128, 64, 2, 2), (4, (100, 96), 64, 96, 2, 1)])
 def test_bf16_valu_shapes(gpu_lib, step, T, d, L, Hq, Hkv):
     run_case(gpu_lib, 120 + step + L, 2, Hq, Hkv, d, L, step, T, "bf16")
@@ -71,6 +71,31 @@ def test_bf16_valu_shapes(gpu_lib, step, T, d, L, Hq, Hkv):
 # standalone suffix kernel on an fp32 state).
 PATHS = [("stored", "fused"), ("recompute", "fused"), ("stored", "separate"),
          ("fused-suffix", "fused")]
+
+
+# bf16 at head_dim 64 with Q_LEN a multiple of 128: the matrix-core kernels, through
+# head_dim-128 copies of the rows whose upper half is zero.
+@pytest.mark.parametrize("dq_mode,suffix", PATHS + [("stored", "dense")])
+@pytest.mark.parametrize("step,T,L,Hq,Hkv", [(0, (128, 37), 128, 4, 2), (1, (256, 1), 256, 8, 2),
+                                             (2, (200, 256), 256, 4, 1), (3, (512, 333), 512, 8, 4)])
+def test_bf16_head_dim_64_matrix_core(gpu_lib, step, T, L, Hq, Hkv, dq_mode, suffix):
+    run_case(gpu_lib, 160 + step, 2, Hq, Hkv, 64, L, step, T, "bf16", dq_mode=dq_mode,
+             suffix=suffix)
+
+
+def test_bf16_head_dim_64_runs_on_the_matrix_cores(gpu_lib):
+    """The forward pads q, k, v and unpads o; the backward pads q, k, v, o, dO and unpads dq, dk,
+    dv; in between run the matrix-core kernels, not the vector-ALU ones."""
+    gpu_lib.timing_reset()
+    gpu_lib.timing_enable(True)
+    try:
+        run_case(gpu_lib, 171, 1, 4, 2, 64, 256, 2, (256,), "bf16")
+    finally:
+        gpu_lib.timing_enable(False)
+    t = gpu_lib.timing_read()
+    assert t["pad64"][0] == 3 + 5 and t["unpad64"][0] == 1 + 3
+    assert t["fwd_causal_mfma"][0] == 1 and t["bwd_dkdv_mfma"][0] == 1
+    assert not any("valu" in name for name in t)
 
 
 @pytest.mark.parametrize("dq_mode,suffix", PATHS)
