@@ -99,13 +99,12 @@ enum ttt_attn_status {
  * Problem description.  Supported combinations:
  *   dtype F32 : head_dim in {64, 128}, any q_len >= 1 (vector-ALU kernels).
  *   dtype BF16: head_dim in {64, 128}, any q_len >= 1.  head_dim 128 with q_len a multiple of
- *               128 runs on the matrix-core kernels (the fast path, and the only one the
- *               whole-TTT calls take).  head_dim 64 with q_len a multiple of 128 runs on the
- *               same kernels in ttt_attn_fwd and ttt_attn_bwd, through head_dim-128 copies of
- *               the rows whose upper half is zero (exact: the zero half adds nothing to any
- *               sum), which the workspace holds; the flags below apply to both.  Other bf16
- *               shapes, and head_dim 64 in ttt_attn_bwd_noalloc, run on the vector-ALU kernels
- *               (bf16 storage, fp32 arithmetic).
+ *               128 runs on the matrix-core kernels (the fast path).  head_dim 64 with q_len a
+ *               multiple of 128 runs on the same kernels through head_dim-128 copies of the
+ *               rows whose upper half is zero (exact: the zero half adds nothing to any sum),
+ *               which the workspace holds; the flags below apply to both.  The whole-TTT calls
+ *               take these two; other bf16 shapes, and head_dim 64 in ttt_attn_bwd_noalloc,
+ *               run on the vector-ALU kernels (bf16 storage, fp32 arithmetic).
  * scale multiplies q.k before masking (1/sqrt(head_dim) in the usual setting); it must be
  * finite and positive (the streaming softmax tracks the row maximum of the raw q.k).
  */

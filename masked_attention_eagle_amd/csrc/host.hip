@@ -143,7 +143,7 @@ int validate(const ttt_attn_params* p) {
 int validate_sweep(const ttt_attn_params* p) {
   const int rc = validate(p);
   if (rc != TTT_OK) return rc;
-  if (!mfma_path(p)) return TTT_E_UNSUPPORTED;
+  if (!mfma_path(p) && !pad64_path(p)) return TTT_E_UNSUPPORTED;
   const int64_t rows_all = ((int64_t)p->ttt_step + 1) * p->batch * p->heads_q * p->q_len;
   if (rows_all * p->head_dim > (1ll << 40) || rows_all / 16 >= (1ll << 31)) return TTT_E_SHAPE;
   return TTT_OK;
@@ -261,10 +261,11 @@ BwdLayout bwd_layout(const Shape& s, bool mfma, bool with_ds, bool dense = false
 struct PadLayout {
   size_t q = 0, k = 0, v = 0, o = 0, dout = 0, dq = 0, dk = 0, dv = 0, inner = 0;
 };
-PadLayout pad_layout(const Shape& s, bool bwd) {
+// rows_q: rows of q (o, dO, dq); rows_kv: rows of k (v, dk, dv)
+PadLayout pad_regions(size_t rows_q, size_t rows_kv, bool bwd) {
   PadLayout w;
-  const size_t rq = round_up((size_t)s.B * s.Hq * s.L * 128 * 2);
-  const size_t rkv = round_up((size_t)s.B * s.Hkv * s.KV * 128 * 2);
+  const size_t rq = round_up(rows_q * 128 * 2);
+  const size_t rkv = round_up(rows_kv * 128 * 2);
   size_t off = 0;
   w.q = off; off += rq;
   w.k = off; off += rkv;
@@ -278,6 +279,9 @@ PadLayout pad_layout(const Shape& s, bool bwd) {
   }
   w.inner = off;
   return w;
+}
+PadLayout pad_layout(const Shape& s, bool bwd) {
+  return pad_regions((size_t)s.B * s.Hq * s.L, (size_t)s.B * s.Hkv * s.KV, bwd);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_E_HIP; }
@@ -500,6 +504,80 @@ Shape sweep_all_shape(const ttt_attn_params* p) {
   return s;
 }
 
+// Whole-TTT forward and backward on validated arguments (head_dim-128 rows: the head_dim-64
+// calls pass their zero-padded copies).
+int run_fwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                  const int32_t* seq_T, void* o, float* lse, char* ws, hipStream_t st) {
+  const size_t qel = (size_t)p->batch * p->heads_q * p->q_len * p->head_dim;  // per step
+  const size_t rows = (size_t)p->batch * p->heads_q * p->q_len;
+  for (int kk = 0; kk <= p->ttt_step; ++kk) {
+    const int rc = run_fwd(p, sweep_shape(p, kk), (const bf16*)q + kk * qel, k, v, seq_T,
+                           (bf16*)o + kk * qel, lse + kk * rows, ws, st);
+    if (rc != TTT_OK) return rc;
+  }
+  return TTT_OK;
+}
+size_t sweep_bwd_ws(const ttt_attn_params* p) {
+  const ttt_attn_params pb = sweep_bwd_params(p);
+  return bwd_layout(sweep_all_shape(p), true, stored_ds(&pb)).total;
+}
+int run_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
+                  const int32_t* seq_T, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, char* ws, hipStream_t st) {
+  const ttt_attn_params pb = sweep_bwd_params(p);
+  const bool with_ds = stored_ds(&pb);
+  const Shape sa = sweep_all_shape(p);
+  const BwdLayout w = bwd_layout(sa, true, with_ds);
+  const size_t qel = (size_t)p->batch * p->heads_q * p->q_len * p->head_dim;
+  const size_t rows = (size_t)p->batch * p->heads_q * p->q_len;
+  const bf16* qb = (const bf16*)q;
+  const bf16* kb = (const bf16*)k;
+  const bf16* vb = (const bf16*)v;
+  const bf16* dob = (const bf16*)dout;
+  float* Dd = (float*)(ws + w.Dd);
+  float* lse2 = (float*)(ws + w.lse2);
+  float* part = w.nsplit > 1 ? (float*)(ws + w.part) : nullptr;
+  bf16* dsb = with_ds ? (bf16*)(ws + w.ds) : nullptr;
+  float* dqacc = (float*)(ws + w.dqacc);
+  hipError_t e;
+  // Block 0: one row-dot launch, one dK/dV launch and one reduction over the queries of all
+  // steps (the keys of block 0 are seen by every step), which writes its dk/dv rows.
+  unsigned* sched = (unsigned*)(ws + w.sched);
+  if ((e = launch_bwd_rowdot<bf16>(sa, (const bf16*)o, dob, Dd, lse, lse2, sched, st)) != hipSuccess)
+    return TTT_E_HIP;
+  if ((e = launch_bwd_dkdv_mfma(sa, qb, kb, vb, dob, lse2, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
+                                w.nsplit, dsb, false, nullptr, sched, st)) != hipSuccess)
+    return TTT_E_HIP;
+  if (w.nsplit > 1 &&
+      (e = launch_bwd_dkdv_reduce(sa, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
+    return TTT_E_HIP;
+  // Per step, the block-0 dQ: final for step 0, into its fp32 accumulator for the others.
+  for (int kk = 0; kk <= p->ttt_step; ++kk) {
+    const Shape s = sweep_shape(p, kk);
+    void* dq_causal = kk == 0 ? (void*)((bf16*)dq) : (void*)(dqacc + (kk - 1) * qel);
+    if (with_ds)
+      e = launch_bwd_dq_ds(s, kb, dsb + kk * ds_step_elems(s), seq_T, dq_causal, kk == 0, nullptr,
+                           st);
+    else
+      e = launch_bwd_dq_mfma(s, qb + kk * qel, kb, vb, dob + kk * qel, lse + kk * rows,
+                             Dd + kk * rows, seq_T, dq_causal, kk == 0, false, st);
+    if (e != hipSuccess) return TTT_E_HIP;
+  }
+  // Blocks 1..K-1 and the diagonal part of dQ: one launch over every step.
+  if (p->ttt_step > 0 &&
+      (e = launch_bwd_suffix_sweep(sa, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq,
+                                   (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
+    return TTT_E_HIP;
+  return TTT_OK;
+}
+// The head_dim-128 copies of a whole-TTT head_dim-64 call: q, o (dO, dq) of every step and the
+// cache k, v (dk, dv).
+PadLayout sweep_pad(const ttt_attn_params* p, bool bwd) {
+  const size_t K = (size_t)p->ttt_step + 1;
+  return pad_regions(K * p->batch * p->heads_q * p->q_len, K * p->batch * p->heads_kv * p->q_len,
+                     bwd);
+}
+
 }  // namespace
 }  // namespace ttt
 
@@ -596,13 +674,19 @@ int ttt_attn_bwd_noalloc(const ttt_attn_params* p, const void* q, const void* k,
 
 size_t ttt_attn_fwd_sweep_workspace_size(const ttt_attn_params* p) {
   if (validate_sweep(p) != TTT_OK) return 0;
+  if (pad64_path(p)) {
+    const ttt_attn_params w = widened(p);
+    return sweep_pad(p, false).inner + sweep_fwd_ws(&w);
+  }
   return sweep_fwd_ws(p);
 }
-
 size_t ttt_attn_bwd_sweep_workspace_size(const ttt_attn_params* p) {
   if (validate_sweep(p) != TTT_OK) return 0;
-  const ttt_attn_params pb = sweep_bwd_params(p);
-  return bwd_layout(sweep_all_shape(p), true, stored_ds(&pb)).total;
+  if (pad64_path(p)) {
+    const ttt_attn_params w = widened(p);
+    return sweep_pad(p, true).inner + sweep_bwd_ws(&w);
+  }
+  return sweep_bwd_ws(p);
 }
 
 int ttt_attn_fwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
@@ -611,20 +695,29 @@ int ttt_attn_fwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
   int rc = validate_sweep(p);
   if (rc != TTT_OK) return rc;
   if (!q || !k || !v || !seq_T || !o || !lse) return TTT_E_NULL;
-  const size_t need = sweep_fwd_ws(p);
+  const size_t need = ttt_attn_fwd_sweep_workspace_size(p);
   if (need > 0 && !workspace) return TTT_E_NULL;
   if (workspace_bytes < need) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(workspace))
     return TTT_E_ALIGN;
-  const size_t qel = (size_t)p->batch * p->heads_q * p->q_len * p->head_dim;  // per step
-  const size_t rows = (size_t)p->batch * p->heads_q * p->q_len;
-  for (int kk = 0; kk <= p->ttt_step; ++kk) {
-    rc = run_fwd(p, sweep_shape(p, kk), (const bf16*)q + kk * qel, k, v, seq_T,
-                 (bf16*)o + kk * qel, lse + kk * rows, (char*)workspace, (hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  if (pad64_path(p)) {
+    const ttt_attn_params p2 = widened(p);
+    const PadLayout w = sweep_pad(p, false);
+    char* ws = (char*)workspace;
+    const size_t K = (size_t)p->ttt_step + 1;
+    const size_t rq = K * p->batch * p->heads_q * p->q_len;
+    const size_t rkv = K * p->batch * p->heads_kv * p->q_len;
+    if (launch_pad64(q, ws + w.q, rq, st) != hipSuccess ||
+        launch_pad64(k, ws + w.k, rkv, st) != hipSuccess ||
+        launch_pad64(v, ws + w.v, rkv, st) != hipSuccess)
+      return TTT_E_HIP;
+    rc = run_fwd_sweep(&p2, ws + w.q, ws + w.k, ws + w.v, seq_T, ws + w.o, lse, ws + w.inner, st);
     if (rc != TTT_OK) return rc;
+    return hip_status(launch_unpad64(ws + w.o, o, rq, st));
   }
-  return TTT_OK;
+  return run_fwd_sweep(p, q, k, v, seq_T, o, lse, (char*)workspace, st);
 }
 
 int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, const void* v,
@@ -635,58 +728,35 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
   if (rc != TTT_OK) return rc;
   if (!q || !k || !v || !seq_T || !o || !lse || !dout || !dq || !dk || !dv) return TTT_E_NULL;
   if (!workspace) return TTT_E_NULL;
-  const ttt_attn_params pb = sweep_bwd_params(p);
-  const bool with_ds = stored_ds(&pb);
-  const Shape sa = sweep_all_shape(p);
-  const BwdLayout w = bwd_layout(sa, true, with_ds);
-  if (workspace_bytes < w.total) return TTT_E_WORKSPACE;
+  if (workspace_bytes < ttt_attn_bwd_sweep_workspace_size(p)) return TTT_E_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || !aligned16(workspace))
     return TTT_E_ALIGN;
-  char* ws = (char*)workspace;
-  const size_t qel = (size_t)p->batch * p->heads_q * p->q_len * p->head_dim;
-  const size_t rows = (size_t)p->batch * p->heads_q * p->q_len;
-  hipStream_t st = (hipStream_t)stream;
-  const bf16* qb = (const bf16*)q;
-  const bf16* kb = (const bf16*)k;
-  const bf16* vb = (const bf16*)v;
-  const bf16* dob = (const bf16*)dout;
-  float* Dd = (float*)(ws + w.Dd);
-  float* lse2 = (float*)(ws + w.lse2);
-  float* part = w.nsplit > 1 ? (float*)(ws + w.part) : nullptr;
-  bf16* dsb = with_ds ? (bf16*)(ws + w.ds) : nullptr;
-  float* dqacc = (float*)(ws + w.dqacc);
-  hipError_t e;
-  // Block 0: one row-dot launch, one dK/dV launch and one reduction over the queries of all
-  // steps (the keys of block 0 are seen by every step), which writes its dk/dv rows.
-  unsigned* sched = (unsigned*)(ws + w.sched);
-  if ((e = launch_bwd_rowdot<bf16>(sa, (const bf16*)o, dob, Dd, lse, lse2, sched, st)) != hipSuccess)
-    return TTT_E_HIP;
-  if ((e = launch_bwd_dkdv_mfma(sa, qb, kb, vb, dob, lse2, Dd, seq_T, (bf16*)dk, (bf16*)dv, part,
-                                w.nsplit, dsb, false, nullptr, sched, st)) != hipSuccess)
-    return TTT_E_HIP;
-  if (w.nsplit > 1 &&
-      (e = launch_bwd_dkdv_reduce(sa, part, w.nsplit, (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
-    return TTT_E_HIP;
-  // Per step, the block-0 dQ: final for step 0, into its fp32 accumulator for the others.
-  for (int kk = 0; kk <= p->ttt_step; ++kk) {
-    const Shape s = sweep_shape(p, kk);
-    void* dq_causal = kk == 0 ? (void*)((bf16*)dq) : (void*)(dqacc + (kk - 1) * qel);
-    if (with_ds)
-      e = launch_bwd_dq_ds(s, kb, dsb + kk * ds_step_elems(s), seq_T, dq_causal, kk == 0, nullptr,
-                           st);
-    else
-      e = launch_bwd_dq_mfma(s, qb + kk * qel, kb, vb, dob + kk * qel, lse + kk * rows,
-                             Dd + kk * rows, seq_T, dq_causal, kk == 0, false, st);
-    if (e != hipSuccess) return TTT_E_HIP;
+  const hipStream_t st = (hipStream_t)stream;
+  if (pad64_path(p)) {
+    const ttt_attn_params p2 = widened(p);
+    const PadLayout w = sweep_pad(p, true);
+    char* ws = (char*)workspace;
+    const size_t K = (size_t)p->ttt_step + 1;
+    const size_t rq = K * p->batch * p->heads_q * p->q_len;
+    const size_t rkv = K * p->batch * p->heads_kv * p->q_len;
+    if (launch_pad64(q, ws + w.q, rq, st) != hipSuccess ||
+        launch_pad64(k, ws + w.k, rkv, st) != hipSuccess ||
+        launch_pad64(v, ws + w.v, rkv, st) != hipSuccess ||
+        launch_pad64(o, ws + w.o, rq, st) != hipSuccess ||
+        launch_pad64(dout, ws + w.dout, rq, st) != hipSuccess)
+      return TTT_E_HIP;
+    rc = run_bwd_sweep(&p2, ws + w.q, ws + w.k, ws + w.v, seq_T, ws + w.o, lse, ws + w.dout,
+                       ws + w.dq, ws + w.dk, ws + w.dv, ws + w.inner, st);
+    if (rc != TTT_OK) return rc;
+    if (launch_unpad64(ws + w.dq, dq, rq, st) != hipSuccess ||
+        launch_unpad64(ws + w.dk, dk, rkv, st) != hipSuccess ||
+        launch_unpad64(ws + w.dv, dv, rkv, st) != hipSuccess)
+      return TTT_E_HIP;
+    return TTT_OK;
   }
-  // Blocks 1..K-1 and the diagonal part of dQ: one launch over every step.
-  if (p->ttt_step > 0 &&
-      (e = launch_bwd_suffix_sweep(sa, qb, kb, vb, dob, lse, Dd, seq_T, dqacc, (bf16*)dq,
-                                   (bf16*)dk, (bf16*)dv, st)) != hipSuccess)
-    return TTT_E_HIP;
-  return TTT_OK;
+  return run_bwd_sweep(p, q, k, v, seq_T, o, lse, dout, dq, dk, dv, (char*)workspace, st);
 }
 
 int ttt_loss_grad_inplace(const ttt_loss_params* p, void* z, const void* target, const float* g,

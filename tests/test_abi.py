@@ -291,8 +291,13 @@ def test_sweep_workspace_and_errors():
     assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(pf)) == 0
     good = ctypes.c_void_p(1 << 20)
     args = [good] * 11
+    # head_dim 64: head_dim-128 copies of q, o (dO, dq) of every step and of the cache k, v (dk,
+    # dv) ahead of the head_dim-128 call's workspace
+    rq, rkv = K * rows * 256, K * B * Hkv * L * 256
+    assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(P(step=K - 1, d=64))) == 4 * rq + 4 * rkv + whole
+    assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(P(step=K - 1, d=64))) == 2 * rq + 2 * rkv
     # whole-TTT calls take the matrix-core shapes only
-    for bad in (P(step=2, d=64), P(step=2, L=4032)):
+    for bad in (P(step=2, d=64, L=4032), P(step=2, L=4032)):
         assert lib.ttt_attn_fwd_sweep_workspace_size(ctypes.byref(bad)) == 0
         assert lib.ttt_attn_bwd_sweep_workspace_size(ctypes.byref(bad)) == 0
         assert lib.ttt_attn_fwd_sweep(ctypes.byref(bad), *args[:7], 1 << 40, None) == -3

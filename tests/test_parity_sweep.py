@@ -40,10 +40,20 @@ def _norm_err(got, ref):
                                              # a single step: block 0 only, no suffix launch
                                              (1, 4, 2, 128, 1, 100)])
 def test_sweep_against_oracle(gpu_lib, B, Hq, Hkv, L, K, T, dq_mode):
+    _sweep_vs_oracle(gpu_lib, 128, B, Hq, Hkv, L, K, T, dq_mode)
+
+
+# head_dim 64: the same kernels through zero-padded head_dim-128 copies of every step's rows
+@pytest.mark.parametrize("dq_mode", ["stored", "recompute"])
+@pytest.mark.parametrize("B,Hq,Hkv,L,K,T", [(2, 4, 2, 256, 4, (256, 140)), (1, 8, 2, 128, 3, 77)])
+def test_sweep_head_dim_64_against_oracle(gpu_lib, B, Hq, Hkv, L, K, T, dq_mode):
+    _sweep_vs_oracle(gpu_lib, 64, B, Hq, Hkv, L, K, T, dq_mode)
+
+
+def _sweep_vs_oracle(gpu_lib, d, B, Hq, Hkv, L, K, T, dq_mode):
     import torch
-    d = 128
     q, kc, vc, do, Tarr = _sweep_case(B * 100 + K, B, Hq, Hkv, d, L, K, T)
-    print(f"sweep B={B} Hq={Hq} Hkv={Hkv} L={L} K={K} T={list(Tarr)} dq={dq_mode}", flush=True)
+    print(f"sweep d={d} B={B} Hq={Hq} Hkv={Hkv} L={L} K={K} T={list(Tarr)} dq={dq_mode}", flush=True)
     bf = torch.bfloat16
     qd, kd, vd, dod = to_dev(q, bf), to_dev(kc, bf), to_dev(vc, bf), to_dev(do, bf)
     Td = torch.as_tensor(Tarr, device="cuda")
