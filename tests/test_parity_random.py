@@ -5,8 +5,9 @@ The shapes are drawn from a fixed generator: batch 1..3, KV-group counts 1, 2, 3
 queues by unit depending on whether these counts divide by 8), group sizes 1..8, Q_LEN on and
 off the matrix-core tiling (multiples of 128 and 192), TTT steps 0..3, ragged and out-of-range
 lengths T, and every path flag; every third case is a whole-TTT sweep of 1..5 steps.  The
-tolerances are those of the other bf16 parity tests.  A second draw covers the vector-ALU
-kernels (fp32, bf16 at head_dim 64 or off the matrix-core tiling).
+tolerances are those of the other bf16 parity tests.  Further draws cover bf16 head_dim 64 on
+the matrix-core kernels (zero-padded copies) and the vector-ALU kernels (fp32, bf16 off the
+matrix-core tiling).
 """
 import os
 
@@ -56,18 +57,18 @@ def _norm_err(got, ref):
     return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
 
 
-def _sweep(gpu_lib, seed, B, Hq, Hkv, L, K, T, dq_mode, label):
+def _sweep(gpu_lib, seed, B, Hq, Hkv, L, K, T, dq_mode, label, d=D):
     import torch
     Tn = np.asarray(T, dtype=np.int32)
-    q = np.stack([inputs.round_to_bf16(inputs._normal([seed, s, 20], (B, Hq, L, D), "f32"))
+    q = np.stack([inputs.round_to_bf16(inputs._normal([seed, s, 20], (B, Hq, L, d), "f32"))
                   for s in range(K)])
-    kc = inputs._normal([seed, 99, 21], (B, Hkv, K * L, D), "bf16")
-    vc = inputs._normal([seed, 99, 22], (B, Hkv, K * L, D), "bf16")
-    do = np.stack([inputs._normal([seed, s, 23], (B, Hq, L, D), "bf16") for s in range(K)])
+    kc = inputs._normal([seed, 99, 21], (B, Hkv, K * L, d), "bf16")
+    vc = inputs._normal([seed, 99, 22], (B, Hkv, K * L, d), "bf16")
+    do = np.stack([inputs._normal([seed, s, 23], (B, Hq, L, d), "bf16") for s in range(K)])
     bf = torch.bfloat16
     qd, kd, vd, dod = to_dev(q, bf), to_dev(kc, bf), to_dev(vc, bf), to_dev(do, bf)
     Td = torch.as_tensor(Tn, device="cuda")
-    scale = 1.0 / np.sqrt(D)
+    scale = 1.0 / np.sqrt(d)
     o, lse = gpu_lib.ttt_attn_fwd_sweep(qd, kd, vd, Td, scale)
     dq, dk, dv = gpu_lib.ttt_attn_bwd_sweep(qd, kd, vd, Td, o, lse, dod, scale, dq_mode=dq_mode)
     torch.cuda.synchronize()
@@ -151,6 +152,52 @@ def test_random_valu_case_against_oracle(gpu_lib, idx):
     ro, rlse = O.forward(q, k, v, Tn, scale)
     rdq, rdk, rdv = O.backward(q, k, v, Tn, scale, do, ro)
     check(got, dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv), c["dtype"], label, f32_relative=True)
+
+
+def _draw_d64_cases(n, seed=20261204):
+    """bf16 head_dim 64 at Q_LEN multiples of 128 (the zero-padded matrix-core route): per-step
+    calls on every path flag, and every third case a whole-TTT sweep."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        B = int(rng.integers(1, 3))
+        Hkv = int(rng.choice([1, 2, 3, 4]))
+        G = int(rng.choice([1, 2, 4]))
+        L = int(rng.choice([128, 256, 384]))
+        if c % 3 == 2:
+            cases.append(dict(kind="sweep", B=B, Hq=Hkv * G, Hkv=Hkv, L=L, K=int(rng.integers(1, 5)),
+                              T=tuple(int(t) for t in rng.integers(0, L + 6, size=B)),
+                              dq_mode=str(rng.choice(["stored", "recompute"]))))
+            continue
+        dq_mode = str(rng.choice(["stored", "recompute", "fused-suffix"]))
+        suffix = "fused" if dq_mode == "fused-suffix" else str(rng.choice(["fused", "separate", "dense"]))
+        cases.append(dict(kind="step", B=B, Hq=Hkv * G, Hkv=Hkv, L=L, step=int(rng.integers(0, 4)),
+                          T=tuple(int(t) for t in rng.integers(0, L + 6, size=B)),
+                          dq_mode=dq_mode, suffix=suffix))
+    return cases
+
+
+D64_CASES = _draw_d64_cases(12)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("idx", range(len(D64_CASES)))
+def test_random_head_dim_64_case_against_oracle(gpu_lib, idx):
+    c = D64_CASES[idx]
+    label = f"random head_dim-64 case {idx}: {c}"
+    print(label, flush=True)
+    if c["kind"] == "sweep":
+        _sweep(gpu_lib, 900 + idx, c["B"], c["Hq"], c["Hkv"], c["L"], c["K"], c["T"],
+               c["dq_mode"], label, d=64)
+        return
+    q, k, v, do, Tn = inputs.make_case(2000 + idx, c["B"], c["Hq"], c["Hkv"], 64, c["L"],
+                                       c["step"], c["T"], "bf16")
+    scale = 1.0 / np.sqrt(64)
+    got = gpu_fwd_bwd(gpu_lib, q, k, v, do, Tn, scale, "bf16", dq_mode=c["dq_mode"],
+                      suffix=c["suffix"])
+    ro, rlse = O.forward(q, k, v, Tn, scale)
+    rdq, rdk, rdv = O.backward(q, k, v, Tn, scale, do, ro)
+    check(got, dict(o=ro, lse=rlse, dq=rdq, dk=rdk, dv=rdv), "bf16", label)
 
 
 @pytest.mark.gpu
