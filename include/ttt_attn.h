@@ -102,8 +102,8 @@ enum ttt_attn_status {
  *               128 runs on the matrix-core kernels (the fast path).  head_dim 64 with q_len a
  *               multiple of 128 runs on the same kernels through head_dim-128 copies of the
  *               rows whose upper half is zero (exact: the zero half adds nothing to any sum),
- *               which the workspace holds; the flags below apply to both.  The whole-TTT calls
- *               take these two; other bf16 shapes, and head_dim 64 in ttt_attn_bwd_noalloc,
+ *               which the workspace (ttt_attn_bwd_noalloc: its scratch array) holds; the flags
+ *               below apply to both.  The whole-TTT calls take these two; other bf16 shapes
  *               run on the vector-ALU kernels (bf16 storage, fp32 arithmetic).
  * scale multiplies q.k before masking (1/sqrt(head_dim) in the usual setting); it must be
  * finite and positive (the streaming softmax tracks the row maximum of the raw q.k).
@@ -194,7 +194,8 @@ int ttt_attn_bwd_sweep(const ttt_attn_params* p, const void* q, const void* k, c
  * No-allocation backward, for callers that cannot allocate device memory or take a workspace
  * argument (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments and results as ttt_attn_bwd without the workspace: the
- * backward's scratch (D, lse * log2(e), split dK/dV partials, the fp32 dQ accumulator) lives in
+ * backward's scratch (D, lse * log2(e), split dK/dV partials, the fp32 dQ accumulator, and at
+ * bf16 head_dim 64 the zero-padded head_dim-128 copies of the rows) lives in
  * a device array of TTT_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
  * until the process ends; the dQ kernel recomputes S and dP (TTT_FLAG_RECOMPUTE_DQ is implied:
  * the stored-dS path needs a logits-sized buffer), so dq, dk and dv are bitwise those of

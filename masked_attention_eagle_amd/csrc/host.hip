@@ -662,14 +662,35 @@ int ttt_attn_bwd_noalloc(const ttt_attn_params* p, const void* q, const void* k,
   ttt_attn_params pr = *p;
   pr.flags |= TTT_FLAG_RECOMPUTE_DQ;  // no logits-sized dS buffer
   const Shape s = make_shape(&pr);
-  const BwdLayout w = bwd_layout(s, mfma_path(&pr), stored_ds(&pr), dense_bwd(&pr));
-  if (w.total > TTT_NOALLOC_SCRATCH_BYTES) return TTT_E_SCRATCH;
+  // bf16 head_dim 64 takes the zero-padded copies as ttt_attn_bwd does (same kernels, same bits);
+  // they sit at the start of the scratch array, ahead of the head_dim-128 call's regions
+  const bool pad = pad64_path(&pr);
+  const ttt_attn_params p2 = pad ? widened(&pr) : pr;
+  const PadLayout pl = pad ? pad_layout(s, true) : PadLayout{};
+  const BwdLayout w = bwd_layout(make_shape(&p2), mfma_path(&p2), stored_ds(&p2), dense_bwd(&p2));
+  if (pl.inner + w.total > TTT_NOALLOC_SCRATCH_BYTES) return TTT_E_SCRATCH;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(seq_T) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return TTT_E_ALIGN;
   char* ws = nullptr;
   if ((rc = scratch_of_current_device(&ws)) != TTT_OK) return rc;
-  return run_bwd(&pr, s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, ws, (hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  if (!pad) return run_bwd(&pr, s, q, k, v, seq_T, o, lse, dout, dq, dk, dv, ws, st);
+  const size_t rq = (size_t)s.B * s.Hq * s.L, rkv = (size_t)s.B * s.Hkv * s.KV;
+  if (launch_pad64(q, ws + pl.q, rq, st) != hipSuccess ||
+      launch_pad64(k, ws + pl.k, rkv, st) != hipSuccess ||
+      launch_pad64(v, ws + pl.v, rkv, st) != hipSuccess ||
+      launch_pad64(o, ws + pl.o, rq, st) != hipSuccess ||
+      launch_pad64(dout, ws + pl.dout, rq, st) != hipSuccess)
+    return TTT_E_HIP;
+  rc = run_bwd(&p2, make_shape(&p2), ws + pl.q, ws + pl.k, ws + pl.v, seq_T, ws + pl.o, lse,
+               ws + pl.dout, ws + pl.dq, ws + pl.dk, ws + pl.dv, ws + pl.inner, st);
+  if (rc != TTT_OK) return rc;
+  if (launch_unpad64(ws + pl.dq, dq, rq, st) != hipSuccess ||
+      launch_unpad64(ws + pl.dk, dk, rkv, st) != hipSuccess ||
+      launch_unpad64(ws + pl.dv, dv, rkv, st) != hipSuccess)
+    return TTT_E_HIP;
+  return TTT_OK;
 }
 
 size_t ttt_attn_fwd_sweep_workspace_size(const ttt_attn_params* p) {

@@ -2,8 +2,8 @@
 dQ kernel recomputing S and dP): the same kernels run on the library's fixed scratch array
 instead of a caller workspace, so dq, dk and dv must be bitwise equal.  Calls in a row share
 the array and each starts from what the previous one left there: the full-size
-Llama-3.1-8B-shaped step first, then smaller shapes (matrix-core, vector-ALU bf16 and fp32
-paths), then the first shape again."""
+Llama-3.1-8B-shaped step first, then smaller shapes (matrix-core at head_dim 128 and 64,
+vector-ALU bf16 and fp32 paths), then the first shape again."""
 import ctypes
 
 import numpy as np
@@ -44,6 +44,8 @@ def test_noalloc_backward_matches_workspace_backward(gpu_lib):
              _case("bf16 B2 Hq8 Hkv2 L512 k3", *inputs.make_case(81, 2, 8, 2, 128, 512, 3, (512, 301), "bf16"), "bf16"),
              _case("bf16 B1 Hq4 Hkv1 L256 k1", *inputs.make_case(82, 1, 4, 1, 128, 256, 1, 200, "bf16"), "bf16"),
              _case("bf16 d64 B2 Hq4 Hkv2 L192 k2", *inputs.make_case(83, 2, 4, 2, 64, 192, 2, (150, 192), "bf16"), "bf16"),
+             # head_dim 64 on the matrix-core kernels: zero-padded copies in the scratch array
+             _case("bf16 d64 B2 Hq8 Hkv2 L256 k2", *inputs.make_case(85, 2, 8, 2, 64, 256, 2, (256, 97), "bf16"), "bf16"),
              _case("f32 B1 Hq2 Hkv1 L128 k2", *inputs.make_case(84, 1, 2, 1, 64, 128, 2, 100, "f32"), "f32"),
              full]
     for label, (qd, kd, vd, Td, dod) in cases:
