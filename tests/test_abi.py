@@ -220,6 +220,9 @@ def test_noalloc_argument_errors():
     # 320 MiB maximum
     assert lib.ttt_attn_bwd_noalloc(ctypes.byref(P(B=8)), *args, None) == -7
     assert lib.ttt_attn_bwd_noalloc(ctypes.byref(P(B=16, L=2048)), *args, None) == -7
+    # bf16 head_dim 64 adds its zero-padded head_dim-128 copies to the scratch: at B 2 x Hq 32 x
+    # Q_LEN 4096, k = 6 the copies alone (q, o, dO, dq and k, v, dk, dv) take 704 MiB
+    assert lib.ttt_attn_bwd_noalloc(ctypes.byref(P(d=64, step=6)), *args, None) == -7
     bad = list(args)
     bad[5] = None
     assert lib.ttt_attn_bwd_noalloc(ctypes.byref(P()), *bad, None) == -1
